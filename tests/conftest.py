@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "exhaustive: 2^32 sweeps, run only when KVQ_EXHAUSTIVE=1")
+
+
+def pytest_collection_modifyitems(config, items):
+    if os.environ.get("KVQ_EXHAUSTIVE") == "1":
+        return
+    skip = pytest.mark.skip(reason="full 2^32 sweep: set KVQ_EXHAUSTIVE=1")
+    for item in items:
+        if "exhaustive" in item.keywords:
+            item.add_marker(skip)
