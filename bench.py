@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Bench of the KV codec's hot path on one MI355X.
+
+One step = every row of the hot path over one batch of the bulk workload (T=131072 tokens,
+H_kv=8, D=128, bf16 Student-t nu=3, ~268 MB per K or V tensor), for both formats (INT4 G64 and
+NVFP4 G16) and both kinds (K, V):
+    R0 = unpack(pack(X0)); R = encode_residual(X1, R0); R1 = decode_residual(R, R0)
+with X1 = bf16(X0 + 0.1 N(0,1)). Inputs are resident in HBM before the timed region; output
+planes are preallocated, so the timed region holds only kernel launches.
+
+value = algorithmic bytes of the whole step / step time (GB/s). Algorithmic bytes per element
+(n = T*H*D): pack INT4 2.5625, NVFP4 4.5625 (+4 B); unpack 2.5625 (+4 B); residual encode
+INT4 4.5625, NVFP4 8.5625 (+4 B); residual decode 4.5625 (+4 B). NVFP4 encodes read their input
+twice (tensor amax first, then the codes), which the method's per-tensor scale requires.
+
+Prints one JSON line on stdout; per-op timings go to stderr (and --detail FILE).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD public spec
+T_FULL, H, D = 131072, 8, 128
+FORMS = (("int4", 64), ("nvfp4", 16))
+KINDS = ("key", "value")
+OPS = ("pack", "unpack", "encode_residual", "decode_residual")
+
+
+def algo_bytes(op: str, fmt: str, n: int) -> float:
+    """Bytes the method must move for one op on n elements (see module docstring)."""
+    meta = 0.0625 if fmt == "int4" else 0.0625  # 4 B per 64 (int4) = 1 B per 16 (nvfp4) = 1/16 B/elem
+    code = 0.5
+    extra = 4 if fmt == "nvfp4" else 0
+    if op == "pack":
+        return n * (2 + code + meta) + (n * 2 if fmt == "nvfp4" else 0) + extra
+    if op == "unpack":
+        return n * (code + meta + 2) + extra
+    if op == "encode_residual":
+        return n * (4 + code + meta) + (n * 4 if fmt == "nvfp4" else 0) + extra
+    if op == "decode_residual":
+        return n * (code + meta + 2 + 2) + extra
+    raise ValueError(op)
+
+
+def cpu_baseline(T_sample: int):
+    """The oracle (single-threaded plain C) on the leading T_sample rows of the same workload."""
+    import oracle
+    from workloads import c4_residual_target, c4_tensors
+
+    oracle.build(force=False)
+    d = c4_tensors(0, T=T_sample)
+    data = {"key": (d["K"], c4_residual_target(d["K"], stream=0)), "value": (d["V"], c4_residual_target(d["V"], stream=1))}
+    n = T_sample * H * D
+    total_bytes = 0.0
+    t0 = time.perf_counter()
+    for fmt, G in FORMS:
+        for kind in KINDS:
+            X0, X1 = data[kind]
+            p = oracle.pack(X0, kind, fmt, G)
+            R0 = oracle.unpack(p)
+            r = oracle.encode_residual(X1, R0, kind, fmt, G)
+            oracle.decode_residual(r, R0)
+            total_bytes += sum(algo_bytes(op, fmt, n) for op in OPS)
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"leading {T_sample} of {T_FULL} tokens (H=8, D=128), all 16 ops of one step, "
+                      f"single-threaded C oracle, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--tokens", type=int, default=T_FULL, help="T (default: the bulk workload)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--detail", default="")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this codec build measures one GPU only; multi-GPU runs are not part of it "
+              f"(got --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import kv_cache_quantization_kvq_amd as kvq
+    from workloads import c4_residual_target, c4_tensors
+
+    dev = torch.device("cuda:0")
+    T = args.tokens
+    n = T * H * D
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_gen = time.perf_counter()
+    d = c4_tensors(0, T=T)
+    X = {}
+    for kind, key, stream in (("key", "K", 0), ("value", "V", 1)):
+        X[kind] = (to_dev(d[key]), to_dev(c4_residual_target(d[key], stream=stream)))
+    del d
+    print(f"inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    # preallocated outputs
+    bufs = {}
+    for fmt, G in FORMS:
+        for kind in KINDS:
+            bufs[(fmt, kind)] = dict(
+                p=kvq.alloc_packed(fmt, kind, G, T, H, D, T, dev),
+                r=kvq.alloc_packed(fmt, kind, G, T, H, D, T, dev),
+                R0=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
+                R1=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
+            )
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        k = 0
+        for fmt, G in FORMS:
+            for kind in KINDS:
+                b = bufs[(fmt, kind)]
+                x0, x1 = X[kind]
+                if events is not None:
+                    events[k].record(stream)
+                kvq.pack(x0, kind, fmt, G, out=b["p"])
+                if events is not None:
+                    events[k + 1].record(stream)
+                kvq.unpack(b["p"], out=b["R0"])
+                if events is not None:
+                    events[k + 2].record(stream)
+                kvq.encode_residual(x1, b["R0"], kind, fmt, G, out=b["r"])
+                if events is not None:
+                    events[k + 3].record(stream)
+                kvq.decode_residual(b["r"], b["R0"], out=b["R1"])
+                if events is not None:
+                    events[k + 4].record(stream)
+                k += 5
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    n_ev = 5 * len(FORMS) * len(KINDS)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-op durations from the events (same stream as the kernels)
+    per_op = {}
+    k = 0
+    for fmt, G in FORMS:
+        for kind in KINDS:
+            for j, op in enumerate(OPS):
+                ms = [events[s][k + j].elapsed_time(events[s][k + j + 1]) for s in range(args.steps)]
+                ms = np.array(ms)
+                nbytes = algo_bytes(op, fmt, n)
+                per_op[f"{fmt}-{kind}-{op}"] = dict(
+                    mean_us=float(ms.mean() * 1e3), p50_us=float(np.percentile(ms, 50) * 1e3),
+                    p90_us=float(np.percentile(ms, 90) * 1e3), bytes=nbytes,
+                    gbs=float(nbytes / (np.percentile(ms, 50) * 1e-3) / 1e9),
+                    launches=2 if (fmt == "nvfp4" and op in ("pack", "encode_residual")) else 1)
+            k += 5
+    step_bytes = sum(v["bytes"] for v in per_op.values())
+    ms_per_step = elapsed / args.steps * 1e3
+    value = step_bytes / (elapsed / args.steps) / 1e9
+
+    # dominant single-kernel op: the one-launch op with the largest share of the step
+    single = {k: v for k, v in per_op.items() if v["launches"] == 1}
+    dom_name, dom = max(single.items(), key=lambda kv: kv[1]["mean_us"])
+    achieved = dom["bytes"] / (dom["mean_us"] * 1e-6) / 1e9
+
+    for name, v in per_op.items():
+        print(f"{name:34s} mean {v['mean_us']:8.1f} us  p50 {v['p50_us']:8.1f}  p90 {v['p90_us']:8.1f}  "
+              f"{v['gbs']:7.1f} GB/s  {100 * v['gbs'] / PEAK_HBM_GBS:5.1f}% of peak", file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(min(args.cpu_sample_tokens, T))
+
+    line = {
+        "metric": "codec GB/s and % HBM peak (pack/unpack/residual), INT4-G64 & NVFP4-G16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "bulk codec: T=131072 tokens, H_kv=8, D=128, bf16 Student-t nu=3; INT4-G64 and "
+                        "NVFP4-G16, K and V; pack, unpack, residual encode, residual decode per step",
+            "T": T, "H_kv": H, "D": D, "bytes_per_step": step_bytes,
+            "pct_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom_name,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"line": line, "per_op": per_op}, f, indent=1)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

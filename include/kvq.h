@@ -1,0 +1,181 @@
+/*
+ * kvq.h -- C ABI of the KV-cache quantization codec for AMD Instinct MI355X (gfx950).
+ *
+ * The library packs and unpacks one request/layer's logical [token, KV head, channel] K or V
+ * tensor, and encodes/decodes cross-loop residuals against a reconstructed predecessor, in two
+ * 4-bit formats. All compute runs in HIP kernels on the caller's stream.
+ *
+ * Sources (by page title and section):
+ *   [PR166] vllm-rlt pull request #166, "INT4 KV packing/unpacking and cross-loop residual
+ *           reconstruction": "Purpose" (API, formats, group axes, residual semantics), the
+ *           first codec review (FP32 codes before FP16 metadata; 4.5 bits per element), the
+ *           interface review (payload-only storage accounting; no device sync in validation).
+ *   [PR408] FreeToken pull request #408, "feat(kvcache): add nvfp4 kv quantization":
+ *           "Summary" (76 B per D=128 row; graph-safe writes with device-resident ids) and the
+ *           nvfp4 codec-port commit (low-nibble-first packing; quantize against the stored,
+ *           rounded block scale).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are bf16, logical [T, H, D] (token, KV head, channel), with channel stride 1 and
+ *     arbitrary non-negative token/head strides in elements (e.g. K as a view into a fused QKV
+ *     buffer). All data pointers are device pointers.
+ *   - The library never allocates, frees or synchronizes. The caller allocates every buffer;
+ *     kvq_plane_bytes gives the size of each packed plane.
+ *   - Every call is asynchronous on `stream` and only enqueues kernels (no memset/memcpy
+ *     nodes), so it may be captured into a HIP graph.
+ *   - Host-detectable errors return a status before anything is enqueued. A failed launch
+ *     returns KVQ_ERR_HIP. Data preconditions that only the device can see (finite inputs,
+ *     positions in range and distinct) are not checked on the hot path; see
+ *     kvq_validate_positions.
+ *   - Sizes: rows, H, D < 2^31 and rows*H*D < 2^36 elements.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_NULL = 1,      /* a required pointer is NULL */
+    KVQ_ERR_SHAPE = 2,     /* negative or too large size, or shapes that disagree */
+    KVQ_ERR_LAYOUT = 3,    /* negative stride, or out/prev partially overlapping */
+    KVQ_ERR_FORMAT = 4,    /* unknown format or kind */
+    KVQ_ERR_GROUP = 5,     /* group size invalid for the format (NVFP4 requires 16) */
+    KVQ_ERR_DTYPE = 6,     /* tensor dtype other than bf16 */
+    KVQ_ERR_MISMATCH = 7,  /* packed descriptor disagrees with the tensors it is used with */
+    KVQ_ERR_HIP = 8,       /* a kernel launch failed */
+    KVQ_ERR_WORKSPACE = 9  /* NVFP4 encode without a workspace */
+} kvq_status;
+
+/* Group axis follows the kind ([PR166] "Purpose", third bullet): KEY groups run over token rows
+ * for each (head, channel); VALUE groups run over channels for each (token, head). */
+typedef enum kvq_kind { KVQ_KEY = 0, KVQ_VALUE = 1 } kvq_kind;
+
+/* KVQ_INT4: affine groups, FP32 math, FP16 minimum and scale, default group size 64.
+ * KVQ_NVFP4: E2M1 codes (nearest-even), one E4M3 scale per 16 values, one FP32 global
+ * multiplier per encoded tensor; group size 16 only. ([PR166] "Purpose", second bullet.) */
+typedef enum kvq_format { KVQ_INT4 = 0, KVQ_NVFP4 = 1 } kvq_format;
+
+typedef enum kvq_dtype { KVQ_BF16 = 0 } kvq_dtype;
+
+/* A strided bf16 view: element (t, h, d) is at data + t*stride_t + h*stride_h + d (elements). */
+typedef struct kvq_tensor {
+    void* data;
+    int32_t dtype; /* kvq_dtype */
+    int32_t reserved;
+    int64_t T, H, D;
+    int64_t stride_t, stride_h;
+} kvq_tensor;
+
+/* One encoded tensor ([PR166] "Purpose", first bullet: packed objects carry format, axis and
+ * group size). The caller owns every plane; the library fills the scalar fields on encode.
+ *   codes        [rows, H, ceil(D/2)] u8: channel 2j in the low nibble, 2j+1 in the high
+ *                nibble ([PR408] codec-port commit: low first); an odd D leaves the last
+ *                high nibble 0.
+ *   meta0        INT4: f16 group minimums; NVFP4: E4M3 block scales (u8).
+ *   meta1        INT4: f16 group scales;   NVFP4: unused (NULL).
+ *                Metadata shape: KEY [ceil(rows/G), H, D], VALUE [rows, H, ceil(D/G)].
+ *   global_scale NVFP4: one float, the encoding multiplier g (decode scale = block/g).
+ *   positions    sparse residual: the owned int32 copy of the position map, [rows]. A non-NULL
+ *                pointer is what marks a residual sparse; with rows == 0 it is not read.
+ *   rows         T for a dense tensor, M for a sparse residual; full_T is the row count of the
+ *                tensor it reconstructs (== rows when dense). */
+typedef struct kvq_packed {
+    int32_t format;     /* kvq_format */
+    int32_t kind;       /* kvq_kind */
+    int32_t group_size;
+    int32_t dtype;      /* dtype of the tensor it decodes to (kvq_dtype) */
+    int64_t rows, H, D;
+    int64_t full_T;
+    uint8_t* codes;
+    void* meta0;
+    void* meta1;
+    float* global_scale;
+    int32_t* positions;
+} kvq_packed;
+
+/* Plane indices for kvq_plane_bytes. */
+enum { KVQ_PLANE_CODES = 0, KVQ_PLANE_META0 = 1, KVQ_PLANE_META1 = 2, KVQ_PLANE_GLOBAL = 3,
+       KVQ_PLANE_POSITIONS = 4, KVQ_NUM_PLANES = 5 };
+
+/* Library version string (static storage). */
+const char* kvq_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* kvq_status_string(kvq_status status);
+
+/* Exact payload bytes of one encoded tensor ([PR166] interface review: payload only, no
+ * allocator slack, no decode scratch): rows*H*ceil(D/2) code bytes + 4 B per INT4 group or
+ * 1 B per NVFP4 block + 4 B global scale (NVFP4) + 4 B per row of an owned position map
+ * (sparse != 0). group_size 0 selects the format default. Host-only; writes *bytes.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_FORMAT, KVQ_ERR_GROUP. */
+kvq_status kvq_storage_bytes(kvq_format format, kvq_kind kind, int32_t group_size, int64_t rows, int64_t H,
+                             int64_t D, int32_t sparse, uint64_t* bytes);
+
+/* Per-plane byte sizes (sizes[KVQ_NUM_PLANES], indexed by KVQ_PLANE_*); they sum to
+ * kvq_storage_bytes. Host-only. Same errors as kvq_storage_bytes. */
+kvq_status kvq_plane_bytes(kvq_format format, kvq_kind kind, int32_t group_size, int64_t rows, int64_t H,
+                           int64_t D, int32_t sparse, uint64_t sizes[KVQ_NUM_PLANES]);
+
+/* Bytes of device workspace an NVFP4 encode needs (a tensor-wide max accumulator and a block
+ * counter). The caller zero-fills it once before first use; every completed call leaves it
+ * zeroed again. Calls that may run concurrently need distinct workspaces. */
+size_t kvq_workspace_bytes(void);
+
+/* pack_kv ([PR166] "Purpose" usage example, first line): encode x into *out.
+ * The caller sets out->codes, out->meta0, out->meta1 (INT4), out->global_scale (NVFP4); the
+ * library sets the scalar fields and out->positions = NULL. group_size 0 = format default
+ * (INT4 64, NVFP4 16). NVFP4 needs `workspace` (kvq_workspace_bytes, zeroed); INT4 ignores it.
+ * The NVFP4 global multiplier is recomputed on every call ([PR166] "Purpose", paragraph after
+ * the example). Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, DTYPE, WORKSPACE, HIP. */
+kvq_status kvq_pack(const kvq_tensor* x, kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out,
+                    void* workspace, hipStream_t stream);
+
+/* unpack_kv ([PR166] "Purpose" usage example, second line): decode *p into the bf16 view
+ * `out` of shape [p->rows, p->H, p->D]. Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, DTYPE,
+ * MISMATCH, HIP. */
+kvq_status kvq_unpack(const kvq_packed* p, const kvq_tensor* out, hipStream_t stream);
+
+/* encode_residual ([PR166] "Purpose", fourth bullet and usage example, third line): encode
+ * cur - prev, subtracted in the input dtype (one binary32 subtraction rounded to bf16), where
+ * prev is the reconstructed predecessor. Dense when positions == NULL (rows = T); sparse when
+ * positions is non-NULL: a device array of M distinct row indices in [0, T) (not read when
+ * M == 0, but still non-NULL, as is out->positions). Compact row i is
+ * cur[positions[i]] - prev[positions[i]], KEY groups follow compact row order, and the
+ * residual keeps its own copy of the map in out->positions (caller-allocated, M int32).
+ * The residual's format/kind/group size are independent of how prev was produced (mixed-format
+ * chains). Same workspace rule and errors as kvq_pack. */
+kvq_status kvq_encode_residual(const kvq_tensor* cur, const kvq_tensor* prev, const int32_t* positions, int64_t M,
+                               kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out,
+                               void* workspace, hipStream_t stream);
+
+/* decode_residual ([PR166] "Purpose", fourth bullet and usage example, fourth line):
+ * out = prev + unpack(r), both in the input dtype (the decoded residual is rounded to bf16,
+ * then the binary32 sum is rounded to bf16). Sparse: rows not in r->positions are copied from
+ * prev bit for bit (absent rows inherit the predecessor). prev and out are [r->full_T, H, D];
+ * out may be exactly prev (same data and strides: in place, only kept rows are written), but
+ * must not partially overlap it. Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, DTYPE, MISMATCH,
+ * HIP. */
+kvq_status kvq_decode_residual(const kvq_packed* r, const kvq_tensor* prev, const kvq_tensor* out,
+                               hipStream_t stream);
+
+/* Opt-in device-side check of a position map (the codec page's interface review asks that
+ * validation never force a host sync). Writes *status (device int32): 0 = valid, bit 0 = some
+ * position outside [0, T), bit 1 = some position repeated. `scratch` is a device buffer of
+ * ceil(T/32) uint32 words, overwritten. Nothing is read back on the host.
+ * Errors: NULL, SHAPE, HIP. */
+kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* scratch,
+                                  int32_t* status, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

@@ -1,0 +1,71 @@
+"""Build the HIP library ``libkvq.so`` for gfx950 with hipcc (no torch involved)."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkvq.so")
+SOURCES = ["kvq_abi.hip", "kvq_encode.hip", "kvq_decode.hip"]
+HEADERS = ["kvq_device.hpp", "kvq_launch.hpp"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Numerics flags: no fused multiply-add contraction, IEEE-correct fp32 division, denormals kept.
+# Packed fp32 instructions are disabled for all device code.
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+    "-I", INCLUDE,
+    "-I", CSRC,
+]
+
+
+def _compile(src: str, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    # forward real diagnostics but drop the host pass's note about the device-only feature flag
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    for line in (r.stderr or "").splitlines():
+        if line.strip() and noise not in line and "warning generated" not in line and "warnings generated" not in line:
+            sys.stderr.write(line + "\n")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``libkvq.so`` in the package directory. Always rebuilds."""
+    build_dir = os.path.join(PKG, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc link failed")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,377 @@
+// kvq_abi.hip -- the C ABI: argument checks, plane sizes, and kernel dispatch on the caller's
+// stream. Nothing here allocates, frees or synchronizes.
+#include <string.h>
+
+#include "kvq.h"
+#include "kvq_launch.hpp"
+
+using namespace kvq;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxElems = (int64_t)1 << 36;
+constexpr size_t kWorkspaceBytes = 256;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dims_ok(int64_t rows, int64_t H, int64_t D) {
+    if (rows < 0 || H < 0 || D < 0) return false;
+    if (rows >= kMaxDim || H >= kMaxDim || D >= kMaxDim) return false;
+    return (unsigned __int128)rows * (unsigned __int128)H * (unsigned __int128)D < (unsigned __int128)kMaxElems;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2i(int64_t v) {
+    int s = 0;
+    while (((int64_t)1 << s) < v) ++s;
+    return s;
+}
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+FastDiv fastdiv_make(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    f.m = (uint32_t)(((((uint64_t)1 << l) - d) << 32) / d + 1);
+    f.s = l;
+    f.pad = 0;
+    return f;
+}
+
+kvq_status check_kind_format(int kind, int format) {
+    if (kind != KVQ_KEY && kind != KVQ_VALUE) return KVQ_ERR_FORMAT;
+    if (format != KVQ_INT4 && format != KVQ_NVFP4) return KVQ_ERR_FORMAT;
+    return KVQ_OK;
+}
+
+int32_t resolve_group(int format, int32_t G) {
+    if (G == 0) return format == KVQ_INT4 ? 64 : 16;
+    return G;
+}
+
+kvq_status check_group(int format, int32_t G) {
+    if (G < 1) return KVQ_ERR_GROUP;
+    if (format == KVQ_NVFP4 && G != 16) return KVQ_ERR_GROUP;
+    return KVQ_OK;
+}
+
+kvq_status plane_sizes(int format, int kind, int32_t G, int64_t rows, int64_t H, int64_t D, int sparse,
+                       uint64_t s[KVQ_NUM_PLANES]) {
+    kvq_status st = check_kind_format(kind, format);
+    if (st) return st;
+    G = resolve_group(format, G);
+    if ((st = check_group(format, G))) return st;
+    if (!dims_ok(rows, H, D)) return KVQ_ERR_SHAPE;
+    const uint64_t ng = (kind == KVQ_KEY) ? (uint64_t)cdiv(rows, G) * H * D : (uint64_t)rows * H * cdiv(D, G);
+    s[KVQ_PLANE_CODES] = (uint64_t)rows * H * cdiv(D, 2);
+    s[KVQ_PLANE_META0] = (format == KVQ_INT4) ? 2 * ng : ng;
+    s[KVQ_PLANE_META1] = (format == KVQ_INT4) ? 2 * ng : 0;
+    s[KVQ_PLANE_GLOBAL] = (format == KVQ_NVFP4) ? 4 : 0;
+    s[KVQ_PLANE_POSITIONS] = sparse ? 4 * (uint64_t)rows : 0;
+    return KVQ_OK;
+}
+
+kvq_status check_tensor(const kvq_tensor* x) {
+    if (!x) return KVQ_ERR_NULL;
+    if (x->dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (!dims_ok(x->T, x->H, x->D)) return KVQ_ERR_SHAPE;
+    if (x->stride_t < 0 || x->stride_h < 0) return KVQ_ERR_LAYOUT;
+    if (x->T * x->H * x->D > 0 && !x->data) return KVQ_ERR_NULL;
+    return KVQ_OK;
+}
+
+// A strided view reaches [data, data + span) bytes.
+void view_span(const kvq_tensor* x, uintptr_t* lo, uintptr_t* hi) {
+    *lo = (uintptr_t)x->data;
+    if (x->T * x->H * x->D == 0) {
+        *hi = *lo;
+        return;
+    }
+    const int64_t last = (x->T - 1) * x->stride_t + (x->H - 1) * x->stride_h + (x->D - 1);
+    *hi = *lo + (uintptr_t)(last + 1) * 2u;
+}
+
+bool view_vec_ok(const void* data, int64_t st, int64_t sh) {
+    return aligned(data, 16) && (st % 8) == 0 && (sh % 8) == 0;
+}
+
+// Geometry of the 8-channel vector path.
+template <typename Args>
+void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, int rows_per_task) {
+    a.D8 = (int32_t)(D / 8);
+    a.C8 = (int32_t)(H * (D / 8));
+    a.n_slabs = (int32_t)cdiv(a.C8, 64);
+    a.lpg = (G % 8 == 0) ? G / 8 : 1;
+    a.lpg_shift = log2i(a.lpg);
+    a.ngr = a.C8 / a.lpg;
+    a.div_D8 = fastdiv_make((uint32_t)a.D8);
+    a.div_slabs = fastdiv_make((uint32_t)a.n_slabs);
+    a.n_tasks = (uint32_t)(cdiv(rows, rows_per_task) * a.n_slabs);
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+kvq_status encode_common(const kvq_tensor* cur, const kvq_tensor* prev, const int32_t* positions, int64_t M,
+                         int kind, int format, int32_t G, kvq_packed* out, void* workspace, hipStream_t stream) {
+    kvq_status st = check_kind_format(kind, format);
+    if (st) return st;
+    G = resolve_group(format, G);
+    if ((st = check_group(format, G))) return st;
+    if ((st = check_tensor(cur))) return st;
+    if (prev) {
+        if ((st = check_tensor(prev))) return st;
+        if (prev->T != cur->T || prev->H != cur->H || prev->D != cur->D) return KVQ_ERR_SHAPE;
+    }
+    const bool sparse = positions != nullptr;
+    if (M < 0 || (sparse && M > cur->T)) return KVQ_ERR_SHAPE;
+    if (!sparse && M != 0) return KVQ_ERR_SHAPE;
+    const int64_t rows = sparse ? M : cur->T;
+    const int64_t H = cur->H, D = cur->D;
+    if (!out) return KVQ_ERR_NULL;
+    uint64_t sz[KVQ_NUM_PLANES];
+    if ((st = plane_sizes(format, kind, G, rows, H, D, sparse ? 1 : 0, sz))) return st;
+    if (sz[KVQ_PLANE_CODES] && !out->codes) return KVQ_ERR_NULL;
+    if (sz[KVQ_PLANE_META0] && !out->meta0) return KVQ_ERR_NULL;
+    if (sz[KVQ_PLANE_META1] && !out->meta1) return KVQ_ERR_NULL;
+    if (sz[KVQ_PLANE_GLOBAL] && !out->global_scale) return KVQ_ERR_NULL;
+    if (sz[KVQ_PLANE_POSITIONS] && !out->positions) return KVQ_ERR_NULL;
+    if (format == KVQ_NVFP4 && !workspace) return KVQ_ERR_WORKSPACE;
+
+    out->format = format;
+    out->kind = kind;
+    out->group_size = G;
+    out->dtype = KVQ_BF16;
+    out->rows = rows;
+    out->H = H;
+    out->D = D;
+    out->full_T = cur->T;
+    if (!sparse) out->positions = nullptr;
+
+    const int64_t n = rows * H * D;
+    if (n == 0) {
+        hipError_t e = hipSuccess;
+        if (format == KVQ_NVFP4) e = launch_set_global(out->global_scale, 0x3F800000u, stream);  // g = 1
+        if (e == hipSuccess && sparse && M > 0) e = launch_copy_i32(out->positions, positions, M, stream);
+        return hip_status(e);
+    }
+
+    EncArgs a;
+    memset(&a, 0, sizeof a);
+    a.cur = static_cast<const uint16_t*>(cur->data);
+    a.cst = cur->stride_t;
+    a.csh = cur->stride_h;
+    if (prev) {
+        a.prev = static_cast<const uint16_t*>(prev->data);
+        a.pst = prev->stride_t;
+        a.psh = prev->stride_h;
+    }
+    a.pos = positions;
+    a.pos_out = sparse ? out->positions : nullptr;
+    a.rows = rows;
+    a.H = (int32_t)H;
+    a.D = (int32_t)D;
+    a.G = G;
+    a.codes = out->codes;
+    a.meta0 = out->meta0;
+    a.meta1 = out->meta1;
+    a.gscale = out->global_scale;
+    a.ws = static_cast<uint32_t*>(workspace);
+
+    // vector path eligibility
+    bool vec = (D % 8 == 0) && view_vec_ok(cur->data, cur->stride_t, cur->stride_h) && aligned(out->codes, 4) &&
+               (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
+    if (prev) vec = vec && view_vec_ok(prev->data, prev->stride_t, prev->stride_h);
+    if (kind == KVQ_VALUE) {
+        vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8) && (G / 8) <= 16;
+    } else if (format == KVQ_INT4) {
+        vec = vec && (G == 16 || G == 32 || G == 64 || G == 128) && aligned(out->meta0, 16) && aligned(out->meta1, 16);
+    } else {
+        vec = vec && aligned(out->meta0, 8);
+    }
+    if (vec) {
+        if (kind == KVQ_VALUE) {
+            fill_vec_geometry(a, rows, H, D, G, 4);
+        } else {
+            fill_vec_geometry(a, rows, H, D, G, G);
+        }
+        a.div_C8 = fastdiv_make((uint32_t)a.C8);
+    }
+
+    hipError_t e = hipSuccess;
+    if (format == KVQ_NVFP4) e = launch_amax(a, prev != nullptr, sparse, vec, stream);
+    if (e == hipSuccess) e = launch_encode(format, kind, a, prev != nullptr, sparse, vec, stream);
+    return hip_status(e);
+}
+
+kvq_status check_packed(const kvq_packed* p) {
+    if (!p) return KVQ_ERR_NULL;
+    kvq_status st = check_kind_format(p->kind, p->format);
+    if (st) return st;
+    if ((st = check_group(p->format, p->group_size))) return st;
+    if (p->dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (!dims_ok(p->rows, p->H, p->D)) return KVQ_ERR_SHAPE;
+    uint64_t sz[KVQ_NUM_PLANES];
+    if ((st = plane_sizes(p->format, p->kind, p->group_size, p->rows, p->H, p->D, 0, sz))) return st;
+    if (sz[KVQ_PLANE_CODES] && !p->codes) return KVQ_ERR_NULL;
+    if (sz[KVQ_PLANE_META0] && !p->meta0) return KVQ_ERR_NULL;
+    if (sz[KVQ_PLANE_META1] && !p->meta1) return KVQ_ERR_NULL;
+    if (p->format == KVQ_NVFP4 && !p->global_scale) return KVQ_ERR_NULL;
+    return KVQ_OK;
+}
+
+// Decode p's rows into `out` (optionally adding prev), scattering by `positions` if given.
+kvq_status decode_common(const kvq_packed* p, const kvq_tensor* prev, const kvq_tensor* out,
+                         const int32_t* positions, hipStream_t stream) {
+    const int64_t rows = p->rows, H = p->H, D = p->D;
+    if (rows * H * D == 0) return KVQ_OK;
+    DecArgs a;
+    memset(&a, 0, sizeof a);
+    a.codes = p->codes;
+    a.meta0 = p->meta0;
+    a.meta1 = p->meta1;
+    a.gscale = p->global_scale;
+    a.pos = positions;
+    if (prev) {
+        a.prev = static_cast<const uint16_t*>(prev->data);
+        a.pst = prev->stride_t;
+        a.psh = prev->stride_h;
+    }
+    a.out = static_cast<uint16_t*>(out->data);
+    a.ost = out->stride_t;
+    a.osh = out->stride_h;
+    a.rows = rows;
+    a.H = (int32_t)H;
+    a.D = (int32_t)D;
+    a.G = p->group_size;
+    const int32_t G = p->group_size;
+    bool vec = (D % 8 == 0) && view_vec_ok(out->data, out->stride_t, out->stride_h) && aligned(p->codes, 4) &&
+               (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
+    if (prev) vec = vec && view_vec_ok(prev->data, prev->stride_t, prev->stride_h);
+    if (p->kind == KVQ_VALUE) {
+        vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8);
+    } else {
+        vec = vec && (G % 8 == 0) &&
+              (p->format == KVQ_INT4 ? (aligned(p->meta0, 16) && aligned(p->meta1, 16)) : aligned(p->meta0, 8));
+    }
+    if (vec) fill_vec_geometry(a, rows, H, D, G, 8);
+    return hip_status(launch_decode(p->format, p->kind, a, prev != nullptr, positions != nullptr, vec, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_version(void) { return "kvq 0.1.0 gfx950"; }
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_NULL: return "null pointer";
+        case KVQ_ERR_SHAPE: return "bad shape";
+        case KVQ_ERR_LAYOUT: return "bad layout";
+        case KVQ_ERR_FORMAT: return "bad format or kind";
+        case KVQ_ERR_GROUP: return "bad group size";
+        case KVQ_ERR_DTYPE: return "unsupported dtype";
+        case KVQ_ERR_MISMATCH: return "descriptor does not match tensor";
+        case KVQ_ERR_HIP: return "HIP launch failed";
+        case KVQ_ERR_WORKSPACE: return "missing workspace";
+    }
+    return "unknown status";
+}
+
+kvq_status kvq_storage_bytes(kvq_format format, kvq_kind kind, int32_t group_size, int64_t rows, int64_t H, int64_t D,
+                             int32_t sparse, uint64_t* bytes) {
+    if (!bytes) return KVQ_ERR_NULL;
+    uint64_t s[KVQ_NUM_PLANES];
+    kvq_status st = plane_sizes(format, kind, group_size, rows, H, D, sparse, s);
+    if (st) return st;
+    *bytes = s[0] + s[1] + s[2] + s[3] + s[4];
+    return KVQ_OK;
+}
+
+kvq_status kvq_plane_bytes(kvq_format format, kvq_kind kind, int32_t group_size, int64_t rows, int64_t H, int64_t D,
+                           int32_t sparse, uint64_t sizes[KVQ_NUM_PLANES]) {
+    if (!sizes) return KVQ_ERR_NULL;
+    return plane_sizes(format, kind, group_size, rows, H, D, sparse, sizes);
+}
+
+size_t kvq_workspace_bytes(void) { return kWorkspaceBytes; }
+
+kvq_status kvq_pack(const kvq_tensor* x, kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out,
+                    void* workspace, hipStream_t stream) {
+    return encode_common(x, nullptr, nullptr, 0, kind, format, group_size, out, workspace, stream);
+}
+
+kvq_status kvq_encode_residual(const kvq_tensor* cur, const kvq_tensor* prev, const int32_t* positions, int64_t M,
+                               kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out,
+                               void* workspace, hipStream_t stream) {
+    if (!prev) return KVQ_ERR_NULL;
+    if (!positions && M != 0) return KVQ_ERR_SHAPE;
+    return encode_common(cur, prev, positions, M, kind, format, group_size, out, workspace, stream);
+}
+
+kvq_status kvq_unpack(const kvq_packed* p, const kvq_tensor* out, hipStream_t stream) {
+    kvq_status st = check_packed(p);
+    if (st) return st;
+    if ((st = check_tensor(out))) return st;
+    if (out->T != p->rows || out->H != p->H || out->D != p->D) return KVQ_ERR_MISMATCH;
+    return decode_common(p, nullptr, out, nullptr, stream);
+}
+
+kvq_status kvq_decode_residual(const kvq_packed* r, const kvq_tensor* prev, const kvq_tensor* out,
+                               hipStream_t stream) {
+    kvq_status st = check_packed(r);
+    if (st) return st;
+    if ((st = check_tensor(prev))) return st;
+    if ((st = check_tensor(out))) return st;
+    if (prev->H != r->H || prev->D != r->D || prev->T != r->full_T) return KVQ_ERR_MISMATCH;
+    if (out->T != prev->T || out->H != prev->H || out->D != prev->D) return KVQ_ERR_SHAPE;
+    const bool sparse = r->positions != nullptr;
+    if (!sparse && r->rows != r->full_T) return KVQ_ERR_MISMATCH;
+    if (sparse && r->rows > r->full_T) return KVQ_ERR_MISMATCH;
+
+    const bool same = out->data == prev->data && out->stride_t == prev->stride_t && out->stride_h == prev->stride_h;
+    if (!same) {
+        uintptr_t plo, phi, olo, ohi;
+        view_span(prev, &plo, &phi);
+        view_span(out, &olo, &ohi);
+        if (plo < ohi && olo < phi) return KVQ_ERR_LAYOUT;  // partial overlap
+    }
+    if (sparse && !same) {
+        CopyArgs c;
+        memset(&c, 0, sizeof c);
+        c.src = static_cast<const uint16_t*>(prev->data);
+        c.sst = prev->stride_t;
+        c.ssh = prev->stride_h;
+        c.dst = static_cast<uint16_t*>(out->data);
+        c.dst_t = out->stride_t;
+        c.dsh = out->stride_h;
+        c.T = prev->T;
+        c.H = (int32_t)prev->H;
+        c.D = (int32_t)prev->D;
+        const bool vec = (prev->D % 8 == 0) && view_vec_ok(prev->data, prev->stride_t, prev->stride_h) &&
+                         view_vec_ok(out->data, out->stride_t, out->stride_h) &&
+                         (uint64_t)prev->T * (uint64_t)(prev->H * prev->D / 8) < ((uint64_t)1 << 31);
+        if (vec) {
+            c.C8 = (int32_t)(prev->H * prev->D / 8);
+            c.div_C8 = fastdiv_make((uint32_t)(c.C8 > 0 ? c.C8 : 1));
+            c.div_D8 = fastdiv_make((uint32_t)(prev->D / 8 > 0 ? prev->D / 8 : 1));
+        }
+        if (prev->T * prev->H * prev->D > 0) {
+            hipError_t e = launch_copy_rows(c, vec, stream);
+            if (e != hipSuccess) return KVQ_ERR_HIP;
+        }
+    }
+    return decode_common(r, prev, out, r->positions, stream);
+}
+
+kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,
+                                  hipStream_t stream) {
+    if (M < 0 || T < 0 || T >= kMaxDim || M >= kMaxDim) return KVQ_ERR_SHAPE;
+    if (!status || (M > 0 && !positions) || (T > 0 && !scratch)) return KVQ_ERR_NULL;
+    return hip_status(launch_validate_positions(positions, M, T, scratch, status, stream));
+}
+
+}  // extern "C"

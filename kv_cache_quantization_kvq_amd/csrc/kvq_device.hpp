@@ -1,0 +1,254 @@
+// kvq_device.hpp -- device-side numerics of the KV codec (gfx950).
+//
+// Every conversion here is integer arithmetic on bit patterns or exact float scaling, so the
+// results do not depend on the hardware conversion instructions' rounding or denormal modes.
+// Floating-point steps that the format defines as single binary32 operations are written as
+// separate __fadd_rn/__fmul_rn/__fsub_rn calls (the library is also built with
+// -ffp-contract=off), and divisions use the IEEE-correct '/' (the library is built with
+// correctly rounded fp32 division).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// ---- bf16 ------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 -> bf16, round to nearest even. Valid for every non-NaN input; values past the
+// largest finite bf16 (by at least half an ulp) carry into the exponent and give +-inf.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Two bf16 results packed into one word (low element first).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// bf16(fl(a - b)) for the two halves of packed words: the residual subtraction in the input
+// dtype ([PR166] "Purpose", fourth bullet).
+__device__ __forceinline__ uint32_t sub_bf16x2(uint32_t a, uint32_t b) {
+    return pack_bf16x2(__fsub_rn(bf16lo(a), bf16lo(b)), __fsub_rn(bf16hi(a), bf16hi(b)));
+}
+
+// ---- f16 (INT4 metadata) --------------------------------------------------------------------
+
+// binary32 -> binary16 bits, round to nearest even, gradual underflow, overflow to inf.
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+    uint32_t x = __float_as_uint(f);
+    uint32_t sign = (x >> 16) & 0x8000u;
+    uint32_t ax = x & 0x7FFFFFFFu;
+    if (ax >= 0x477FF000u) return sign | 0x7C00u;  // >= 65520: rounds to inf
+    if (ax >= 0x38800000u) {                        // >= 2^-14: normal half
+        uint32_t r = ax + 0x0FFFu + ((ax >> 13) & 1u);
+        return sign | ((r >> 13) - (112u << 10));
+    }
+    // subnormal half: multiple of 2^-24; scaling by 2^24 is exact, rint is nearest-even
+    float a = __uint_as_float(ax) * 16777216.0f;
+    return sign | (uint32_t)__builtin_rintf(a);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    uint32_t sign = (h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1Fu;
+    uint32_t m = h & 0x3FFu;
+    if (e == 0) return __uint_as_float(sign | __float_as_uint((float)m * 5.9604644775390625e-8f));
+    if (e == 31) return __uint_as_float(sign | 0x7F800000u | (m << 13));
+    return __uint_as_float(sign | ((e + 112u) << 23) | (m << 13));
+}
+
+// ---- E4M3 (NVFP4 block scales) --------------------------------------------------------------
+
+// Non-negative binary32 s <= 448 -> E4M3fn code, nearest even, with E4M3 subnormals (k * 2^-9).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+    uint32_t x = __float_as_uint(s);
+    if (x >= 0x3C800000u) {  // s >= 2^-6: 3 mantissa bits, rebias exponent 127 -> 7
+        uint32_t r = x + 0x7FFFFu + ((x >> 20) & 1u);
+        return (r >> 20) - (120u << 3);
+    }
+    return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scaling, then nearest-even
+}
+
+// E4M3fn code (sign bit clear, finite) -> binary32, exact.
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+    uint32_t E = (b >> 3) & 0xFu, M = b & 7u;
+    if (E == 0) return (float)M * 0.001953125f;  // M * 2^-9
+    return __uint_as_float(((E + 120u) << 23) | (M << 20));
+}
+
+// ---- E2M1 (NVFP4 codes) ---------------------------------------------------------------------
+
+// Magnitude code of |q| on {0, .5, 1, 1.5, 2, 3, 4, 6}, nearest with ties to the even code:
+// the half-way points 0.25, 1.25, 2.5, 5 go down, 0.75, 1.75, 3.5 go up; anything above 5
+// saturates to 6 (code 7). Written as threshold counts.
+__device__ __forceinline__ uint32_t e2m1_mag(float q) {
+    float m = __builtin_fabsf(q);
+    return (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) + (uint32_t)(m >= 1.75f) +
+           (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
+}
+
+// Signed E2M1 code -> binary32 value (exact): exponent bits 2..1 with bias 1, mantissa bit 0,
+// subnormal 0.5; bit 3 is the sign.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+    uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    uint32_t mag = (e == 0) ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
+    return __uint_as_float(mag | ((c & 8u) << 28));
+}
+
+// ---- sortable keys --------------------------------------------------------------------------
+
+// bf16 bit pattern -> int with the order of IEEE totalOrder on finite values (-0 < +0):
+// negative patterns have their magnitude bits inverted.
+__device__ __forceinline__ int bf16_key(uint32_t b16) {
+    int s = (int)(int16_t)(uint16_t)b16;
+    return s ^ ((s >> 31) & 0x7FFF);
+}
+// inverse of bf16_key (an involution on the low 16 bits)
+__device__ __forceinline__ float key_to_f32(int k) {
+    uint32_t b = (uint32_t)(k ^ ((k >> 31) & 0x7FFF)) & 0xFFFFu;
+    return __uint_as_float(b << 16);
+}
+
+// Packed 16-bit lanes: two keys per 32-bit word.
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ short2_t as_s2(uint32_t w) { return __builtin_bit_cast(short2_t, w); }
+__device__ __forceinline__ uint32_t s2_as_u(short2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ ushort2_t as_us2(uint32_t w) { return __builtin_bit_cast(ushort2_t, w); }
+__device__ __forceinline__ uint32_t us2_as_u(ushort2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// keys of the two bf16 halves of a word (per-half arithmetic shift, mask, xor)
+__device__ __forceinline__ short2_t keys2(uint32_t w) {
+    short2_t v = as_s2(w);
+    short2_t sgn = v >> (short2_t){15, 15};
+    return v ^ (sgn & (short2_t){0x7FFF, 0x7FFF});
+}
+__device__ __forceinline__ short2_t min2(short2_t a, short2_t b) { return __builtin_elementwise_min(a, b); }
+__device__ __forceinline__ short2_t max2(short2_t a, short2_t b) { return __builtin_elementwise_max(a, b); }
+__device__ __forceinline__ ushort2_t umax2(ushort2_t a, ushort2_t b) { return __builtin_elementwise_max(a, b); }
+// magnitudes |x| of both halves as unsigned 16-bit patterns (order of |x| = unsigned order)
+__device__ __forceinline__ ushort2_t mag2(uint32_t w) { return as_us2(w & 0x7FFF7FFFu); }
+
+// ---- cross-lane (DPP) -----------------------------------------------------------------------
+
+// Row-local data-parallel-primitive moves. All patterns read a valid lane, so no lane keeps a
+// stale value. quad_perm [1,0,3,2] = 0xB1 (xor 1), [2,3,0,1] = 0x4E (xor 2),
+// row_half_mirror = 0x141 (i -> 7-i within 8), row_mirror = 0x140 (i -> 15-i within 16).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// All-reduce over aligned groups of `lanes` lanes (1, 2, 4, 8 or 16; uniform across the wave).
+template <typename Op>
+__device__ __forceinline__ uint32_t group_allreduce(uint32_t v, int lanes, Op op) {
+    if (lanes >= 2) v = op(v, dpp<0xB1>(v));
+    if (lanes >= 4) v = op(v, dpp<0x4E>(v));
+    if (lanes >= 8) v = op(v, dpp<0x141>(v));
+    if (lanes >= 16) v = op(v, dpp<0x140>(v));
+    return v;
+}
+
+// ---- integer division by a runtime constant --------------------------------------------------
+
+// n / d for 32-bit n with a precomputed multiplier (round-up method): t = mulhi(n, m),
+// q = (t + n) >> s, evaluated in 64 bits. Host side fills it with fastdiv_make().
+struct FastDiv {
+    uint32_t d, m, s, pad;
+};
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    uint32_t t = __umulhi(n, f.m);
+    return (uint32_t)(((uint64_t)t + n) >> f.s);
+}
+
+// ---- INT4 element code ----------------------------------------------------------------------
+
+// Per-group constants of an INT4 group: the minimum, the FP32 scale fl(fl(mx - mn) / 15) and
+// its reciprocal. A scale of 0 takes rcp = 0 (every code 0); a scale whose reciprocal
+// overflows sets `exact` so that every member uses the division.
+struct Int4Group {
+    float mn, scale, rcp;
+    bool exact;
+};
+
+__device__ __forceinline__ Int4Group int4_group(float mn, float mx) {
+    Int4Group g;
+    g.mn = mn;
+    float range = __fsub_rn(mx, mn);
+    g.scale = range / 15.0f;
+    float r = (g.scale != 0.0f) ? 1.0f / g.scale : 0.0f;
+    g.exact = __builtin_isinf(r);
+    g.rcp = r;
+    return g;
+}
+
+// code = clamp(rne(fl(fl(x - mn) / scale)), 0, 15), bit-exact with the IEEE division.
+// Fast path: q' = fl(d * fl(1/scale)) differs from fl(d/scale) by at most 3*2^-24*q + tiny
+// (q <= 15 + 2^-19), i.e. below 2^-19; whenever q' is farther than 2^-17 from a half-integer,
+// both round to the same integer. Otherwise (or when 1/scale overflowed) divide.
+__device__ __forceinline__ uint32_t int4_code(float x, const Int4Group& g) {
+    float d = __fsub_rn(x, g.mn);
+    float q = __fmul_rn(d, g.rcp);
+    float c = __builtin_rintf(q);
+    if (__builtin_expect(g.exact || __builtin_fabsf(__fsub_rn(q, c)) > 0.4999923706054688f, 0)) {
+        c = __builtin_rintf(d / g.scale);
+    }
+    c = __builtin_fminf(c, 15.0f);
+    return (uint32_t)c;
+}
+
+// INT4 decode: bf16(fl(fl(c * scale16) + min16)).
+__device__ __forceinline__ float int4_value(uint32_t c, float s16, float m16) {
+    return __fadd_rn(__fmul_rn((float)c, s16), m16);
+}
+
+// ---- NVFP4 block constants ------------------------------------------------------------------
+
+// Block scale from the block amax (bf16 magnitude bits) and the tensor multiplier g:
+// s = min(fl(g * fl(bamax / 6)), 448); code = e4m3(s); decode scale s_dec = fl(f32(code) / g);
+// element multiplier r = fl(1 / s_dec), 0 when the code is 0, with `div` set when the
+// reciprocal overflows (then q = fl(x / s_dec)).
+struct Fp4Block {
+    uint32_t code;
+    float s_dec, rcp;
+    bool div;
+};
+
+__device__ __forceinline__ Fp4Block fp4_block(uint32_t bamax_bits, float g) {
+    Fp4Block b;
+    float bamax = bf16_to_f32(bamax_bits);
+    float t6 = bamax / 6.0f;
+    float s = __fmul_rn(g, t6);
+    s = (s <= 448.0f) ? s : 448.0f;  // also maps +inf to 448
+    b.code = e4m3_encode(s);
+    float sf = e4m3_decode(b.code);
+    b.s_dec = sf / g;
+    float r = (sf != 0.0f) ? 1.0f / b.s_dec : 0.0f;
+    b.div = __builtin_isinf(r);
+    b.rcp = r;
+    return b;
+}
+
+__device__ __forceinline__ uint32_t fp4_code(float x, const Fp4Block& b) {
+    float q = b.div ? (x / b.s_dec) : __fmul_rn(x, b.rcp);
+    return e2m1_mag(q) | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// NVFP4 global multiplier from the tensor amax (bf16 magnitude bits): fl(2688 / amax);
+// amax == 0 -> 1; an overflowing quotient -> FLT_MAX.
+__device__ __forceinline__ float fp4_global(uint32_t amax_bits) {
+    float amax = bf16_to_f32(amax_bits);
+    if (amax == 0.0f) return 1.0f;
+    float g = 2688.0f / amax;
+    return __builtin_isinf(g) ? 3.4028234663852886e38f : g;
+}
+
+}  // namespace kvq

@@ -1,0 +1,78 @@
+// kvq_launch.hpp -- argument blocks and launchers shared by the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.hpp"
+
+namespace kvq {
+
+enum : int { FMT_INT4 = 0, FMT_NVFP4 = 1 };
+enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
+
+// Rows being encoded: row r is source row t = pos ? pos[r] : r; the element value is
+// cur[t, h, d], or bf16(cur[t, h, d] - prev[t, h, d]) for a residual.
+struct EncArgs {
+    const uint16_t* cur;
+    int64_t cst, csh;
+    const uint16_t* prev;  // residual only
+    int64_t pst, psh;
+    const int32_t* pos;    // sparse residual only
+    int32_t* pos_out;      // owned copy of pos
+    int64_t rows;
+    int32_t H, D, G;
+    // vector-path geometry: C8 = H*D/8 chunks of 8 channels per row; a VALUE group spans
+    // lpg = G/8 = 1 << lpg_shift lanes, ngr = C8 / lpg groups per row
+    int32_t C8, D8, n_slabs, lpg, lpg_shift, ngr;
+    uint32_t n_tasks;
+    FastDiv div_D8, div_slabs, div_C8;
+    uint8_t* codes;
+    void* meta0;
+    void* meta1;
+    float* gscale;
+    uint32_t* ws;  // NVFP4: [0] amax bits, [1] finished-block counter
+};
+
+// Rows being decoded: packed row r goes to output row t = pos ? pos[r] : r; with `prev`
+// the output is bf16(prev[t] + bf16(decoded)).
+struct DecArgs {
+    const uint8_t* codes;
+    const void* meta0;
+    const void* meta1;
+    const float* gscale;
+    const int32_t* pos;
+    const uint16_t* prev;
+    int64_t pst, psh;
+    uint16_t* out;
+    int64_t ost, osh;
+    int64_t rows;
+    int32_t H, D, G;
+    int32_t C8, D8, n_slabs, lpg, lpg_shift, ngr;
+    uint32_t n_tasks;
+    FastDiv div_D8, div_slabs;
+};
+
+struct CopyArgs {
+    const uint16_t* src;
+    int64_t sst, ssh;
+    uint16_t* dst;
+    int64_t dst_t, dsh;
+    int64_t T;
+    int32_t H, D, C8;
+    FastDiv div_C8, div_D8;
+};
+
+// ---- launchers (return hipGetLastError() of the launch) ----
+// vec: the 8-channel vector path is legal for these arguments (alignment, strides, G).
+
+hipError_t launch_amax(const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
+hipError_t launch_set_global(float* gscale, uint32_t value_bits, hipStream_t s);
+hipError_t launch_encode(int fmt, int kind, const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
+hipError_t launch_decode(int fmt, int kind, const DecArgs& a, bool add, bool scatter, bool vec, hipStream_t s);
+hipError_t launch_copy_rows(const CopyArgs& a, bool vec, hipStream_t s);
+hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
+hipError_t launch_validate_positions(const int32_t* pos, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,
+                                     hipStream_t s);
+
+}  // namespace kvq

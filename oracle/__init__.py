@@ -55,12 +55,14 @@ def _lib():
         i64 = ctypes.c_int64
         i32 = ctypes.c_int32
         ci = ctypes.c_int
-        lib.kvq_oracle_pack.argtypes = [p, i64, i64, i64, i64, i64, ci, ci, i32, p, p, p, p]
+        lib.kvq_oracle_pack.argtypes = [p, i64, i64, i64, i64, i64, ci, ci, i32, p, p, p, p, ctypes.c_float]
         lib.kvq_oracle_pack.restype = ci
         lib.kvq_oracle_unpack.argtypes = [ci, ci, i32, i64, i64, i64, p, p, p, p, p, i64, i64]
         lib.kvq_oracle_unpack.restype = ci
         lib.kvq_oracle_encode_residual.argtypes = [p, i64, i64, p, i64, i64, i64, i64, i64, p, i64, ci, ci, i32,
-                                                   p, p, p, p, p]
+                                                   p, p, p, p, p, ctypes.c_float]
+        lib.kvq_oracle_tensor_amax.argtypes = [p, i64, i64, p, i64, i64, i64, i64, i64, p, i64]
+        lib.kvq_oracle_tensor_amax.restype = ctypes.c_float
         lib.kvq_oracle_encode_residual.restype = ci
         lib.kvq_oracle_decode_residual.argtypes = [ci, ci, i32, i64, i64, i64, p, p, p, p, p, p, i64, i64, i64,
                                                    p, i64, i64]
@@ -134,14 +136,18 @@ def default_group(fmt: str) -> int:
     return 64 if fmt == "int4" else 16
 
 
-def pack(x: np.ndarray, kind: str, fmt: str = "int4", G: Optional[int] = None) -> Packed:
-    """pack_kv of a bf16 [T, H, D] view."""
+def pack(x: np.ndarray, kind: str, fmt: str = "int4", G: Optional[int] = None,
+         global_scale: Optional[float] = None) -> Packed:
+    """pack_kv of a bf16 [T, H, D] view. ``global_scale`` (NVFP4 only) encodes these rows with
+    the multiplier of a larger tensor they are a slice of; by default the rows are the whole
+    encoded tensor and the multiplier is computed from their own amax."""
     G = G or default_group(fmt)
     st, sh = _view_strides(x)
     T, H, D = x.shape
     out = _alloc(fmt, kind, G, T, H, D)
     rc = _lib().kvq_oracle_pack(_ptr(x), T, H, D, st, sh, KIND[kind], FORMAT[fmt], G, _ptr(out.codes),
-                                _ptr(out.meta0), _ptr(out.meta1), _ptr(out.global_scale))
+                                _ptr(out.meta0), _ptr(out.meta1), _ptr(out.global_scale),
+                                -1.0 if global_scale is None else float(global_scale))
     if rc:
         raise ValueError(f"oracle pack failed ({rc})")
     return out
@@ -160,8 +166,9 @@ def unpack(p: Packed, out: Optional[np.ndarray] = None) -> np.ndarray:
 
 
 def encode_residual(cur: np.ndarray, prev: np.ndarray, kind: str, fmt: str = "int4", G: Optional[int] = None,
-                    positions: Optional[np.ndarray] = None) -> Packed:
-    """encode_residual of cur against the reconstructed predecessor prev (both [T, H, D])."""
+                    positions: Optional[np.ndarray] = None, global_scale: Optional[float] = None) -> Packed:
+    """encode_residual of cur against the reconstructed predecessor prev (both [T, H, D]).
+    ``global_scale`` as in ``pack``."""
     G = G or default_group(fmt)
     cst, csh = _view_strides(cur)
     pst, psh = _view_strides(prev)
@@ -179,7 +186,8 @@ def encode_residual(cur: np.ndarray, prev: np.ndarray, kind: str, fmt: str = "in
         out.positions = np.zeros(M, np.int32)
     rc = _lib().kvq_oracle_encode_residual(_ptr(cur), cst, csh, _ptr(prev), pst, psh, T, H, D, _ptr(pos), M,
                                            KIND[kind], FORMAT[fmt], G, _ptr(out.codes), _ptr(out.meta0),
-                                           _ptr(out.meta1), _ptr(out.global_scale), _ptr(out.positions))
+                                           _ptr(out.meta1), _ptr(out.global_scale), _ptr(out.positions),
+                                           -1.0 if global_scale is None else float(global_scale))
     if rc:
         raise ValueError(f"oracle encode_residual failed ({rc})")
     return out
@@ -198,6 +206,16 @@ def decode_residual(r: Packed, prev: np.ndarray, out: Optional[np.ndarray] = Non
     if rc:
         raise ValueError(f"oracle decode_residual failed ({rc})")
     return out
+
+
+def tensor_amax(cur: np.ndarray, prev: Optional[np.ndarray] = None, positions: Optional[np.ndarray] = None) -> float:
+    """max |x| over the rows an encode of (cur[, prev][, positions]) sees."""
+    cst, csh = _view_strides(cur)
+    pst, psh = _view_strides(prev) if prev is not None else (0, 0)
+    T, H, D = cur.shape
+    pos = None if positions is None else np.ascontiguousarray(positions, dtype=np.int32)
+    M = 0 if pos is None else int(pos.shape[0])
+    return float(_lib().kvq_oracle_tensor_amax(_ptr(cur), cst, csh, _ptr(prev), pst, psh, T, H, D, _ptr(pos), M))
 
 
 def storage_bytes(fmt: str, kind: str, G: int, rows: int, H: int, D: int, sparse: bool = False) -> int:

@@ -436,15 +436,22 @@ static void nvfp4_group(void* vctx, int64_t gid, int64_t n, const int64_t* idx) 
     }
 }
 
-static int nvfp4_encode(const float* dense, int kind, int64_t rows, int64_t H, int64_t D, uint8_t* codes,
-                        uint8_t* sc8, float* gscale) {
-    /* tensor amax over every encoded element ([PR166] "Purpose": one scale per encoded tensor) */
+/* Tensor amax over every encoded element ([PR166] "Purpose": one scale per encoded tensor). */
+static float dense_amax(const float* dense, int64_t n) {
     float amax = 0.0f;
-    for (int64_t i = 0; i < rows * H * D; ++i) {
+    for (int64_t i = 0; i < n; ++i) {
         float a = fabsf(dense[i]);
         if (a > amax) amax = a;
     }
-    float g = kvq_oracle_nvfp4_global(amax);
+    return amax;
+}
+
+/* NVFP4 encode of dense rows. g_given < 0 means "the tensor's own multiplier" (the normal
+ * case); a non-negative g_given is the multiplier of a larger tensor these rows belong to,
+ * which lets a test check a slice of a tensor too large to encode here in full. */
+static int nvfp4_encode(const float* dense, int kind, int64_t rows, int64_t H, int64_t D, uint8_t* codes,
+                        uint8_t* sc8, float* gscale, float g_given) {
+    float g = (g_given >= 0.0f) ? g_given : kvq_oracle_nvfp4_global(dense_amax(dense, rows * H * D));
     uint8_t* c = (uint8_t*)calloc((size_t)(rows * H * D) + 1, 1);
     if (!c) return KVQO_NOMEM;
     nvfp4_ctx ctx = {dense, c, sc8, g};
@@ -476,9 +483,9 @@ static int check_common(int kind, int format, int32_t G, int64_t rows, int64_t H
 }
 
 static int encode_dense(const float* dense, int kind, int format, int32_t G, int64_t rows, int64_t H, int64_t D,
-                        uint8_t* codes, void* meta0, void* meta1, float* gscale) {
+                        uint8_t* codes, void* meta0, void* meta1, float* gscale, float g_given) {
     if (format == KVQO_INT4) return int4_encode(dense, kind, G, rows, H, D, codes, (uint16_t*)meta0, (uint16_t*)meta1);
-    return nvfp4_encode(dense, kind, rows, H, D, codes, (uint8_t*)meta0, gscale);
+    return nvfp4_encode(dense, kind, rows, H, D, codes, (uint8_t*)meta0, gscale, g_given);
 }
 
 /* pack_kv: encode the strided bf16 view x[T, H, D] (token stride st, head stride sh, channel
@@ -486,13 +493,13 @@ static int encode_dense(const float* dense, int kind, int format, int32_t G, int
  * Metadata: INT4 meta0 = f16 minimums, meta1 = f16 scales; NVFP4 meta0 = E4M3 block scales,
  * meta1 unused. Plane shapes: K [ceil(T/G), H, D], V [T, H, ceil(D/G)]. */
 int kvq_oracle_pack(const uint16_t* x, int64_t T, int64_t H, int64_t D, int64_t st, int64_t sh, int kind, int format,
-                    int32_t G, uint8_t* codes, void* meta0, void* meta1, float* gscale) {
+                    int32_t G, uint8_t* codes, void* meta0, void* meta1, float* gscale, float g_given) {
     int rc = check_common(kind, format, G, T, H, D);
     if (rc) return rc;
     float* dense = (float*)malloc(sizeof(float) * (size_t)(T * H * D) + 4);
     if (!dense) return KVQO_NOMEM;
     materialize(x, st, sh, NULL, 0, 0, NULL, T, H, D, dense);
-    rc = encode_dense(dense, kind, format, G, T, H, D, codes, meta0, meta1, gscale);
+    rc = encode_dense(dense, kind, format, G, T, H, D, codes, meta0, meta1, gscale, g_given);
     free(dense);
     return rc;
 }
@@ -529,7 +536,7 @@ int kvq_oracle_unpack(int kind, int format, int32_t G, int64_t rows, int64_t H, 
 int kvq_oracle_encode_residual(const uint16_t* cur, int64_t cst, int64_t csh, const uint16_t* prev, int64_t pst,
                                int64_t psh, int64_t T, int64_t H, int64_t D, const int32_t* positions, int64_t M,
                                int kind, int format, int32_t G, uint8_t* codes, void* meta0, void* meta1,
-                               float* gscale, int32_t* positions_out) {
+                               float* gscale, int32_t* positions_out, float g_given) {
     int64_t rows = positions ? M : T;
     int rc = check_common(kind, format, G, rows, H, D);
     if (rc) return rc;
@@ -540,7 +547,7 @@ int kvq_oracle_encode_residual(const uint16_t* cur, int64_t cst, int64_t csh, co
     float* dense = (float*)malloc(sizeof(float) * (size_t)(rows * H * D) + 4);
     if (!dense) return KVQO_NOMEM;
     materialize(cur, cst, csh, prev, pst, psh, positions, rows, H, D, dense);
-    rc = encode_dense(dense, kind, format, G, rows, H, D, codes, meta0, meta1, gscale);
+    rc = encode_dense(dense, kind, format, G, rows, H, D, codes, meta0, meta1, gscale, g_given);
     free(dense);
     if (positions && positions_out)
         for (int64_t i = 0; i < M; ++i) positions_out[i] = positions[i];
@@ -577,6 +584,27 @@ int kvq_oracle_decode_residual(int kind, int format, int32_t G, int64_t rows, in
             }
     }
     return KVQO_OK;
+}
+
+/* Tensor amax of the rows an encode would see (plain tensor, or the residual rows when prev is
+ * given, gathered by positions when given), as a float. */
+float kvq_oracle_tensor_amax(const uint16_t* cur, int64_t cst, int64_t csh, const uint16_t* prev, int64_t pst,
+                             int64_t psh, int64_t T, int64_t H, int64_t D, const int32_t* positions, int64_t M) {
+    int64_t rows = positions ? M : T;
+    float amax = 0.0f;
+    float* row = (float*)malloc(sizeof(float) * (size_t)(H * D) + 4);
+    for (int64_t i = 0; i < rows; ++i) {
+        const int32_t* p = positions ? positions + i : NULL;
+        if (p) {
+            materialize(cur, cst, csh, prev, pst, psh, p, 1, H, D, row);
+        } else {
+            materialize(cur + i * cst, cst, csh, prev ? prev + i * pst : NULL, pst, psh, NULL, 1, H, D, row);
+        }
+        float a = dense_amax(row, H * D);
+        if (a > amax) amax = a;
+    }
+    free(row);
+    return amax;
 }
 
 /* Element-wise helpers exposed for the pin tests (vectorized over n values). */

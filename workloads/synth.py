@@ -96,23 +96,49 @@ def c3_chain_inputs(seed: int = 0):
     return {"XK": XK, "XV": XV, "positions": positions}
 
 
+C4_CHUNK = 4096  # rows per independently seeded chunk of the bulk tensors
+
+
+def _chunked(seed_words, T: int, H: int, D: int, draw) -> np.ndarray:
+    """Rows in chunks of C4_CHUNK, chunk i drawn from its own generator
+    default_rng(SeedSequence(seed_words).spawn(n)[i]); the first k chunks are therefore the
+    same for any T >= k * C4_CHUNK. Chunks are drawn on a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = -(-T // C4_CHUNK)
+    seqs = np.random.SeedSequence(seed_words).spawn(max(n, 1))
+    out = np.empty((T, H, D), np.uint16)
+
+    def work(i):
+        r0 = i * C4_CHUNK
+        r1 = min(T, r0 + C4_CHUNK)
+        rng = np.random.default_rng(seqs[i])
+        out[r0:r1] = bf16_bits(draw(rng, (r1 - r0, H, D), r0, r1))
+
+    with ThreadPoolExecutor(max_workers=min(16, max(1, n))) as ex:
+        list(ex.map(work, range(n)))
+    return out
+
+
 def c4_tensors(seed: int = 0, T: int | None = None):
-    """Heavy-tailed bulk K and V (Student-t, nu = 3). T may be lowered for a bounded sample;
-    the sample is then the leading rows of a smaller draw, not of the full tensors."""
+    """Heavy-tailed bulk K and V (Student-t, nu = 3). A smaller T gives the leading rows of the
+    full tensors (chunked seeding)."""
     c = CONFIGS["c4"]
-    T = T or c["T"]
-    rng = np.random.default_rng(seed)
-    shape = (T, c["H"], c["D"])
-    K = bf16_bits(rng.standard_t(3, shape))
-    V = bf16_bits(rng.standard_t(3, shape))
+    T = c["T"] if T is None else T
+    t3 = lambda rng, shape, r0, r1: rng.standard_t(3, shape)  # noqa: E731
+    K = _chunked([seed, 0], T, c["H"], c["D"], t3)
+    V = _chunked([seed, 1], T, c["H"], c["D"], t3)
     return {"K": K, "V": V}
 
 
-def c4_residual_target(X0: np.ndarray, seed: int = 1) -> np.ndarray:
-    """Next-loop state X1 = bf16(X0 + 0.1 N(0,1)), drawn with its own seed."""
-    rng = np.random.default_rng(seed)
-    z = rng.standard_normal(X0.shape)
-    return bf16_bits(bf16_to_f32(X0).astype(np.float64) + 0.1 * z)
+def c4_residual_target(X0: np.ndarray, seed: int = 1, stream: int = 0) -> np.ndarray:
+    """Next-loop state X1 = bf16(X0 + 0.1 N(0,1)), with its own chunked seed."""
+    T, H, D = X0.shape
+
+    def draw(rng, shape, r0, r1):
+        return bf16_to_f32(X0[r0:r1]).astype(np.float64) + 0.1 * rng.standard_normal(shape)
+
+    return _chunked([seed, 2 + stream], T, H, D, draw)
 
 
 def _block_factors(rng: np.random.Generator, n_blocks_shape) -> np.ndarray:
