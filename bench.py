@@ -38,7 +38,7 @@ OPS = ("pack", "unpack", "encode_residual", "decode_residual")
 
 def algo_bytes(op: str, fmt: str, n: int) -> float:
     """Bytes the method must move for one op on n elements (see module docstring)."""
-    meta = 0.0625 if fmt == "int4" else 0.0625  # 4 B per 64 (int4) = 1 B per 16 (nvfp4) = 1/16 B/elem
+    meta = 0.0625  # 4 B per 64 values (INT4 G64) = 1 B per 16 values (NVFP4 G16)
     code = 0.5
     extra = 4 if fmt == "nvfp4" else 0
     if op == "pack":
@@ -126,64 +126,68 @@ def main() -> int:
             )
     stream = torch.cuda.current_stream(dev)
 
-    def step(events=None):
-        k = 0
-        for fmt, G in FORMS:
-            for kind in KINDS:
-                b = bufs[(fmt, kind)]
-                x0, x1 = X[kind]
-                if events is not None:
-                    events[k].record(stream)
-                kvq.pack(x0, kind, fmt, G, out=b["p"])
-                if events is not None:
-                    events[k + 1].record(stream)
-                kvq.unpack(b["p"], out=b["R0"])
-                if events is not None:
-                    events[k + 2].record(stream)
-                kvq.encode_residual(x1, b["R0"], kind, fmt, G, out=b["r"])
-                if events is not None:
-                    events[k + 3].record(stream)
-                kvq.decode_residual(b["r"], b["R0"], out=b["R1"])
-                if events is not None:
-                    events[k + 4].record(stream)
-                k += 5
+    calls = []  # (name, fmt, op, fn) in step order
+    for fmt, G in FORMS:
+        for kind in KINDS:
+            b = bufs[(fmt, kind)]
+            x0, x1 = X[kind]
+            calls.append((f"{fmt}-{kind}-pack", fmt, "pack",
+                          lambda x0=x0, kind=kind, fmt=fmt, G=G, b=b: kvq.pack(x0, kind, fmt, G, out=b["p"])))
+            calls.append((f"{fmt}-{kind}-unpack", fmt, "unpack",
+                          lambda b=b: kvq.unpack(b["p"], out=b["R0"])))
+            calls.append((f"{fmt}-{kind}-encode_residual", fmt, "encode_residual",
+                          lambda x1=x1, kind=kind, fmt=fmt, G=G, b=b: kvq.encode_residual(x1, b["R0"], kind, fmt, G,
+                                                                                         out=b["r"])))
+            calls.append((f"{fmt}-{kind}-decode_residual", fmt, "decode_residual",
+                          lambda b=b: kvq.decode_residual(b["r"], b["R0"], out=b["R1"])))
+    # kernel launches per op: NVFP4 encodes run amax, finalize and the encode kernel
+    launches = {name: (3 if (fmt == "nvfp4" and op in ("pack", "encode_residual")) else 1)
+                for name, fmt, op, _ in calls}
+
+    def step(timed=None, events=None):
+        for name, _fmt, _op, fn in calls:
+            if events is not None and (timed is None or name == timed):
+                events.append((name, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                events[-1][1].record(stream)
+                fn()
+                events[-1][2].record(stream)
+            else:
+                fn()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    n_ev = 5 * len(FORMS) * len(KINDS)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    # per-op table from an instrumented pass (events around every op; not the timed region)
+    prof = []
+    for _ in range(min(10, max(1, args.steps))):
+        step(events=prof)
+    torch.cuda.synchronize()
+    per_op = {}
+    for name, fmt, op, _ in calls:
+        ms = np.array([e0.elapsed_time(e1) for nm, e0, e1 in prof if nm == name])
+        nbytes = algo_bytes(op, fmt, n)
+        per_op[name] = dict(mean_us=float(ms.mean() * 1e3), p50_us=float(np.percentile(ms, 50) * 1e3),
+                            p90_us=float(np.percentile(ms, 90) * 1e3), bytes=nbytes,
+                            gbs=float(nbytes / (np.percentile(ms, 50) * 1e-3) / 1e9), launches=launches[name])
+    # the dominant single-kernel op: the one-launch op with the largest share of the step
+    dom_name = max((k for k in per_op if per_op[k]["launches"] == 1), key=lambda k: per_op[k]["mean_us"])
+
+    # timed region: K steps; events only around the dominant op (for the roofline figure)
+    dom_events = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
+    for _ in range(args.steps):
+        step(timed=dom_name, events=dom_events)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    dom_us = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in dom_events]) * 1e3)
 
-    # per-op durations from the events (same stream as the kernels)
-    per_op = {}
-    k = 0
-    for fmt, G in FORMS:
-        for kind in KINDS:
-            for j, op in enumerate(OPS):
-                ms = [events[s][k + j].elapsed_time(events[s][k + j + 1]) for s in range(args.steps)]
-                ms = np.array(ms)
-                nbytes = algo_bytes(op, fmt, n)
-                per_op[f"{fmt}-{kind}-{op}"] = dict(
-                    mean_us=float(ms.mean() * 1e3), p50_us=float(np.percentile(ms, 50) * 1e3),
-                    p90_us=float(np.percentile(ms, 90) * 1e3), bytes=nbytes,
-                    gbs=float(nbytes / (np.percentile(ms, 50) * 1e-3) / 1e9),
-                    launches=2 if (fmt == "nvfp4" and op in ("pack", "encode_residual")) else 1)
-            k += 5
     step_bytes = sum(v["bytes"] for v in per_op.values())
     ms_per_step = elapsed / args.steps * 1e3
     value = step_bytes / (elapsed / args.steps) / 1e9
-
-    # dominant single-kernel op: the one-launch op with the largest share of the step
-    single = {k: v for k, v in per_op.items() if v["launches"] == 1}
-    dom_name, dom = max(single.items(), key=lambda kv: kv[1]["mean_us"])
-    achieved = dom["bytes"] / (dom["mean_us"] * 1e-6) / 1e9
+    dom = per_op[dom_name]
+    achieved = dom["bytes"] / (dom_us * 1e-6) / 1e9
 
     for name, v in per_op.items():
         print(f"{name:34s} mean {v['mean_us']:8.1f} us  p50 {v['p50_us']:8.1f}  p90 {v['p90_us']:8.1f}  "
@@ -215,6 +219,8 @@ def main() -> int:
         "roofline": {
             "bound": "hbm",
             "kernel": dom_name,
+            "kernel_avg_us": round(dom_us, 2),
+            "bytes_per_launch": dom["bytes"],
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -124,15 +124,15 @@ kvq_status kvq_storage_bytes(kvq_format format, kvq_kind kind, int32_t group_siz
 kvq_status kvq_plane_bytes(kvq_format format, kvq_kind kind, int32_t group_size, int64_t rows, int64_t H,
                            int64_t D, int32_t sparse, uint64_t sizes[KVQ_NUM_PLANES]);
 
-/* Bytes of device workspace an NVFP4 encode needs (a tensor-wide max accumulator and a block
- * counter). The caller zero-fills it once before first use; every completed call leaves it
- * zeroed again. Calls that may run concurrently need distinct workspaces. */
+/* Bytes of device workspace an NVFP4 encode needs (per-block partial maxima of the tensor-amax
+ * pass). No initialization is needed; every call overwrites what it reads. Calls that may run
+ * concurrently need distinct workspaces. */
 size_t kvq_workspace_bytes(void);
 
 /* pack_kv ([PR166] "Purpose" usage example, first line): encode x into *out.
  * The caller sets out->codes, out->meta0, out->meta1 (INT4), out->global_scale (NVFP4); the
  * library sets the scalar fields and out->positions = NULL. group_size 0 = format default
- * (INT4 64, NVFP4 16). NVFP4 needs `workspace` (kvq_workspace_bytes, zeroed); INT4 ignores it.
+ * (INT4 64, NVFP4 16). NVFP4 needs `workspace` (kvq_workspace_bytes); INT4 ignores it.
  * The NVFP4 global multiplier is recomputed on every call ([PR166] "Purpose", paragraph after
  * the example). Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, DTYPE, WORKSPACE, HIP. */
 kvq_status kvq_pack(const kvq_tensor* x, kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out,

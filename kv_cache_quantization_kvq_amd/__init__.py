@@ -195,8 +195,8 @@ def _empty_map(dev: torch.device) -> torch.Tensor:
 
 
 def workspace(dev: torch.device) -> torch.Tensor:
-    """Zero-initialized workspace for NVFP4 encodes, one per (device, current stream). The
-    library leaves it zeroed after every call, so it is allocated once."""
+    """Workspace for NVFP4 encodes (per-block partial maxima), one per (device, current stream),
+    allocated once."""
     key = (dev.index if dev.index is not None else torch.cuda.current_device(), torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None:

@@ -11,7 +11,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxElems = (int64_t)1 << 36;
-constexpr size_t kWorkspaceBytes = 256;
+constexpr size_t kWorkspaceBytes = KVQ_AMAX_MAX_BLOCKS * sizeof(uint32_t);
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -192,7 +192,7 @@ kvq_status encode_common(const kvq_tensor* cur, const kvq_tensor* prev, const in
     }
     if (vec) {
         if (kind == KVQ_VALUE) {
-            fill_vec_geometry(a, rows, H, D, G, 4);
+            fill_vec_geometry(a, rows, H, D, G, 8);  // rows per VALUE-encode wave task
         } else {
             fill_vec_geometry(a, rows, H, D, G, G);
         }

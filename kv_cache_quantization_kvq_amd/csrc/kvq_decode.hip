@@ -20,12 +20,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint32_t finish_pair(float y0, float y1, uint32_t prev_word, bool add) {
-    if (!add) return pack_bf16x2(y0, y1);
-    // residual decode: round the decoded delta to bf16 first, then add in binary32, round again
-    const float d0 = bf16_to_f32(f32_to_bf16(y0));
-    const float d1 = bf16_to_f32(f32_to_bf16(y1));
-    return pack_bf16x2(__fadd_rn(bf16lo(prev_word), d0), __fadd_rn(bf16hi(prev_word), d1));
+// Output word of two decoded values: bf16 of each, or for a residual the bf16 of prev plus the
+// bf16-rounded decoded value (both steps in the input dtype).
+template <bool ADD>
+__device__ __forceinline__ uint32_t finish_pair(float y0, float y1, uint32_t prev_word) {
+    const uint32_t yb = pack_bf16x2(y0, y1);
+    if constexpr (!ADD) return yb;
+    return pack_bf16x2(__fadd_rn(bf16lo(prev_word), bf16lo(yb)), __fadd_rn(bf16hi(prev_word), bf16hi(yb)));
 }
 
 template <int FMT, int KIND, bool ADD, bool SCATTER>
@@ -36,101 +37,107 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     if (task >= a.n_tasks) return;
     const uint32_t rtile = fdiv(task, a.div_slabs);
     const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
-    const uint32_t c8 = slab * 64u + lane;
-    const bool valid = c8 < (uint32_t)a.C8;
+    const uint32_t c8raw = slab * 64u + lane;
+    const bool valid = c8raw < (uint32_t)a.C8;
+    const uint32_t c8 = valid ? c8raw : (uint32_t)a.C8 - 1u;  // idle lanes read a valid chunk
     const uint32_t h = fdiv(c8, a.div_D8);
     const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
     const int64_t r0 = (int64_t)rtile * RW;
     const int nr = (int)min<int64_t>(RW, a.rows - r0);
-    if (!valid) return;  // no cross-lane work in this kernel
 
-    uint32_t cw[RW];
-    int64_t tt[RW];
-    uint4 pv[RW];
+    // all loads first (tail rows re-read the last row; only stores are masked)
+    int64_t rr[RW], tt[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-        cw[i] = 0;
-        tt[i] = r0 + i;
-        pv[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (i < nr) {
-            cw[i] = reinterpret_cast<const uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8];
-            if constexpr (SCATTER) tt[i] = a.pos[r0 + i];
-            if constexpr (ADD) pv[i] = *reinterpret_cast<const uint4*>(a.prev + tt[i] * a.pst + (int64_t)h * a.psh + d);
+        rr[i] = min<int64_t>(r0 + i, a.rows - 1);
+        tt[i] = SCATTER ? (int64_t)a.pos[rr[i]] : rr[i];
+    }
+    uint32_t cw[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.codes) + (size_t)rr[i] * (uint32_t)a.C8 + c8);
+    u32x4 pv[RW];
+    if constexpr (ADD) {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) pv[i] = ld_stream(a.prev + tt[i] * a.pst + (int64_t)h * a.psh + d);
+    }
+    // per-row metadata (VALUE): one group per lane and row
+    float vs[RW], vm[RW];
+    if constexpr (KIND == KIND_VALUE) {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            const size_t midx = (size_t)rr[i] * (uint32_t)a.ngr + (c8 >> a.lpg_shift);
+            if constexpr (FMT == FMT_INT4) {
+                vs[i] = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta1)[midx]);
+                vm[i] = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta0)[midx]);
+            } else {
+                vs[i] = (float)reinterpret_cast<const uint8_t*>(a.meta0)[midx];  // code, scaled below
+                vm[i] = 0.0f;
+            }
         }
     }
 
     float g = 0.0f;
     if constexpr (FMT == FMT_NVFP4) g = *a.gscale;
 
-    // KEY: per-channel metadata of this task's token group, loaded once
+    // KEY: per-channel metadata of this task's token group (G % RW == 0), loaded once
     float ks[8], km[8];
     if constexpr (KIND == KIND_KEY) {
         const size_t mbase = ((size_t)(r0 / a.G) * (uint32_t)a.C8 + c8) * 8u;
         if constexpr (FMT == FMT_INT4) {
-            const uint4 mins = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.meta0) + mbase);
-            const uint4 scs = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.meta1) + mbase);
-            const uint32_t mw[4] = {mins.x, mins.y, mins.z, mins.w};
-            const uint32_t sw[4] = {scs.x, scs.y, scs.z, scs.w};
+            const u32x4 mins = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.meta0) + mbase);
+            const u32x4 scs = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.meta1) + mbase);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                km[2 * j] = f16_to_f32(mw[j] & 0xFFFFu);
-                km[2 * j + 1] = f16_to_f32(mw[j] >> 16);
-                ks[2 * j] = f16_to_f32(sw[j] & 0xFFFFu);
-                ks[2 * j + 1] = f16_to_f32(sw[j] >> 16);
+                km[2 * j] = f16_to_f32(mins[j] & 0xFFFFu);
+                km[2 * j + 1] = f16_to_f32(mins[j] >> 16);
+                ks[2 * j] = f16_to_f32(scs[j] & 0xFFFFu);
+                ks[2 * j + 1] = f16_to_f32(scs[j] >> 16);
             }
         } else {
             const uint2 sc = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.meta0) + mbase);
             const uint32_t sw[2] = {sc.x, sc.y};
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const uint32_t code = (sw[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                ks[k] = e4m3_decode(code) / g;
+                ks[k] = e4m3_decode((sw[k >> 2] >> (8 * (k & 3))) & 0xFFu) / g;
                 km[k] = 0.0f;
             }
         }
+    } else if constexpr (FMT == FMT_NVFP4) {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) vs[i] = e4m3_decode((uint32_t)vs[i]) / g;
     }
 
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-        if (i >= nr) break;
-        const int64_t r = r0 + i;
-        float vs[8], vm[8];
-        if constexpr (KIND == KIND_VALUE) {
-            const size_t midx = (size_t)r * (uint32_t)a.ngr + (c8 >> a.lpg_shift);
-            float s, m = 0.0f;
-            if constexpr (FMT == FMT_INT4) {
-                s = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta1)[midx]);
-                m = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta0)[midx]);
-            } else {
-                s = e4m3_decode(reinterpret_cast<const uint8_t*>(a.meta0)[midx]) / g;
-            }
+        float y[8];
+        if constexpr (FMT == FMT_INT4) {
+            // nibbles 2j / 2j+1 sit in the low / high half of byte j
+            const uint32_t lo = cw[i] & 0x0F0F0F0Fu, hi = (cw[i] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                vs[k] = s;
-                vm[k] = m;
+            for (int j = 0; j < 4; ++j) {
+                const float c0 = (float)((lo >> (8 * j)) & 0xFFu), c1 = (float)((hi >> (8 * j)) & 0xFFu);
+                if constexpr (KIND == KIND_KEY) {
+                    y[2 * j] = int4_value_f(c0, ks[2 * j], km[2 * j]);
+                    y[2 * j + 1] = int4_value_f(c1, ks[2 * j + 1], km[2 * j + 1]);
+                } else {
+                    y[2 * j] = int4_value_f(c0, vs[i], vm[i]);
+                    y[2 * j + 1] = int4_value_f(c1, vs[i], vm[i]);
+                }
             }
         } else {
+            const f32x2 e0 = e2m1_values<0>(cw[i]), e1 = e2m1_values<1>(cw[i]);
+            const f32x2 e2 = e2m1_values<2>(cw[i]), e3 = e2m1_values<3>(cw[i]);
+            const float e[8] = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                vs[k] = ks[k];
-                vm[k] = km[k];
-            }
+            for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(e[k], (KIND == KIND_KEY) ? ks[k] : vs[i]);
         }
-        float y[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t c = (cw[i] >> (4 * k)) & 0xFu;
-            if constexpr (FMT == FMT_INT4)
-                y[k] = int4_value(c, vs[k], vm[k]);
-            else
-                y[k] = __fmul_rn(e2m1_value(c), vs[k]);
-        }
-        uint4 o;
-        o.x = finish_pair(y[0], y[1], pv[i].x, ADD);
-        o.y = finish_pair(y[2], y[3], pv[i].y, ADD);
-        o.z = finish_pair(y[4], y[5], pv[i].z, ADD);
-        o.w = finish_pair(y[6], y[7], pv[i].w, ADD);
-        *reinterpret_cast<uint4*>(a.out + tt[i] * a.ost + (int64_t)h * a.osh + d) = o;
+        u32x4 o;
+        o.x = finish_pair<ADD>(y[0], y[1], ADD ? pv[i].x : 0u);
+        o.y = finish_pair<ADD>(y[2], y[3], ADD ? pv[i].y : 0u);
+        o.z = finish_pair<ADD>(y[4], y[5], ADD ? pv[i].z : 0u);
+        o.w = finish_pair<ADD>(y[6], y[7], ADD ? pv[i].w : 0u);
+        if (i < nr && valid) *reinterpret_cast<u32x4*>(a.out + tt[i] * a.ost + (int64_t)h * a.osh + d) = o;
     }
 }
 
@@ -160,12 +167,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
             y = int4_value(c, f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta1)[midx]),
                            f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta0)[midx]));
         } else {
-            y = __fmul_rn(e2m1_value(c), e4m3_decode(reinterpret_cast<const uint8_t*>(a.meta0)[midx]) / g);
+            y = __fmul_rn(e2m1_values<0>(c)[0], e4m3_decode(reinterpret_cast<const uint8_t*>(a.meta0)[midx]) / g);
         }
-        uint32_t outb = f32_to_bf16(y);
+        uint32_t outb = bf16_bits(y);
         if constexpr (ADD) {
             const float p = bf16_to_f32(a.prev[t * a.pst + h * a.psh + dd]);
-            outb = f32_to_bf16(__fadd_rn(p, bf16_to_f32(outb)));
+            outb = bf16_bits(__fadd_rn(p, bf16_to_f32(outb)));
         }
         a.out[t * a.ost + h * a.osh + dd] = (uint16_t)outb;
     }

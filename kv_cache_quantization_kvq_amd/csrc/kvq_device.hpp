@@ -1,11 +1,13 @@
 // kvq_device.hpp -- device-side numerics of the KV codec (gfx950).
 //
-// Every conversion here is integer arithmetic on bit patterns or exact float scaling, so the
-// results do not depend on the hardware conversion instructions' rounding or denormal modes.
-// Floating-point steps that the format defines as single binary32 operations are written as
-// separate __fadd_rn/__fmul_rn/__fsub_rn calls (the library is also built with
-// -ffp-contract=off), and divisions use the IEEE-correct '/' (the library is built with
-// correctly rounded fp32 division).
+// Roundings come in two forms. The integer formulations (namespace kvq::ref) are written from
+// the format definitions; the gfx950 conversion instructions used on the hot path
+// (v_cvt_pk_bf16_f32, v_cvt_f16_f32, v_cvt_scalef32_pk_fp4_f32 and v_cvt_scalef32_pk_f32_fp4)
+// were checked against them for every binary32 input (tests/probes/cvt_probe.hip) and are only
+// used where that check holds. Floating-point steps that the format defines as single binary32
+// operations are written as separate __fadd_rn/__fmul_rn/__fsub_rn calls (the library is also
+// built with -ffp-contract=off), and divisions use the IEEE-correct '/' (the library is built
+// with correctly rounded fp32 division and keeps denormals).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,18 +21,29 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// binary32 -> bf16, round to nearest even. Valid for every non-NaN input; values past the
-// largest finite bf16 (by at least half an ulp) carry into the exponent and give +-inf.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+namespace ref {
+// binary32 -> bf16, round to nearest even (integer formulation). Valid for every non-NaN
+// input; values past the largest finite bf16 (by at least half an ulp) give +-inf.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
 }
+}  // namespace ref
 
-// Two bf16 results packed into one word (low element first).
+// Two binary32 values -> two bf16 (low element first), round to nearest even, one
+// v_cvt_pk_bf16_f32 (identical to ref::f32_to_bf16 on every non-NaN input).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+// bf16 bits of x (round to nearest even)
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, x) & 0xFFFFu; }
 
 // bf16(fl(a - b)) for the two halves of packed words: the residual subtraction in the input
 // dtype ([PR166] "Purpose", fourth bullet).
@@ -38,9 +51,16 @@ __device__ __forceinline__ uint32_t sub_bf16x2(uint32_t a, uint32_t b) {
     return pack_bf16x2(__fsub_rn(bf16lo(a), bf16lo(b)), __fsub_rn(bf16hi(a), bf16hi(b)));
 }
 
+// Streaming 16-byte load of data read once (non-temporal hint).
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // ---- f16 (INT4 metadata) --------------------------------------------------------------------
 
-// binary32 -> binary16 bits, round to nearest even, gradual underflow, overflow to inf.
+namespace ref {
+// binary32 -> binary16 bits, round to nearest even, gradual underflow, overflow to inf
+// (integer formulation).
 __device__ __forceinline__ uint32_t f32_to_f16(float f) {
     uint32_t x = __float_as_uint(f);
     uint32_t sign = (x >> 16) & 0x8000u;
@@ -54,15 +74,14 @@ __device__ __forceinline__ uint32_t f32_to_f16(float f) {
     float a = __uint_as_float(ax) * 16777216.0f;
     return sign | (uint32_t)__builtin_rintf(a);
 }
+}  // namespace ref
 
-__device__ __forceinline__ float f16_to_f32(uint32_t h) {
-    uint32_t sign = (h & 0x8000u) << 16;
-    uint32_t e = (h >> 10) & 0x1Fu;
-    uint32_t m = h & 0x3FFu;
-    if (e == 0) return __uint_as_float(sign | __float_as_uint((float)m * 5.9604644775390625e-8f));
-    if (e == 31) return __uint_as_float(sign | 0x7F800000u | (m << 13));
-    return __uint_as_float(sign | ((e + 112u) << 23) | (m << 13));
-}
+// binary32 -> binary16 bits with v_cvt_f16_f32 (identical to ref::f32_to_f16 on every non-NaN
+// input, subnormals and overflow included).
+__device__ __forceinline__ uint32_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// binary16 bits -> binary32 (exact; f16 subnormals are kept by the denormal mode).
+__device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
 // ---- E4M3 (NVFP4 block scales) --------------------------------------------------------------
 
@@ -85,6 +104,7 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
 
 // ---- E2M1 (NVFP4 codes) ---------------------------------------------------------------------
 
+namespace ref {
 // Magnitude code of |q| on {0, .5, 1, 1.5, 2, 3, 4, 6}, nearest with ties to the even code:
 // the half-way points 0.25, 1.25, 2.5, 5 go down, 0.75, 1.75, 3.5 go up; anything above 5
 // saturates to 6 (code 7). Written as threshold counts.
@@ -100,6 +120,22 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
     uint32_t e = (c >> 1) & 3u, m = c & 1u;
     uint32_t mag = (e == 0) ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
     return __uint_as_float(mag | ((c & 8u) << 28));
+}
+}  // namespace ref
+
+// Two scaled values -> one byte of two E2M1 codes (first value in the low nibble), written into
+// byte SEL of `word`: v_cvt_scalef32_pk_fp4_f32 with scale 1, which equals ref::e2m1_mag with
+// the sign bit of the value for every finite input (saturating above 5, signed zeros kept).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t word, float q0, float q1) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q0, q1, 1.0f, SEL);
+}
+
+// The two E2M1 values of byte SEL of `word` (low nibble first): v_cvt_scalef32_pk_f32_fp4 with
+// scale 1, equal to ref::e2m1_value for all 16 codes.
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1_values(uint32_t word) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
 }
 
 // ---- sortable keys --------------------------------------------------------------------------
@@ -192,8 +228,11 @@ __device__ __forceinline__ Int4Group int4_group(float mn, float mx) {
 
 // code = clamp(rne(fl(fl(x - mn) / scale)), 0, 15), bit-exact with the IEEE division.
 // Fast path: q' = fl(d * fl(1/scale)) differs from fl(d/scale) by at most 3*2^-24*q + tiny
-// (q <= 15 + 2^-19), i.e. below 2^-19; whenever q' is farther than 2^-17 from a half-integer,
+// (q <= 15 + 2^-12), i.e. below 2^-18; whenever q' is farther than 2^-17 from a half-integer,
 // both round to the same integer. Otherwise (or when 1/scale overflowed) divide.
+// The clamp never binds for bf16 members: x >= mn gives d >= +0, and d <= fl(mx - mn) with
+// scale >= (mx - mn)/15 * (1 - 2^-13) (the worst case is a subnormal scale over the smallest
+// nonzero bf16 range 2^-133) keeps q below 15.01, so rne(q) is already in [0, 15].
 __device__ __forceinline__ uint32_t int4_code(float x, const Int4Group& g) {
     float d = __fsub_rn(x, g.mn);
     float q = __fmul_rn(d, g.rcp);
@@ -201,14 +240,14 @@ __device__ __forceinline__ uint32_t int4_code(float x, const Int4Group& g) {
     if (__builtin_expect(g.exact || __builtin_fabsf(__fsub_rn(q, c)) > 0.4999923706054688f, 0)) {
         c = __builtin_rintf(d / g.scale);
     }
-    c = __builtin_fminf(c, 15.0f);
     return (uint32_t)c;
 }
 
-// INT4 decode: bf16(fl(fl(c * scale16) + min16)).
-__device__ __forceinline__ float int4_value(uint32_t c, float s16, float m16) {
-    return __fadd_rn(__fmul_rn((float)c, s16), m16);
+// INT4 decode before the final rounding to bf16: fl(fl(c * scale16) + min16).
+__device__ __forceinline__ float int4_value_f(float c, float s16, float m16) {
+    return __fadd_rn(__fmul_rn(c, s16), m16);
 }
+__device__ __forceinline__ float int4_value(uint32_t c, float s16, float m16) { return int4_value_f((float)c, s16, m16); }
 
 // ---- NVFP4 block constants ------------------------------------------------------------------
 
@@ -237,9 +276,15 @@ __device__ __forceinline__ Fp4Block fp4_block(uint32_t bamax_bits, float g) {
     return b;
 }
 
+// Scaled element q = fl(x * r), or fl(x / s_dec) when 1/s_dec overflowed; the E2M1 code of q
+// carries the sign of x (q has it too: r and s_dec are positive or r is zero).
+__device__ __forceinline__ float fp4_scaled(float x, const Fp4Block& b) {
+    return b.div ? (x / b.s_dec) : __fmul_rn(x, b.rcp);
+}
+
+// Reference single-element code (generic paths).
 __device__ __forceinline__ uint32_t fp4_code(float x, const Fp4Block& b) {
-    float q = b.div ? (x / b.s_dec) : __fmul_rn(x, b.rcp);
-    return e2m1_mag(q) | ((__float_as_uint(x) >> 28) & 8u);
+    return e2m1_pair<0>(0u, fp4_scaled(x, b), 0.0f) & 0xFu;
 }
 
 // NVFP4 global multiplier from the tensor amax (bf16 magnitude bits): fl(2688 / amax);

@@ -6,12 +6,15 @@
 // group along the axis may be partial.
 //
 // Vector path (D % 8 == 0, 16-byte aligned rows): one lane owns 8 consecutive channels of a
-// row and moves them with one 16-byte load; codes leave as one 32-bit word per lane.
+// row and moves them with one 16-byte streaming load; codes leave as one 32-bit word per lane.
 //   VALUE: a group is G/8 adjacent lanes; its min/max (or abs-max) is an all-reduce over those
 //          lanes with DPP row moves.
 //   KEY:   a group is a column of G rows; each lane keeps its rows in registers and reduces over
 //          them itself (no transpose); when a group is split over several waves the partial
 //          results meet in LDS once.
+// All loads of a wave task are issued before any arithmetic and without branches: a tail row
+// or an idle lane reads an in-bounds duplicate (the last row of the same group, or a valid
+// chunk) whose value cannot change a min, max or abs-max, and only the stores are masked.
 // Generic path: any D, G, stride or alignment; one thread per (row, head) for VALUE and per
 // (token group, head, channel pair) for KEY, two passes over the members.
 #include "kvq_launch.hpp"
@@ -21,21 +24,10 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kEncodeRowsV = 8;                           // rows per VALUE-encode wave task
+constexpr uint32_t kAmaxMaxBlocks = KVQ_AMAX_MAX_BLOCKS;  // partial maxima held in the workspace
 
 // ---- element access ----------------------------------------------------------------------------
-
-template <bool DIFF>
-__device__ __forceinline__ uint4 load_row8(const EncArgs& a, int64_t t, uint32_t h, uint32_t d) {
-    uint4 v = *reinterpret_cast<const uint4*>(a.cur + t * a.cst + (int64_t)h * a.csh + d);
-    if constexpr (DIFF) {
-        uint4 p = *reinterpret_cast<const uint4*>(a.prev + t * a.pst + (int64_t)h * a.psh + d);
-        v.x = sub_bf16x2(v.x, p.x);
-        v.y = sub_bf16x2(v.y, p.y);
-        v.z = sub_bf16x2(v.z, p.z);
-        v.w = sub_bf16x2(v.w, p.w);
-    }
-    return v;
-}
 
 // bf16 bits of the encoded value of element (t, h, d) (generic path)
 template <bool DIFF>
@@ -43,29 +35,73 @@ __device__ __forceinline__ uint32_t load_one(const EncArgs& a, int64_t t, int64_
     uint32_t c = a.cur[t * a.cst + h * a.csh + d];
     if constexpr (DIFF) {
         uint32_t p = a.prev[t * a.pst + h * a.psh + d];
-        return f32_to_bf16(__fsub_rn(bf16_to_f32(c), bf16_to_f32(p)));
+        return bf16_bits(__fsub_rn(bf16_to_f32(c), bf16_to_f32(p)));
     }
     return c;
+}
+
+// Loads the RW rows' 8-channel chunks of one lane (all issued before use), residual applied.
+template <int RW, bool DIFF, bool GATHER>
+__device__ __forceinline__ void load_rows8(const EncArgs& a, int64_t r0, uint32_t h, uint32_t d, u32x4 (&v)[RW]) {
+    int64_t t[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        const int64_t r = min<int64_t>(r0 + i, a.rows - 1);  // tail rows duplicate the last row
+        t[i] = GATHER ? (int64_t)a.pos[r] : r;
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i) v[i] = ld_stream(a.cur + t[i] * a.cst + (int64_t)h * a.csh + d);
+    if constexpr (DIFF) {
+        u32x4 p[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) p[i] = ld_stream(a.prev + t[i] * a.pst + (int64_t)h * a.psh + d);
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            v[i].x = sub_bf16x2(v[i].x, p[i].x);
+            v[i].y = sub_bf16x2(v[i].y, p[i].y);
+            v[i].z = sub_bf16x2(v[i].z, p[i].z);
+            v[i].w = sub_bf16x2(v[i].w, p[i].w);
+        }
+    }
 }
 
 __device__ __forceinline__ uint32_t imin_op(uint32_t x, uint32_t y) { return (uint32_t)min((int)x, (int)y); }
 __device__ __forceinline__ uint32_t imax_op(uint32_t x, uint32_t y) { return (uint32_t)max((int)x, (int)y); }
 __device__ __forceinline__ uint32_t umax_op(uint32_t x, uint32_t y) { return max(x, y); }
 
-template <int FMT, typename GC>
-__device__ __forceinline__ uint32_t code_of(float x, const GC& g) {
-    if constexpr (FMT == FMT_INT4)
-        return int4_code(x, g);
-    else
-        return fp4_code(x, g);
+// 8 INT4 codes of one chunk (channel 2j in nibble 2j); group constants gp[k * stride]
+__device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* gp, int stride) {
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        word |= int4_code(bf16lo(w4[j]), gp[(2 * j) * stride]) << (8 * j);
+        word |= int4_code(bf16hi(w4[j]), gp[(2 * j + 1) * stride]) << (8 * j + 4);
+    }
+    return word;
 }
 
-template <int FMT, typename GC>
-__device__ __forceinline__ uint32_t codes8(const uint4& v, const GC& g) {
-    return code_of<FMT>(bf16lo(v.x), g) | (code_of<FMT>(bf16hi(v.x), g) << 4) | (code_of<FMT>(bf16lo(v.y), g) << 8) |
-           (code_of<FMT>(bf16hi(v.y), g) << 12) | (code_of<FMT>(bf16lo(v.z), g) << 16) |
-           (code_of<FMT>(bf16hi(v.z), g) << 20) | (code_of<FMT>(bf16lo(v.w), g) << 24) |
-           (code_of<FMT>(bf16hi(v.w), g) << 28);
+// 8 NVFP4 codes of one chunk: scaled values, then 4 packed E2M1 conversions
+__device__ __forceinline__ uint32_t fp4_word(const u32x4& v, const Fp4Block* fb, int stride) {
+    float q[8];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        q[2 * j] = __fmul_rn(bf16lo(w4[j]), fb[(2 * j) * stride].rcp);
+        q[2 * j + 1] = __fmul_rn(bf16hi(w4[j]), fb[(2 * j + 1) * stride].rcp);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (__builtin_expect(fb[k * stride].div, 0)) {
+            const uint32_t w = w4[k >> 1];
+            q[k] = ((k & 1) ? bf16hi(w) : bf16lo(w)) / fb[k * stride].s_dec;
+        }
+    }
+    uint32_t word = e2m1_pair<0>(0u, q[0], q[1]);
+    word = e2m1_pair<1>(word, q[2], q[3]);
+    word = e2m1_pair<2>(word, q[4], q[5]);
+    word = e2m1_pair<3>(word, q[6], q[7]);
+    return word;
 }
 
 // ---- VALUE, vector path ------------------------------------------------------------------------
@@ -73,41 +109,32 @@ __device__ __forceinline__ uint32_t codes8(const uint4& v, const GC& g) {
 // A wave task is RW consecutive rows of one 64-chunk column slab.
 template <int FMT, bool DIFF, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
-    constexpr int RW = 4;
+    constexpr int RW = kEncodeRowsV;
     const int lane = threadIdx.x & 63;
     const uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
     const uint32_t rtile = fdiv(task, a.div_slabs);
     const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
-    const uint32_t c8 = slab * 64u + lane;
-    const bool valid = c8 < (uint32_t)a.C8;
+    const uint32_t c8raw = slab * 64u + lane;
+    const bool valid = c8raw < (uint32_t)a.C8;
+    const uint32_t c8 = valid ? c8raw : (uint32_t)a.C8 - 1u;  // idle lanes read a valid chunk
     const uint32_t h = fdiv(c8, a.div_D8);
     const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
     const int64_t r0 = (int64_t)rtile * RW;
     const int nr = (int)min<int64_t>(RW, a.rows - r0);
     const int lpg = a.lpg;
 
-    uint4 v[RW];
-    int64_t tt[RW];
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-        v[i] = make_uint4(0u, 0u, 0u, 0u);
-        tt[i] = r0 + i;
-        if (i < nr) {
-            if constexpr (GATHER) tt[i] = a.pos[r0 + i];
-            if (valid) v[i] = load_row8<DIFF>(a, tt[i], h, d);
-        }
-    }
+    u32x4 v[RW];
+    load_rows8<RW, DIFF, GATHER>(a, r0, h, d, v);
     float g = 0.0f;
     if constexpr (FMT == FMT_NVFP4) g = *a.gscale;
     const bool leader = valid && ((lane & (lpg - 1)) == 0);
 
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-        if (i >= nr) break;
         const int64_t r = r0 + i;
-        uint32_t word;
         const size_t midx = (size_t)r * (uint32_t)a.ngr + (c8 >> a.lpg_shift);
+        uint32_t word;
         if constexpr (FMT == FMT_INT4) {
             short2_t k = keys2(v[i].x), mn = k, mx = k;
             k = keys2(v[i].y); mn = min2(mn, k); mx = max2(mx, k);
@@ -118,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
             kmn = group_allreduce(kmn, lpg, imin_op);
             kmx = group_allreduce(kmx, lpg, imax_op);
             const Int4Group gp = int4_group(key_to_f32((int)kmn), key_to_f32((int)kmx));
-            word = codes8<FMT_INT4>(v[i], gp);
-            if (leader) {
+            word = int4_word(v[i], &gp, 0);
+            if (i < nr && leader) {
                 reinterpret_cast<uint16_t*>(a.meta0)[midx] = (uint16_t)f32_to_f16(gp.mn);
                 reinterpret_cast<uint16_t*>(a.meta1)[midx] = (uint16_t)f32_to_f16(gp.scale);
             }
@@ -128,12 +155,14 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
             uint32_t bam = max((uint32_t)m.x, (uint32_t)m.y);
             bam = group_allreduce(bam, lpg, umax_op);
             const Fp4Block fb = fp4_block(bam, g);
-            word = codes8<FMT_NVFP4>(v[i], fb);
-            if (leader) reinterpret_cast<uint8_t*>(a.meta0)[midx] = (uint8_t)fb.code;
+            word = fp4_word(v[i], &fb, 0);
+            if (i < nr && leader) reinterpret_cast<uint8_t*>(a.meta0)[midx] = (uint8_t)fb.code;
         }
-        if (valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)r * (uint32_t)a.C8 + c8] = word;
-        if constexpr (GATHER) {
-            if (c8 == 0) a.pos_out[r] = (int32_t)tt[i];
+        if (i < nr) {
+            if (valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)r * (uint32_t)a.C8 + c8] = word;
+            if constexpr (GATHER) {
+                if (c8raw == 0) a.pos_out[r] = a.pos[r];
+            }
         }
     }
 }
@@ -153,26 +182,22 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wsub = wave % WPG;
-    const uint32_t item = blockIdx.x * (uint32_t)IPB + (uint32_t)(wave / WPG);
-    const bool item_ok = item < a.n_tasks;
+    const uint32_t item_raw = blockIdx.x * (uint32_t)IPB + (uint32_t)(wave / WPG);
+    const bool item_ok = item_raw < a.n_tasks;
+    const uint32_t item = item_ok ? item_raw : a.n_tasks - 1u;  // surplus waves mirror the last item
     const uint32_t b = fdiv(item, a.div_slabs);
     const uint32_t slab = item - b * (uint32_t)a.n_slabs;
-    const uint32_t c8 = slab * 64u + lane;
-    const bool valid = item_ok && c8 < (uint32_t)a.C8;
+    const uint32_t c8raw = slab * 64u + lane;
+    const bool valid = item_ok && c8raw < (uint32_t)a.C8;
+    const uint32_t c8 = (c8raw < (uint32_t)a.C8) ? c8raw : (uint32_t)a.C8 - 1u;
     const uint32_t h = fdiv(c8, a.div_D8);
     const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
     const int64_t r0 = (int64_t)b * G + (int64_t)wsub * RPW;
+    // rows of this wave that exist; the others load row rows-1, which lies in this (last) group
     const int nr = item_ok ? (int)max<int64_t>(0, min<int64_t>(RPW, a.rows - r0)) : 0;
 
-    uint4 v[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        v[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (i < nr && valid) {
-            const int64_t t = GATHER ? (int64_t)a.pos[r0 + i] : r0 + i;
-            v[i] = load_row8<DIFF>(a, t, h, d);
-        }
-    }
+    u32x4 v[RPW];
+    load_rows8<RPW, DIFF, GATHER>(a, r0, h, d, v);
 
     // per-channel statistics over this wave's rows: channel 2j in .x, 2j+1 in .y of word j
     uint32_t st[NW];
@@ -180,19 +205,16 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
         short2_t mn[4], mx[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            mn[j] = (short2_t){0x7FFF, 0x7FFF};
-            mx[j] = (short2_t){-32768, -32768};
+            mn[j] = keys2(v[0][j]);
+            mx[j] = mn[j];
         }
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            if (i < nr) {
-                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        for (int i = 1; i < RPW; ++i) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    short2_t k = keys2(w4[j]);
-                    mn[j] = min2(mn[j], k);
-                    mx[j] = max2(mx[j], k);
-                }
+            for (int j = 0; j < 4; ++j) {
+                const short2_t k = keys2(v[i][j]);
+                mn[j] = min2(mn[j], k);
+                mx[j] = max2(mx[j], k);
             }
         }
 #pragma unroll
@@ -203,15 +225,11 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
     } else {
         ushort2_t am[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) am[j] = (ushort2_t){0, 0};
+        for (int j = 0; j < 4; ++j) am[j] = mag2(v[0][j]);
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            if (i < nr) {
-                am[0] = umax2(am[0], mag2(v[i].x));
-                am[1] = umax2(am[1], mag2(v[i].y));
-                am[2] = umax2(am[2], mag2(v[i].z));
-                am[3] = umax2(am[3], mag2(v[i].w));
-            }
+        for (int i = 1; i < RPW; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) am[j] = umax2(am[j], mag2(v[i][j]));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) st[j] = us2_as_u(am[j]);
@@ -251,29 +269,18 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            if (i < nr && valid) {
-                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-                uint32_t word = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    word |= int4_code(bf16lo(w4[j]), gp[2 * j]) << (8 * j);
-                    word |= int4_code(bf16hi(w4[j]), gp[2 * j + 1]) << (8 * j + 4);
-                }
-                reinterpret_cast<uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8] = word;
-            }
+            const uint32_t word = int4_word(v[i], gp, 1);
+            if (i < nr && valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8] = word;
         }
         if (wsub == 0 && valid) {
-            uint4 mins, scales;
-            mins.x = f32_to_f16(gp[0].mn) | (f32_to_f16(gp[1].mn) << 16);
-            mins.y = f32_to_f16(gp[2].mn) | (f32_to_f16(gp[3].mn) << 16);
-            mins.z = f32_to_f16(gp[4].mn) | (f32_to_f16(gp[5].mn) << 16);
-            mins.w = f32_to_f16(gp[6].mn) | (f32_to_f16(gp[7].mn) << 16);
-            scales.x = f32_to_f16(gp[0].scale) | (f32_to_f16(gp[1].scale) << 16);
-            scales.y = f32_to_f16(gp[2].scale) | (f32_to_f16(gp[3].scale) << 16);
-            scales.z = f32_to_f16(gp[4].scale) | (f32_to_f16(gp[5].scale) << 16);
-            scales.w = f32_to_f16(gp[6].scale) | (f32_to_f16(gp[7].scale) << 16);
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.meta0) + mbase) = mins;
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.meta1) + mbase) = scales;
+            u32x4 mins, scales;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mins[j] = f32_to_f16(gp[2 * j].mn) | (f32_to_f16(gp[2 * j + 1].mn) << 16);
+                scales[j] = f32_to_f16(gp[2 * j].scale) | (f32_to_f16(gp[2 * j + 1].scale) << 16);
+            }
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.meta0) + mbase) = mins;
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.meta1) + mbase) = scales;
         }
     } else {
         const float g = *a.gscale;
@@ -286,16 +293,8 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            if (i < nr && valid) {
-                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-                uint32_t word = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    word |= fp4_code(bf16lo(w4[j]), fb[2 * j]) << (8 * j);
-                    word |= fp4_code(bf16hi(w4[j]), fb[2 * j + 1]) << (8 * j + 4);
-                }
-                reinterpret_cast<uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8] = word;
-            }
+            const uint32_t word = fp4_word(v[i], fb, 1);
+            if (i < nr && valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8] = word;
         }
         if (wsub == 0 && valid) {
             uint2 sc;
@@ -427,68 +426,69 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_gen(EncArgs a) {
 
 // ---- NVFP4 tensor amax + global multiplier -----------------------------------------------------
 
-// Grid-stride max of |x| (bf16 magnitude bits) over every encoded element. Each block folds its
-// maximum into ws[0]; the last block to finish (counter ws[1]) turns the tensor amax into the
-// global multiplier, stores it, and returns the workspace to zero for the next call.
-template <bool DIFF, bool GATHER, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_amax(EncArgs a, uint64_t total) {
-    constexpr int U = 4;
-    uint32_t m = 0;
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    for (uint64_t u0 = (uint64_t)blockIdx.x * kThreads + threadIdx.x; u0 < total; u0 += stride * U) {
-        if constexpr (VEC) {
-            uint4 v[U];
-#pragma unroll
-            for (int k = 0; k < U; ++k) {
-                const uint64_t u = u0 + k * stride;
-                v[k] = make_uint4(0u, 0u, 0u, 0u);
-                if (u < total) {
-                    const uint32_t r = fdiv((uint32_t)u, a.div_C8);
-                    const uint32_t c8 = (uint32_t)u - r * (uint32_t)a.C8;
-                    const uint32_t h = fdiv(c8, a.div_D8);
-                    const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
-                    const int64_t t = GATHER ? (int64_t)a.pos[r] : (int64_t)r;
-                    v[k] = load_row8<DIFF>(a, t, h, d);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < U; ++k) {
-                ushort2_t mm = umax2(umax2(mag2(v[k].x), mag2(v[k].y)), umax2(mag2(v[k].z), mag2(v[k].w)));
-                m = max(m, max((uint32_t)mm.x, (uint32_t)mm.y));
-            }
-        } else {
-            const int64_t HD = (int64_t)a.H * a.D;
-            for (int k = 0; k < U; ++k) {
-                const uint64_t u = u0 + k * stride;
-                if (u < total) {
-                    const int64_t r = (int64_t)(u / (uint64_t)HD);
-                    const int64_t rem = (int64_t)u - r * HD;
-                    const int64_t h = rem / a.D;
-                    const int64_t d = rem - h * a.D;
-                    const int64_t t = GATHER ? (int64_t)a.pos[r] : r;
-                    m = max(m, load_one<DIFF>(a, t, h, d) & 0x7FFFu);
-                }
-            }
-        }
-    }
+// max |x| (bf16 magnitude bits) over every encoded element, in two launches without atomics:
+// each block of the amax kernel writes its partial maximum to ws[blockIdx.x]; a one-block
+// finalize kernel folds the partials into the tensor amax and stores the global multiplier.
+// Vector path: a wave task is RW rows of one 64-chunk slab (all loads issued at once); waves
+// stride over tasks.
+__device__ __forceinline__ uint32_t block_max(uint32_t m) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
     __shared__ uint32_t sm[kThreads / 64];
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        m = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
-        atomicMax(&a.ws[0], m);
-        __threadfence();
-        const uint32_t ticket = atomicAdd(&a.ws[1], 1u);
-        if (ticket == gridDim.x - 1) {
-            __threadfence();
-            const uint32_t amax = atomicMax(&a.ws[0], 0u);
-            *a.gscale = fp4_global(amax);
-            atomicExch(&a.ws[0], 0u);
-            atomicExch(&a.ws[1], 0u);
-        }
+    return max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+}
+
+template <bool DIFF, bool GATHER>
+__global__ __launch_bounds__(kThreads) void k_amax_vec(EncArgs a) {
+    constexpr int RW = DIFF ? 4 : 8;
+    const int lane = threadIdx.x & 63;
+    uint32_t m = 0;
+    const uint32_t nwaves = gridDim.x * 4u;
+    for (uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6)); task < a.n_tasks;
+         task += nwaves) {
+        const uint32_t rtile = fdiv(task, a.div_slabs);
+        const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
+        const uint32_t c8raw = slab * 64u + lane;
+        const uint32_t c8 = (c8raw < (uint32_t)a.C8) ? c8raw : (uint32_t)a.C8 - 1u;
+        const uint32_t h = fdiv(c8, a.div_D8);
+        const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
+        u32x4 v[RW];
+        load_rows8<RW, DIFF, GATHER>(a, (int64_t)rtile * RW, h, d, v);
+        ushort2_t mm = (ushort2_t){0, 0};
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            mm = umax2(mm, umax2(umax2(mag2(v[i].x), mag2(v[i].y)), umax2(mag2(v[i].z), mag2(v[i].w))));
+        m = max(m, max((uint32_t)mm.x, (uint32_t)mm.y));
     }
+    m = block_max(m);
+    if (threadIdx.x == 0) a.ws[blockIdx.x] = m;
+}
+
+// Generic path: grid-stride over elements.
+template <bool DIFF, bool GATHER>
+__global__ __launch_bounds__(kThreads) void k_amax_gen(EncArgs a, uint64_t total) {
+    uint32_t m = 0;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    const int64_t HD = (int64_t)a.H * a.D;
+    for (uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
+        const int64_t r = (int64_t)(u / (uint64_t)HD);
+        const int64_t rem = (int64_t)u - r * HD;
+        const int64_t h = rem / a.D;
+        const int64_t d = rem - h * a.D;
+        const int64_t t = GATHER ? (int64_t)a.pos[r] : r;
+        m = max(m, load_one<DIFF>(a, t, h, d) & 0x7FFFu);
+    }
+    m = block_max(m);
+    if (threadIdx.x == 0) a.ws[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* parts, uint32_t nparts, float* gscale) {
+    uint32_t m = 0;
+    for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, parts[i]);
+    m = block_max(m);
+    if (threadIdx.x == 0) *gscale = fp4_global(m);
 }
 
 __global__ void k_set_global(float* gscale, uint32_t bits) { *gscale = __uint_as_float(bits); }
@@ -553,14 +553,24 @@ hipError_t encode_fmt(int kind, const EncArgs& a, bool diff, bool gather, bool v
 
 template <bool DIFF, bool GATHER>
 hipError_t amax_dispatch(const EncArgs& a, bool vec, hipStream_t s) {
-    const uint64_t total = vec ? (uint64_t)a.rows * (uint64_t)a.C8 : (uint64_t)a.rows * a.H * a.D;
-    uint64_t blocks = (total + kThreads * 4 - 1) / (kThreads * 4);
-    if (blocks > 1024) blocks = 1024;
-    if (blocks < 1) blocks = 1;
-    if (vec)
-        hipLaunchKernelGGL((k_amax<DIFF, GATHER, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a, total);
-    else
-        hipLaunchKernelGGL((k_amax<DIFF, GATHER, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a, total);
+    uint32_t blocks;
+    if (vec) {
+        // amax tiles: 8 rows per wave task (4 for a residual, which loads two tensors)
+        const uint32_t rw = DIFF ? 4u : 8u;
+        EncArgs b = a;
+        b.n_tasks = (uint32_t)((a.rows + rw - 1) / rw) * (uint32_t)a.n_slabs;
+        blocks = ceil_div_u(b.n_tasks, 4);
+        if (blocks > kAmaxMaxBlocks) blocks = kAmaxMaxBlocks;
+        hipLaunchKernelGGL((k_amax_vec<DIFF, GATHER>), dim3(blocks), dim3(kThreads), 0, s, b);
+    } else {
+        const uint64_t total = (uint64_t)a.rows * a.H * a.D;
+        const uint64_t want = (total + kThreads * 4 - 1) / (kThreads * 4);
+        blocks = (uint32_t)(want > 1024 ? 1024 : (want < 1 ? 1 : want));
+        hipLaunchKernelGGL((k_amax_gen<DIFF, GATHER>), dim3(blocks), dim3(kThreads), 0, s, a, total);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(kThreads), 0, s, a.ws, blocks, a.gscale);
     return hipGetLastError();
 }
 

@@ -9,6 +9,9 @@
 namespace kvq {
 
 enum : int { FMT_INT4 = 0, FMT_NVFP4 = 1 };
+
+// The NVFP4 amax pass writes one partial maximum per block into the workspace.
+#define KVQ_AMAX_MAX_BLOCKS 4096u
 enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 
 // Rows being encoded: row r is source row t = pos ? pos[r] : r; the element value is
@@ -31,7 +34,7 @@ struct EncArgs {
     void* meta0;
     void* meta1;
     float* gscale;
-    uint32_t* ws;  // NVFP4: [0] amax bits, [1] finished-block counter
+    uint32_t* ws;  // NVFP4: per-block partial maxima of the amax pass
 };
 
 // Rows being decoded: packed row r goes to output row t = pos ? pos[r] : r; with `prev`

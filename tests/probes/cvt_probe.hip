@@ -1,0 +1,101 @@
+// cvt_probe.hip -- exhaustive check of gfx950 conversion instructions against the codec's
+// software roundings (test infrastructure; loaded only by tests/test_gpu_cvt_proof.py).
+//
+// For every binary32 bit pattern (2^32 inputs, NaNs skipped) it compares
+//   [0] v_cvt_pk_bf16_f32            with kvq::ref::f32_to_bf16       (round to nearest even)
+//   [1] v_cvt_f16_f32                with kvq::ref::f32_to_f16        (nearest even, gradual underflow)
+//   [2] v_cvt_scalef32_pk_fp4_f32    with kvq::ref::e2m1_mag + sign   (scale 1.0), all finite inputs
+//   [3] the same, restricted to |x| <= 8 (the range the NVFP4 encoder feeds it)
+// and, for the 16 E2M1 codes,
+//   [4] v_cvt_scalef32_pk_f32_fp4    with kvq::ref::e2m1_value        (scale 1.0)
+//   [5] nibble order of both packed instructions (first value in the low nibble) and the
+//       exact widening of all 65536 binary16 patterns to binary32 (NaNs skipped)
+// counting mismatches and recording the smallest mismatching input of each check.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.hpp"
+
+using namespace kvq;
+
+namespace {
+
+constexpr int kChecks = 6;
+
+__global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint32_t* first) {
+    unsigned long long c[kChecks] = {0, 0, 0, 0, 0, 0};
+    uint32_t f[kChecks] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < (1ull << 32); u += stride) {
+        const uint32_t bits = (uint32_t)u;
+        const float x = __uint_as_float(bits);
+        if (__builtin_isnan(x)) continue;
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 w = {x, x};
+        const uint32_t hw_bf = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf2)) & 0xFFFFu;
+        if (hw_bf != ref::f32_to_bf16(x)) { ++c[0]; f[0] = min(f[0], bits); }
+        const uint32_t hw_h = __builtin_bit_cast(uint16_t, (_Float16)x);
+        if (hw_h != ref::f32_to_f16(x)) { ++c[1]; f[1] = min(f[1], bits); }
+        if (!__builtin_isinf(x)) {
+            const uint32_t hw4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x, x, 1.0f, 0) & 0xFu;
+            const uint32_t sw4 = ref::e2m1_mag(x) | ((bits >> 28) & 8u);
+            if (hw4 != sw4) {
+                ++c[2]; f[2] = min(f[2], bits);
+                if (__builtin_fabsf(x) <= 8.0f) { ++c[3]; f[3] = min(f[3], bits); }
+            }
+        }
+        if (bits < 65536u) {
+            // binary16 -> binary32 widening, compared with the exact value h * 2^-24 (subnormal)
+            // or the rebiased pattern (normal, inf)
+            const uint32_t hb = bits;
+            const _Float16 hh = __builtin_bit_cast(_Float16, (uint16_t)hb);
+            const uint32_t E = (hb >> 10) & 31u, M = hb & 1023u, S = (hb & 0x8000u) << 16;
+            if (!(E == 31u && M != 0u)) {
+                uint32_t want;
+                if (E == 0u)
+                    want = S | __float_as_uint((float)M * 5.9604644775390625e-8f);
+                else if (E == 31u)
+                    want = S | 0x7F800000u;
+                else
+                    want = S | ((E + 112u) << 23) | (M << 13);
+                if (__float_as_uint((float)hh) != want) { ++c[5]; f[5] = min(f[5], bits); }
+            }
+        }
+        if (bits == 0u) {
+            // pair order: 1.0 (code 2) and -6.0 (code 15) -> byte 0xF2; byte 0xF2 -> {1.0, -6.0}
+            const uint32_t enc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, 1.0f, -6.0f, 1.0f, 0) & 0xFFu;
+            const auto dec = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(0xF2u, 1.0f, 0);
+            if (enc != 0xF2u || dec[0] != 1.0f || dec[1] != -6.0f) { ++c[5]; f[5] = min(f[5], 0xF2u); }
+        }
+        if (bits < 16u) {
+            const float hv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bits, 1.0f, 0)[0];
+            if (__float_as_uint(hv) != __float_as_uint(ref::e2m1_value(bits))) { ++c[4]; f[4] = min(f[4], bits); }
+        }
+    }
+    for (int i = 0; i < kChecks; ++i) {
+        if (c[i]) {
+            atomicAdd(&counts[i], c[i]);
+            atomicMin(&first[i], f[i]);
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_host) {
+    unsigned long long* counts = nullptr;
+    uint32_t* first = nullptr;
+    if (hipMalloc(&counts, kChecks * sizeof(unsigned long long)) != hipSuccess) return 1;
+    if (hipMalloc(&first, kChecks * sizeof(uint32_t)) != hipSuccess) return 2;
+    hipMemset(counts, 0, kChecks * sizeof(unsigned long long));
+    hipMemset(first, 0xFF, kChecks * sizeof(uint32_t));
+    hipLaunchKernelGGL(k_probe, dim3(4096), dim3(256), 0, 0, counts, first);
+    if (hipGetLastError() != hipSuccess) return 3;
+    if (hipDeviceSynchronize() != hipSuccess) return 4;
+    hipMemcpy(counts_host, counts, kChecks * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    hipMemcpy(first_host, first, kChecks * sizeof(uint32_t), hipMemcpyDeviceToHost);
+    hipFree(counts);
+    hipFree(first);
+    return 0;
+}

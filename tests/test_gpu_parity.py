@@ -210,7 +210,7 @@ def test_ties_zeros_and_constants(kind):
         assert_bits_equal(gy, oy, f"zeros {fmt} decoded")
 
 
-def test_workspace_is_reset_between_calls():
+def test_workspace_reuse_across_calls():
     rng = np.random.default_rng(9)
     a = normal_kv(rng, 256, 8, 128)
     b = bf16_bits(oracle.bf16_to_f32(normal_kv(rng, 256, 8, 128)) * 1e-3)
