@@ -52,6 +52,28 @@ def algo_bytes(op: str, fmt: str, n: int) -> float:
     raise ValueError(op)
 
 
+def measured_traffic(kernel_name: str):
+    """HBM bytes per launch of `kernel_name` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (profiles/traffic.json, copy-kernel scaled), or None if those counters were taken on
+    other kernel sources or for another kernel."""
+    import glob
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    srcs = sorted(glob.glob(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc", "*")))
+    for p in srcs + [os.path.join(ROOT, "include", "kvq.h")]:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    if rec.get("source_sha256") != h.hexdigest() or rec.get("kernel") != kernel_name:
+        return None
+    return float(rec["traffic_bytes"])
+
+
 def cpu_baseline(T_sample: int):
     """The oracle (single-threaded plain C) on the leading T_sample rows of the same workload."""
     import oracle
@@ -86,6 +108,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", default="")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain copy kernel of a known size (268 MB) after warmup, for counter scaling")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -157,6 +181,14 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        # a sparse residual with no rows decodes out of place as one row-copy kernel over the
+        # whole tensor: T*H*D*2 bytes read and the same written
+        x0 = X["key"][0]
+        empty = kvq.encode_residual(x0, x0, "key", "int4", 64, positions=torch.zeros(0, dtype=torch.int32, device=dev))
+        kvq.decode_residual(empty, x0, out=torch.empty_like(x0))
+        torch.cuda.synchronize()
+        print(f"copy calibration: {x0.numel() * 2} bytes read and written", file=sys.stderr)
 
     # per-op table from an instrumented pass (events around every op; not the timed region)
     prof = []
@@ -225,7 +257,7 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom_name),
         },
         "cpu_baseline": cpu,
     }

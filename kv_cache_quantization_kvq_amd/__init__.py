@@ -24,7 +24,9 @@ from typing import Dict, Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvq.so")
+# KVQ_LIBRARY may point at another build of the same library (e.g. a tuning variant); it must
+# exist like the default one does -- there is no fallback.
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 
 KIND = {"key": 0, "value": 1}
 FORMAT = {"int4": 0, "nvfp4": 1}

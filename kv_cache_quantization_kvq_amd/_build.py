@@ -34,9 +34,9 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, build_dir: str) -> str:
+def _compile(src: str, build_dir: str, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *("-D" + d for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -49,22 +49,23 @@ def _compile(src: str, build_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libkvq.so`` in the package directory. Always rebuilds."""
-    build_dir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link the library (default ``libkvq.so`` in the package
+    directory; ``out``/``defines`` build a variant elsewhere). Always rebuilds."""
+    build_dir = os.path.join(PKG, "_build") if out == LIB else out + ".build"
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc link failed")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

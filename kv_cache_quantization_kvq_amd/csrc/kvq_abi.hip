@@ -192,7 +192,7 @@ kvq_status encode_common(const kvq_tensor* cur, const kvq_tensor* prev, const in
     }
     if (vec) {
         if (kind == KVQ_VALUE) {
-            fill_vec_geometry(a, rows, H, D, G, 8);  // rows per VALUE-encode wave task
+            fill_vec_geometry(a, rows, H, D, G, KVQ_ENCODE_ROWS_V);
         } else {
             fill_vec_geometry(a, rows, H, D, G, G);
         }
@@ -252,10 +252,10 @@ kvq_status decode_common(const kvq_packed* p, const kvq_tensor* prev, const kvq_
     if (p->kind == KVQ_VALUE) {
         vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8);
     } else {
-        vec = vec && (G % 8 == 0) &&
+        vec = vec && (G % 8 == 0) && (G % KVQ_DECODE_ROWS == 0) &&
               (p->format == KVQ_INT4 ? (aligned(p->meta0, 16) && aligned(p->meta1, 16)) : aligned(p->meta0, 8));
     }
-    if (vec) fill_vec_geometry(a, rows, H, D, G, 8);
+    if (vec) fill_vec_geometry(a, rows, H, D, G, KVQ_DECODE_ROWS);
     return hip_status(launch_decode(p->format, p->kind, a, prev != nullptr, positions != nullptr, vec, stream));
 }
 

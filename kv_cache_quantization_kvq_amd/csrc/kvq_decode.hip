@@ -31,7 +31,7 @@ __device__ __forceinline__ uint32_t finish_pair(float y0, float y1, uint32_t pre
 
 template <int FMT, int KIND, bool ADD, bool SCATTER>
 __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
-    constexpr int RW = 8;
+    constexpr int RW = KVQ_DECODE_ROWS;
     const int lane = threadIdx.x & 63;
     const uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;

@@ -24,7 +24,7 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kEncodeRowsV = 8;                           // rows per VALUE-encode wave task
+constexpr int kEncodeRowsV = KVQ_ENCODE_ROWS_V;           // rows per VALUE-encode wave task
 constexpr uint32_t kAmaxMaxBlocks = KVQ_AMAX_MAX_BLOCKS;  // partial maxima held in the workspace
 
 // ---- element access ----------------------------------------------------------------------------
@@ -484,12 +484,29 @@ __global__ __launch_bounds__(kThreads) void k_amax_gen(EncArgs a, uint64_t total
     if (threadIdx.x == 0) a.ws[blockIdx.x] = m;
 }
 
-__global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* parts, uint32_t nparts, float* gscale) {
-    uint32_t m = 0;
-    for (uint32_t i = threadIdx.x; i < nparts; i += kThreads) m = max(m, parts[i]);
-    m = block_max(m);
-    if (threadIdx.x == 0) *gscale = fp4_global(m);
+// One block of 1024 threads folds up to kAmaxMaxBlocks partials (four independent loads per
+// thread) and stores the global multiplier.
+__global__ __launch_bounds__(1024) void k_amax_finalize(const uint32_t* parts, uint32_t nparts, float* gscale) {
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t i = threadIdx.x + 1024u * k;
+        v[k] = (i < nparts) ? parts[i] : 0u;
+    }
+    uint32_t m = max(max(v[0], v[1]), max(v[2], v[3]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    __shared__ uint32_t sm[16];
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < 16; ++w) t = max(t, sm[w]);
+        *gscale = fp4_global(t);
+    }
 }
+
+static_assert(KVQ_AMAX_MAX_BLOCKS <= 4096u, "finalize folds at most 4 partials per thread");
 
 __global__ void k_set_global(float* gscale, uint32_t bits) { *gscale = __uint_as_float(bits); }
 
@@ -570,7 +587,7 @@ hipError_t amax_dispatch(const EncArgs& a, bool vec, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(kThreads), 0, s, a.ws, blocks, a.gscale);
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(1024), 0, s, a.ws, blocks, a.gscale);
     return hipGetLastError();
 }
 

@@ -12,6 +12,16 @@ enum : int { FMT_INT4 = 0, FMT_NVFP4 = 1 };
 
 // The NVFP4 amax pass writes one partial maximum per block into the workspace.
 #define KVQ_AMAX_MAX_BLOCKS 4096u
+
+// Rows per wave task of the vector VALUE encoder and of the vector decoder (a KEY decode needs
+// G % KVQ_DECODE_ROWS == 0 so that a task's rows share one token group). Shared by the host
+// code that sizes the grids and the kernels.
+#ifndef KVQ_ENCODE_ROWS_V
+#define KVQ_ENCODE_ROWS_V 8
+#endif
+#ifndef KVQ_DECODE_ROWS
+#define KVQ_DECODE_ROWS 8
+#endif
 enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 
 // Rows being encoded: row r is source row t = pos ? pos[r] : r; the element value is
