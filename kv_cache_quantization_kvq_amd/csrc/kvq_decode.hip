@@ -12,6 +12,8 @@
 // writes them with one 16-byte store. A wave task is RW consecutive rows of one 64-chunk slab;
 // for KEY those rows share their token group (G % RW == 0), so the lane loads its 8 channels'
 // metadata once per task.
+#include <type_traits>
+
 #include "kvq_launch.hpp"
 
 namespace kvq {
@@ -32,8 +34,11 @@ __device__ __forceinline__ uint32_t finish_pair(float y0, float y1, uint32_t pre
 template <int FMT, int KIND, bool ADD, bool SCATTER>
 __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     constexpr int RW = KVQ_DECODE_ROWS;
+    __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
+    if constexpr (FMT == FMT_NVFP4) fp4_table_fill(tab, *a.gscale);
     const int lane = threadIdx.x & 63;
-    const uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+    const uint32_t task =
+        __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, gridDim.x) * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
     const uint32_t rtile = fdiv(task, a.div_slabs);
     const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
@@ -63,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     }
     // per-row metadata (VALUE): one group per lane and row
     float vs[RW], vm[RW];
+    uint32_t vc[RW];
     if constexpr (KIND == KIND_VALUE) {
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
@@ -71,14 +77,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
                 vs[i] = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta1)[midx]);
                 vm[i] = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta0)[midx]);
             } else {
-                vs[i] = (float)reinterpret_cast<const uint8_t*>(a.meta0)[midx];  // code, scaled below
+                vc[i] = reinterpret_cast<const uint8_t*>(a.meta0)[midx] & 0x7Fu;  // scaled below
                 vm[i] = 0.0f;
             }
         }
     }
-
-    float g = 0.0f;
-    if constexpr (FMT == FMT_NVFP4) g = *a.gscale;
 
     // KEY: per-channel metadata of this task's token group (G % RW == 0), loaded once
     float ks[8], km[8];
@@ -99,13 +102,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
             const uint32_t sw[2] = {sc.x, sc.y};
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                ks[k] = e4m3_decode((sw[k >> 2] >> (8 * (k & 3))) & 0xFFu) / g;
+                ks[k] = tab.e[(sw[k >> 2] >> (8 * (k & 3))) & 0x7Fu][0];  // sign bit of a stored scale is 0
                 km[k] = 0.0f;
             }
         }
     } else if constexpr (FMT == FMT_NVFP4) {
 #pragma unroll
-        for (int i = 0; i < RW; ++i) vs[i] = e4m3_decode((uint32_t)vs[i]) / g;
+        for (int i = 0; i < RW; ++i) vs[i] = tab.e[vc[i]][0];
     }
 
 #pragma unroll
@@ -144,6 +147,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
 // Generic path: one thread per (row, head, channel pair).
 template <int FMT, int KIND, bool ADD, bool SCATTER>
 __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
+    __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
+    if constexpr (FMT == FMT_NVFP4) fp4_table_fill(tab, *a.gscale);
     const int D = a.D, G = a.G;
     const int Dp = (D + 1) / 2;
     const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -153,8 +158,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
     const int64_t h = rem / Dp;
     const int j = (int)(rem - h * Dp);
     const int64_t t = SCATTER ? (int64_t)a.pos[r] : r;
-    float g = 0.0f;
-    if constexpr (FMT == FMT_NVFP4) g = *a.gscale;
     const uint32_t byte = a.codes[(size_t)(r * a.H + h) * Dp + j];
     for (int k = 0; k < 2; ++k) {
         const int dd = 2 * j + k;
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
             y = int4_value(c, f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta1)[midx]),
                            f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta0)[midx]));
         } else {
-            y = __fmul_rn(e2m1_values<0>(c)[0], e4m3_decode(reinterpret_cast<const uint8_t*>(a.meta0)[midx]) / g);
+            y = __fmul_rn(e2m1_values<0>(c)[0], tab.e[reinterpret_cast<const uint8_t*>(a.meta0)[midx] & 0x7Fu][0]);
         }
         uint32_t outb = bf16_bits(y);
         if constexpr (ADD) {

@@ -138,6 +138,25 @@ __device__ __forceinline__ f32x2 e2m1_values(uint32_t word) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
 }
 
+// ---- division by the format constants -----------------------------------------------------
+
+// fl(x / K) for x >= 0 and K in {15, 6}, from one multiply by fl(1/K) and one FMA correction:
+// q0 = fl(x * c), r = fma(-K, q0, x) (exact), q = fma(r, c, q0). The result equals the IEEE
+// quotient for every non-negative binary32 of at least 2^-100 (tests/probes/cvt_probe.hip checks
+// all of them); smaller x take the division.
+template <int K>
+__device__ __forceinline__ float div_const(float x) {
+    constexpr float c = 1.0f / (float)K;
+    if (__builtin_expect(x < 7.888609052210118e-31f, 0)) return x / (float)K;  // x < 2^-100
+    const float q0 = __fmul_rn(x, c);
+    const float r = __builtin_fmaf(-(float)K, q0, x);
+    return __builtin_fmaf(r, c, q0);
+}
+
+// Approximate reciprocal (v_rcp_f32, within one ulp of fl(1/x) for normal x with a normal
+// reciprocal, as the probe checks); used only where a bounded error is allowed.
+__device__ __forceinline__ float rcp_approx(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // ---- sortable keys --------------------------------------------------------------------------
 
 // bf16 bit pattern -> int with the order of IEEE totalOrder on finite values (-0 < +0):
@@ -193,6 +212,16 @@ __device__ __forceinline__ uint32_t group_allreduce(uint32_t v, int lanes, Op op
     return v;
 }
 
+// ---- block order ------------------------------------------------------------------------------
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). This maps the
+// hardware block id to a logical one so that every XCD works on one contiguous range of
+// logical blocks (a bijection on [0, n)); neighbouring tasks that share data then share an L2.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t n) {
+    const uint32_t x = b & 7u, i = b >> 3, q = n >> 3, r = n & 7u;
+    return (x < r) ? x * (q + 1u) + i : r * (q + 1u) + (x - r) * q + i;
+}
+
 // ---- integer division by a runtime constant --------------------------------------------------
 
 // n / d for 32-bit n with a precomputed multiplier (round-up method): t = mulhi(n, m),
@@ -207,39 +236,69 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 
 // ---- INT4 element code ----------------------------------------------------------------------
 
-// Per-group constants of an INT4 group: the minimum, the FP32 scale fl(fl(mx - mn) / 15) and
-// its reciprocal. A scale of 0 takes rcp = 0 (every code 0); a scale whose reciprocal
-// overflows sets `exact` so that every member uses the division.
+// The codes need rne(fl(d / scale)) bit for bit, where d = fl(x - mn). fl(d / scale) lands on a
+// half-integer (and then rounds to even) far more often than chance, because fl(range / 15)
+// is within half an ulp of range / 15, so a quotient is exact only if it is correctly rounded.
+// This is done without a division or a branch by Markstein's theorem (P. Markstein, IBM J.
+// Res. Dev. 34(1), 1990; also the Handbook of Floating-Point Arithmetic, division chapter): if
+// y = RN(1/b) and q is a faithful approximation of a/b, then r = a - b*q is exact under FMA and
+// RN(q + r*y) = RN(a/b).
+//  * y: one Newton step on v_rcp_f32; that this equals RN(1/scale) for every scale in
+//    [2^-100, 2^100] is checked exhaustively on the device.
+//  * faithful q: q0 = RN(d*y + RN(d*ylo)) with ylo = RN((1 - scale*y) * y), the low part of
+//    1/scale; d*(y + ylo) is within 2^-46 (relative) of d/scale, so q0 is within
+//    half an ulp plus that of the quotient.
+//  * range: for 2^-100 <= scale <= 2^100 no intermediate underflows for any member whose quotient
+//    reaches 0.25 (smaller quotients give code 0 whatever their last bits), and none overflows.
+// Other scales: 0 gives y = ylo = 0 and every code 0; the rest (subnormal or huge) set `slow`
+// and divide.
 struct Int4Group {
-    float mn, scale, rcp;
-    bool exact;
+    float mn, scale, y, ylo;
+    bool slow;
 };
 
-__device__ __forceinline__ Int4Group int4_group(float mn, float mx) {
+__device__ __forceinline__ float rcp_rn(float s) {
+    const float y0 = rcp_approx(s);
+    const float e = __builtin_fmaf(-s, y0, 1.0f);
+    return __builtin_fmaf(e, y0, y0);
+}
+
+// Group constants for a given FP32 scale.
+__device__ __forceinline__ Int4Group int4_group_scale(float mn, float scale) {
     Int4Group g;
     g.mn = mn;
-    float range = __fsub_rn(mx, mn);
-    g.scale = range / 15.0f;
-    float r = (g.scale != 0.0f) ? 1.0f / g.scale : 0.0f;
-    g.exact = __builtin_isinf(r);
-    g.rcp = r;
+    g.scale = scale;
+    const bool fast = scale >= 7.888609052210118e-31f && scale <= 1.2676506002282294e30f;  // 2^-100, 2^100
+    const float y = rcp_rn(scale);
+    const float ylo = __fmul_rn(__builtin_fmaf(-scale, y, 1.0f), y);
+    g.y = fast ? y : 0.0f;
+    g.ylo = fast ? ylo : 0.0f;
+    g.slow = !fast && scale != 0.0f;
     return g;
 }
 
-// code = clamp(rne(fl(fl(x - mn) / scale)), 0, 15), bit-exact with the IEEE division.
-// Fast path: q' = fl(d * fl(1/scale)) differs from fl(d/scale) by at most 3*2^-24*q + tiny
-// (q <= 15 + 2^-12), i.e. below 2^-18; whenever q' is farther than 2^-17 from a half-integer,
-// both round to the same integer. Otherwise (or when 1/scale overflowed) divide.
+__device__ __forceinline__ Int4Group int4_group(float mn, float mx) {
+    return int4_group_scale(mn, div_const<15>(__fsub_rn(mx, mn)));  // fl(fl(mx - mn) / 15), exactly
+}
+
+// fl(d / scale) for a fast group and d >= 0 whose quotient is at least 0.25; below that it
+// stays below 0.5 (0 for a zero scale).
+__device__ __forceinline__ float int4_quot_raw(float d, const Int4Group& g) {
+    const float q0 = __builtin_fmaf(d, g.y, __fmul_rn(d, g.ylo));
+    const float r = __builtin_fmaf(-g.scale, q0, d);
+    return __builtin_fmaf(r, g.y, q0);
+}
+
+// rne(fl(d / scale)) as a float, for a fast group and any d >= 0.
+__device__ __forceinline__ float int4_quot(float d, const Int4Group& g) { return __builtin_rintf(int4_quot_raw(d, g)); }
+
+// code = clamp(rne(fl(fl(x - mn) / scale)), 0, 15).
 // The clamp never binds for bf16 members: x >= mn gives d >= +0, and d <= fl(mx - mn) with
 // scale >= (mx - mn)/15 * (1 - 2^-13) (the worst case is a subnormal scale over the smallest
 // nonzero bf16 range 2^-133) keeps q below 15.01, so rne(q) is already in [0, 15].
 __device__ __forceinline__ uint32_t int4_code(float x, const Int4Group& g) {
-    float d = __fsub_rn(x, g.mn);
-    float q = __fmul_rn(d, g.rcp);
-    float c = __builtin_rintf(q);
-    if (__builtin_expect(g.exact || __builtin_fabsf(__fsub_rn(q, c)) > 0.4999923706054688f, 0)) {
-        c = __builtin_rintf(d / g.scale);
-    }
+    const float d = __fsub_rn(x, g.mn);
+    const float c = __builtin_expect(g.slow, 0) ? __builtin_rintf(d / g.scale) : int4_quot(d, g);
     return (uint32_t)c;
 }
 
@@ -261,18 +320,37 @@ struct Fp4Block {
     bool div;
 };
 
-__device__ __forceinline__ Fp4Block fp4_block(uint32_t bamax_bits, float g) {
+// Per-code decode scale and multiplier for one tensor multiplier g: s_dec = fl(f32(c) / g),
+// r = fl(1 / s_dec) (+inf when it overflows, 0 for the zero code). Computed with IEEE divisions.
+__device__ __forceinline__ f32x2 fp4_code_scales(uint32_t c, float g) {
+    const float sf = e4m3_decode(c);
+    const float s_dec = sf / g;
+    const float r = (sf != 0.0f) ? 1.0f / s_dec : 0.0f;
+    return (f32x2){s_dec, r};
+}
+
+// The per-code table of one kernel launch, in LDS: entry c holds fp4_code_scales(c, g) for
+// the 127 finite positive E4M3 codes (block scales never exceed 448 = code 126).
+struct Fp4Table {
+    f32x2 e[128];
+};
+
+// Fill the table (every thread of the block must call it; ends with a barrier).
+__device__ __forceinline__ void fp4_table_fill(Fp4Table& t, float g) {
+    for (uint32_t c = threadIdx.x; c < 128u; c += blockDim.x) t.e[c] = fp4_code_scales(c, g);
+    __syncthreads();
+}
+
+__device__ __forceinline__ Fp4Block fp4_block(uint32_t bamax_bits, float g, const Fp4Table& t) {
     Fp4Block b;
-    float bamax = bf16_to_f32(bamax_bits);
-    float t6 = bamax / 6.0f;
+    const float t6 = div_const<6>(bf16_to_f32(bamax_bits));  // fl(bamax / 6), exactly
     float s = __fmul_rn(g, t6);
     s = (s <= 448.0f) ? s : 448.0f;  // also maps +inf to 448
     b.code = e4m3_encode(s);
-    float sf = e4m3_decode(b.code);
-    b.s_dec = sf / g;
-    float r = (sf != 0.0f) ? 1.0f / b.s_dec : 0.0f;
-    b.div = __builtin_isinf(r);
-    b.rcp = r;
+    const f32x2 e = t.e[b.code];
+    b.s_dec = e[0];
+    b.div = __builtin_isinf(e[1]);
+    b.rcp = e[1];
     return b;
 }
 

@@ -17,6 +17,8 @@
 // chunk) whose value cannot change a min, max or abs-max, and only the stores are masked.
 // Generic path: any D, G, stride or alignment; one thread per (row, head) for VALUE and per
 // (token group, head, channel pair) for KEY, two passes over the members.
+#include <type_traits>
+
 #include "kvq_launch.hpp"
 
 namespace kvq {
@@ -69,32 +71,59 @@ __device__ __forceinline__ uint32_t imin_op(uint32_t x, uint32_t y) { return (ui
 __device__ __forceinline__ uint32_t imax_op(uint32_t x, uint32_t y) { return (uint32_t)max((int)x, (int)y); }
 __device__ __forceinline__ uint32_t umax_op(uint32_t x, uint32_t y) { return max(x, y); }
 
-// 8 INT4 codes of one chunk (channel 2j in nibble 2j); group constants gp[k * stride]
-__device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* gp, int stride) {
+// 8 INT4 codes of one chunk (channel 2j in nibble 2j); group constants gp[k * stride].
+// `slow` (a lane's OR of its groups' slow flags) sends the whole chunk through the division.
+// Codes are integer-valued floats in [0, 15]; v_cvt_pk_u8_f32 places the even channels' codes
+// in the bytes of one word and the odd channels' in another, and one shift-or interleaves them.
+__device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* gp, int stride, bool slow) {
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    uint32_t word = 0;
+    float d[8], c[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        word |= int4_code(bf16lo(w4[j]), gp[(2 * j) * stride]) << (8 * j);
-        word |= int4_code(bf16hi(w4[j]), gp[(2 * j + 1) * stride]) << (8 * j + 4);
+        d[2 * j] = __fsub_rn(bf16lo(w4[j]), gp[(2 * j) * stride].mn);
+        d[2 * j + 1] = __fsub_rn(bf16hi(w4[j]), gp[(2 * j + 1) * stride].mn);
     }
-    return word;
+    if (__builtin_expect(slow, 0)) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const Int4Group& g = gp[k * stride];
+            c[k] = g.slow ? __builtin_rintf(d[k] / g.scale) : int4_quot(d[k], g);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] = int4_quot(d[k], gp[k * stride]);
+    }
+    uint32_t even = 0, odd = 0;
+    even = __builtin_amdgcn_cvt_pk_u8_f32(c[0], 0, even);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(c[1], 0, odd);
+    even = __builtin_amdgcn_cvt_pk_u8_f32(c[2], 1, even);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(c[3], 1, odd);
+    even = __builtin_amdgcn_cvt_pk_u8_f32(c[4], 2, even);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(c[5], 2, odd);
+    even = __builtin_amdgcn_cvt_pk_u8_f32(c[6], 3, even);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(c[7], 3, odd);
+    return even | (odd << 4);
 }
 
-// 8 NVFP4 codes of one chunk: scaled values, then 4 packed E2M1 conversions
+// 8 NVFP4 codes of one chunk: scaled values, then 4 packed E2M1 conversions. One (rarely
+// taken) branch per chunk applies the direct division where a block's 1/s_dec overflowed.
 __device__ __forceinline__ uint32_t fp4_word(const u32x4& v, const Fp4Block* fb, int stride) {
     float q[8];
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    bool div = false;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         q[2 * j] = __fmul_rn(bf16lo(w4[j]), fb[(2 * j) * stride].rcp);
         q[2 * j + 1] = __fmul_rn(bf16hi(w4[j]), fb[(2 * j + 1) * stride].rcp);
+        div |= fb[(2 * j) * stride].div | fb[(2 * j + 1) * stride].div;
     }
+    if (__builtin_expect(div, 0)) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        if (__builtin_expect(fb[k * stride].div, 0)) {
-            const uint32_t w = w4[k >> 1];
-            q[k] = ((k & 1) ? bf16hi(w) : bf16lo(w)) / fb[k * stride].s_dec;
+        for (int k = 0; k < 8; ++k) {
+            if (fb[k * stride].div) {
+                const uint32_t w = w4[k >> 1];
+                q[k] = ((k & 1) ? bf16hi(w) : bf16lo(w)) / fb[k * stride].s_dec;
+            }
         }
     }
     uint32_t word = e2m1_pair<0>(0u, q[0], q[1]);
@@ -110,6 +139,12 @@ __device__ __forceinline__ uint32_t fp4_word(const u32x4& v, const Fp4Block* fb,
 template <int FMT, bool DIFF, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
     constexpr int RW = kEncodeRowsV;
+    __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
+    float g = 0.0f;
+    if constexpr (FMT == FMT_NVFP4) {
+        g = *a.gscale;
+        fp4_table_fill(tab, g);
+    }
     const int lane = threadIdx.x & 63;
     const uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
@@ -126,8 +161,6 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 
     u32x4 v[RW];
     load_rows8<RW, DIFF, GATHER>(a, r0, h, d, v);
-    float g = 0.0f;
-    if constexpr (FMT == FMT_NVFP4) g = *a.gscale;
     const bool leader = valid && ((lane & (lpg - 1)) == 0);
 
 #pragma unroll
@@ -145,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
             kmn = group_allreduce(kmn, lpg, imin_op);
             kmx = group_allreduce(kmx, lpg, imax_op);
             const Int4Group gp = int4_group(key_to_f32((int)kmn), key_to_f32((int)kmx));
-            word = int4_word(v[i], &gp, 0);
+            word = int4_word(v[i], &gp, 0, gp.slow);
             if (i < nr && leader) {
                 reinterpret_cast<uint16_t*>(a.meta0)[midx] = (uint16_t)f32_to_f16(gp.mn);
                 reinterpret_cast<uint16_t*>(a.meta1)[midx] = (uint16_t)f32_to_f16(gp.scale);
@@ -154,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
             ushort2_t m = umax2(umax2(mag2(v[i].x), mag2(v[i].y)), umax2(mag2(v[i].z), mag2(v[i].w)));
             uint32_t bam = max((uint32_t)m.x, (uint32_t)m.y);
             bam = group_allreduce(bam, lpg, umax_op);
-            const Fp4Block fb = fp4_block(bam, g);
+            const Fp4Block fb = fp4_block(bam, g, tab);
             word = fp4_word(v[i], &fb, 0);
             if (i < nr && leader) reinterpret_cast<uint8_t*>(a.meta0)[midx] = (uint8_t)fb.code;
         }
@@ -178,6 +211,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
     constexpr int IPB = 4 / WPG;
     constexpr int NW = (FMT == FMT_INT4) ? 8 : 4;  // exchanged words per lane
     __shared__ uint32_t lds[WPG > 1 ? 4 * NW * 64 : 1];
+    __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
+    float g = 0.0f;
+    if constexpr (FMT == FMT_NVFP4) {
+        g = *a.gscale;
+        fp4_table_fill(tab, g);
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -267,9 +306,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
             gp[2 * j] = int4_group(key_to_f32(mn.x), key_to_f32(mx.x));
             gp[2 * j + 1] = int4_group(key_to_f32(mn.y), key_to_f32(mx.y));
         }
+        bool slow = false;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) slow |= gp[k].slow;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            const uint32_t word = int4_word(v[i], gp, 1);
+            const uint32_t word = int4_word(v[i], gp, 1, slow);
             if (i < nr && valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8] = word;
         }
         if (wsub == 0 && valid) {
@@ -283,13 +325,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
             *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.meta1) + mbase) = scales;
         }
     } else {
-        const float g = *a.gscale;
         Fp4Block fb[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const ushort2_t am = as_us2(st[j]);
-            fb[2 * j] = fp4_block(am.x, g);
-            fb[2 * j + 1] = fp4_block(am.y, g);
+            fb[2 * j] = fp4_block(am.x, g, tab);
+            fb[2 * j + 1] = fp4_block(am.y, g, tab);
         }
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
@@ -314,6 +355,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
 // VALUE: one thread per (row, head), groups walked along the row.
 template <int FMT, bool DIFF, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_encode_v_gen(EncArgs a) {
+    __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
+    float g = 0.0f;
+    if constexpr (FMT == FMT_NVFP4) {
+        g = *a.gscale;
+        fp4_table_fill(tab, g);
+    }
     const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (idx >= a.rows * a.H) return;
     const int64_t r = idx / a.H;
@@ -322,8 +369,6 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_gen(EncArgs a) {
     const int D = a.D, G = a.G;
     const int ngr = (D + G - 1) / G;
     const int Dp = (D + 1) / 2;
-    float g = 0.0f;
-    if constexpr (FMT == FMT_NVFP4) g = *a.gscale;
     uint8_t* crow = a.codes + (size_t)(r * a.H + h) * Dp;
     uint32_t pending = 0;
     for (int c = 0; c < ngr; ++c) {
@@ -349,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_gen(EncArgs a) {
         } else {
             uint32_t bam = 0;
             for (int dd = d0; dd < d1; ++dd) bam = max(bam, load_one<DIFF>(a, t, h, dd) & 0x7FFFu);
-            const Fp4Block fb = fp4_block(bam, g);
+            const Fp4Block fb = fp4_block(bam, g, tab);
             reinterpret_cast<uint8_t*>(a.meta0)[midx] = (uint8_t)fb.code;
             for (int dd = d0; dd < d1; ++dd) {
                 const uint32_t code = fp4_code(bf16_to_f32(load_one<DIFF>(a, t, h, dd)), fb);
@@ -369,6 +414,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_gen(EncArgs a) {
 // KEY: one thread per (token group, head, channel pair 2j / 2j+1).
 template <int FMT, bool DIFF, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_encode_k_gen(EncArgs a) {
+    __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
+    float g = 0.0f;
+    if constexpr (FMT == FMT_NVFP4) {
+        g = *a.gscale;
+        fp4_table_fill(tab, g);
+    }
     const int D = a.D, G = a.G;
     const int Dp = (D + 1) / 2;
     const int64_t nb = (a.rows + G - 1) / G;
@@ -380,8 +431,6 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_gen(EncArgs a) {
     const int j = (int)(rem - h * Dp);
     const int nch = (2 * j + 1 < D) ? 2 : 1;
     const int64_t r_begin = b * G, r_end = min<int64_t>(a.rows, r_begin + G);
-    float g = 0.0f;
-    if constexpr (FMT == FMT_NVFP4) g = *a.gscale;
 
     Int4Group gp[2];
     Fp4Block fb[2];
@@ -405,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_gen(EncArgs a) {
                 const int64_t t = GATHER ? (int64_t)a.pos[r] : r;
                 bam = max(bam, load_one<DIFF>(a, t, h, dd) & 0x7FFFu);
             }
-            fb[k] = fp4_block(bam, g);
+            fb[k] = fp4_block(bam, g, tab);
             reinterpret_cast<uint8_t*>(a.meta0)[midx] = (uint8_t)fb[k].code;
         }
     }

@@ -8,8 +8,21 @@
 //   [3] the same, restricted to |x| <= 8 (the range the NVFP4 encoder feeds it)
 // and, for the 16 E2M1 codes,
 //   [4] v_cvt_scalef32_pk_f32_fp4    with kvq::ref::e2m1_value        (scale 1.0)
-//   [5] nibble order of both packed instructions (first value in the low nibble) and the
-//       exact widening of all 65536 binary16 patterns to binary32 (NaNs skipped)
+//   [5] nibble order of both packed instructions (first value in the low nibble), the exact
+//       widening of all 65536 binary16 patterns to binary32 (NaNs skipped), and
+//       v_cvt_pk_u8_f32 on the integer-valued floats 0..15 (byte placement, other bytes kept)
+//   [6] kvq::div_const<15>(x) with the IEEE quotient x / 15, every finite x >= 0
+//   [7] kvq::div_const<6>(x)  with the IEEE quotient x / 6,  every finite x >= 0
+//   [8] kvq::rcp_approx(x) within one ulp of the IEEE 1 / x, every normal x > 0 whose
+//       reciprocal is normal
+//   [9] kvq::rcp_rn(x) (v_rcp_f32 plus one Newton step) equal to the IEEE 1 / x, every x in
+//       [2^-100, 2^100]
+// and, in a second kernel, the INT4 quotient kvq::int4_quot_raw(d, group(scale)) against the
+// IEEE d / scale for every scale significand (2^23) at eight exponents from 2^-100 to 2^99:
+//   [10] d = RN(m * scale) and its two neighbours for the 512 points m = h + k * ulp(h) / 2
+//        (h = 0.5 ... 15.5, k = -16 ... 15), i.e. quotients at and next to every half-integer
+//        and float midpoint near it, plus one pseudo-random d in [scale / 2, 16 scale): the
+//        quotient bits must match; for d = RN(scale * 2^-j), j = 3 ... 40, the code (rint) must
 // counting mismatches and recording the smallest mismatching input of each check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -20,11 +33,12 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kChecks = 6;
+constexpr int kChecks = 11;
 
 __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint32_t* first) {
-    unsigned long long c[kChecks] = {0, 0, 0, 0, 0, 0};
-    uint32_t f[kChecks] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    unsigned long long c[kChecks] = {};
+    uint32_t f[kChecks];
+    for (int i = 0; i < kChecks; ++i) f[i] = 0xFFFFFFFFu;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < (1ull << 32); u += stride) {
         const uint32_t bits = (uint32_t)u;
@@ -43,6 +57,17 @@ __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint3
             if (hw4 != sw4) {
                 ++c[2]; f[2] = min(f[2], bits);
                 if (__builtin_fabsf(x) <= 8.0f) { ++c[3]; f[3] = min(f[3], bits); }
+            }
+        }
+        if (!(bits >> 31) && !__builtin_isinf(x)) {
+            if (__float_as_uint(div_const<15>(x)) != __float_as_uint(x / 15.0f)) { ++c[6]; f[6] = min(f[6], bits); }
+            if (__float_as_uint(div_const<6>(x)) != __float_as_uint(x / 6.0f)) { ++c[7]; f[7] = min(f[7], bits); }
+            if (x >= 1.1754943508222875e-38f && x <= 8.507059173023462e37f) {  // x and 1/x normal
+                const int32_t e = (int32_t)__float_as_uint(rcp_approx(x)) - (int32_t)__float_as_uint(1.0f / x);
+                if (e > 1 || e < -1) { ++c[8]; f[8] = min(f[8], bits); }
+            }
+            if (x >= 7.888609052210118e-31f && x <= 1.2676506002282294e30f) {  // 2^-100 .. 2^100
+                if (__float_as_uint(rcp_rn(x)) != __float_as_uint(1.0f / x)) { ++c[9]; f[9] = min(f[9], bits); }
             }
         }
         if (bits < 65536u) {
@@ -67,6 +92,11 @@ __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint3
             const uint32_t enc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, 1.0f, -6.0f, 1.0f, 0) & 0xFFu;
             const auto dec = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(0xF2u, 1.0f, 0);
             if (enc != 0xF2u || dec[0] != 1.0f || dec[1] != -6.0f) { ++c[5]; f[5] = min(f[5], 0xF2u); }
+            // v_cvt_pk_u8_f32 of the integer-valued floats 0..15 (INT4 code packing)
+            for (uint32_t k = 0; k < 16u; ++k) {
+                const uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32((float)k, 2, 0xAABBCCDDu);
+                if (b != ((0xAABBCCDDu & 0xFF00FFFFu) | (k << 16))) { ++c[5]; f[5] = min(f[5], 0x100u + k); }
+            }
         }
         if (bits < 16u) {
             const float hv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bits, 1.0f, 0)[0];
@@ -81,6 +111,45 @@ __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint3
     }
 }
 
+// One scale significand and one of the 512 (h, k) points per thread, for eight exponents.
+__global__ __launch_bounds__(256) void k_probe_div(unsigned long long* counts, uint32_t* first) {
+    unsigned long long c = 0;
+    uint32_t f = 0xFFFFFFFFu;
+    const int kExp[8] = {-100, -99, -60, -1, 0, 1, 37, 99};
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < (1ull << 32); u += stride) {
+        const uint32_t sig = (uint32_t)u & 0x7FFFFFu, j = (uint32_t)(u >> 23);
+        const double h = 0.5 + (double)(j & 15u);
+        const int k = (int)((j >> 4) & 31u) - 16;
+        const int eh = (h < 1.0) ? -1 : (h < 2.0) ? 0 : (h < 4.0) ? 1 : (h < 8.0) ? 2 : 3;
+        const double m = h + (double)k * __builtin_ldexp(1.0, eh - 24);
+        for (int ei = 0; ei < 8; ++ei) {
+            const float s = __builtin_ldexpf(__uint_as_float(0x3F800000u | sig), kExp[ei]);
+            const Int4Group g = int4_group_scale(0.0f, s);
+            if (g.slow || g.y == 0.0f) { ++c; f = min(f, (uint32_t)u); continue; }
+            const float d0 = (float)(m * (double)s);
+            const uint32_t db = __float_as_uint(d0);
+            const uint32_t hsh = (uint32_t)(u * 2654435761ull) ^ (uint32_t)ei * 0x9E3779B9u;
+            const float dr = __uint_as_float(__float_as_uint(s) - (1u << 23) + hsh % (5u << 23));
+            const float ds[4] = {d0, __uint_as_float(db - 1u), __uint_as_float(db + 1u), dr};
+            for (int t = 0; t < 4; ++t) {
+                if (__float_as_uint(int4_quot_raw(ds[t], g)) != __float_as_uint(ds[t] / s)) {
+                    ++c;
+                    f = min(f, (uint32_t)u);
+                }
+            }
+            if (j < 38u) {  // tiny quotients: only the code is specified
+                const float dt = __builtin_ldexpf(s, -(int)j - 3);
+                if (int4_quot(dt, g) != __builtin_rintf(dt / s)) { ++c; f = min(f, (uint32_t)u); }
+            }
+        }
+    }
+    if (c) {
+        atomicAdd(&counts[10], c);
+        atomicMin(&first[10], f);
+    }
+}
+
 }  // namespace
 
 extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_host) {
@@ -91,6 +160,8 @@ extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_ho
     hipMemset(counts, 0, kChecks * sizeof(unsigned long long));
     hipMemset(first, 0xFF, kChecks * sizeof(uint32_t));
     hipLaunchKernelGGL(k_probe, dim3(4096), dim3(256), 0, 0, counts, first);
+    if (hipGetLastError() != hipSuccess) return 3;
+    hipLaunchKernelGGL(k_probe_div, dim3(4096), dim3(256), 0, 0, counts, first);
     if (hipGetLastError() != hipSuccess) return 3;
     if (hipDeviceSynchronize() != hipSuccess) return 4;
     hipMemcpy(counts_host, counts, kChecks * sizeof(unsigned long long), hipMemcpyDeviceToHost);
