@@ -203,14 +203,16 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 // ---- KEY, vector path --------------------------------------------------------------------------
 
 // An item is one token group (G rows) of one 64-chunk column slab. WPG waves share an item,
-// RPW rows each; a block of 4 waves holds 4/WPG items.
+// RPW rows each; a block of WPB waves holds WPB/WPG items.
 template <int FMT, int G, bool DIFF, bool GATHER>
-__global__ __launch_bounds__(kThreads) void k_encode_k_vec(EncArgs a) {
-    constexpr int WPG = (G >= 64) ? 4 : G / 16;
-    constexpr int RPW = G / WPG;
-    constexpr int IPB = 4 / WPG;
+__global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(EncArgs a) {
+    constexpr int WPG = key_waves_per_group(G);
+    constexpr int RPW = key_rows_per_wave(G);
+    constexpr int WPB = key_waves_per_block(G);
+    constexpr int IPB = WPB / WPG;
     constexpr int NW = (FMT == FMT_INT4) ? 8 : 4;  // exchanged words per lane
-    __shared__ uint32_t lds[WPG > 1 ? 4 * NW * 64 : 1];
+    static_assert(WPB <= 16 && WPB % WPG == 0, "KEY encoder block shape");
+    __shared__ uint32_t lds[WPG > 1 ? WPB * NW * 64 : 1];
     __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
     float g = 0.0f;
     if constexpr (FMT == FMT_NVFP4) {
@@ -561,6 +563,14 @@ __global__ void k_set_global(float* gscale, uint32_t bits) { *gscale = __uint_as
 
 inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
 
+// One block per WPB / WPG token-group items.
+template <int FMT, int G, bool DIFF, bool GATHER>
+void launch_key_vec(const EncArgs& a, hipStream_t s) {
+    constexpr uint32_t ipb = (uint32_t)(key_waves_per_block(G) / key_waves_per_group(G));
+    hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER>), dim3(ceil_div_u(a.n_tasks, ipb)),
+                       dim3(64 * key_waves_per_block(G)), 0, s, a);
+}
+
 template <int FMT, bool DIFF, bool GATHER>
 hipError_t encode_dispatch(int kind, const EncArgs& a, bool vec, hipStream_t s) {
     if (vec) {
@@ -570,23 +580,16 @@ hipError_t encode_dispatch(int kind, const EncArgs& a, bool vec, hipStream_t s) 
         } else {
             switch (a.G) {
                 case 16:
-                    hipLaunchKernelGGL((k_encode_k_vec<FMT, 16, DIFF, GATHER>), dim3(ceil_div_u(a.n_tasks, 4)),
-                                       dim3(kThreads), 0, s, a);
+                    launch_key_vec<FMT, 16, DIFF, GATHER>(a, s);
                     break;
                 case 32:
-                    if constexpr (FMT == FMT_INT4)
-                        hipLaunchKernelGGL((k_encode_k_vec<FMT, 32, DIFF, GATHER>), dim3(ceil_div_u(a.n_tasks, 2)),
-                                           dim3(kThreads), 0, s, a);
+                    if constexpr (FMT == FMT_INT4) launch_key_vec<FMT, 32, DIFF, GATHER>(a, s);
                     break;
                 case 64:
-                    if constexpr (FMT == FMT_INT4)
-                        hipLaunchKernelGGL((k_encode_k_vec<FMT, 64, DIFF, GATHER>), dim3(a.n_tasks), dim3(kThreads), 0,
-                                           s, a);
+                    if constexpr (FMT == FMT_INT4) launch_key_vec<FMT, 64, DIFF, GATHER>(a, s);
                     break;
                 case 128:
-                    if constexpr (FMT == FMT_INT4)
-                        hipLaunchKernelGGL((k_encode_k_vec<FMT, 128, DIFF, GATHER>), dim3(a.n_tasks), dim3(kThreads),
-                                           0, s, a);
+                    if constexpr (FMT == FMT_INT4) launch_key_vec<FMT, 128, DIFF, GATHER>(a, s);
                     break;
                 default:
                     return hipErrorInvalidValue;

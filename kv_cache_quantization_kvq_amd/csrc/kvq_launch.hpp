@@ -22,6 +22,17 @@ enum : int { FMT_INT4 = 0, FMT_NVFP4 = 1 };
 #ifndef KVQ_DECODE_ROWS
 #define KVQ_DECODE_ROWS 8
 #endif
+// Rows per wave of the vector KEY encoder (a power of two): min(G, KVQ_KEY_ROWS), but at least
+// G / 16 so that the G / rows waves sharing a token group fit one block of at most 1024 threads.
+#ifndef KVQ_KEY_ROWS
+#define KVQ_KEY_ROWS 8
+#endif
+constexpr int key_rows_per_wave(int G) {
+    const int r = G < KVQ_KEY_ROWS ? G : KVQ_KEY_ROWS;
+    return r < G / 16 ? G / 16 : r;
+}
+constexpr int key_waves_per_group(int G) { return G / key_rows_per_wave(G); }
+constexpr int key_waves_per_block(int G) { return key_waves_per_group(G) > 4 ? key_waves_per_group(G) : 4; }
 enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 
 // Rows being encoded: row r is source row t = pos ? pos[r] : r; the element value is
