@@ -27,7 +27,7 @@ _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
 
 KIND = {"key": 0, "value": 1}
-FORMAT = {"int4": 0, "nvfp4": 1}
+FORMAT = {"int4": 0, "nvfp4": 1, "nvfp4_row": 2, "fp8_row": 3}
 
 # -O2 without -march=native; -ffp-contract=off so that no multiply-add is fused.
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared"]
@@ -67,6 +67,14 @@ def _lib():
         lib.kvq_oracle_decode_residual.argtypes = [ci, ci, i32, i64, i64, i64, p, p, p, p, p, p, i64, i64, i64,
                                                    p, i64, i64]
         lib.kvq_oracle_decode_residual.restype = ci
+        lib.kvq_oracle_pack_paged.argtypes = [p, i64, i64, i64, i64, i64, i64, i64, ci, ci, i32, ci, p, p, p, p]
+        lib.kvq_oracle_pack_paged.restype = ci
+        lib.kvq_oracle_unpack_paged.argtypes = [ci, ci, i32, ci, i64, i64, i64, i64, p, p, p, p, p, i64, i64, i64]
+        lib.kvq_oracle_unpack_paged.restype = ci
+        lib.kvq_oracle_store_rows.argtypes = [p, i64, i64, i64, i64, i64, p, ci, ci, i32, i64, p, p, p]
+        lib.kvq_oracle_store_rows.restype = ci
+        lib.kvq_oracle_load_rows.argtypes = [ci, ci, i32, i64, i64, i64, p, p, p, p, p, i64, p, i64, i64]
+        lib.kvq_oracle_load_rows.restype = ci
         lib.kvq_oracle_storage_bytes.argtypes = [ci, ci, i32, i64, i64, i64, ci]
         lib.kvq_oracle_storage_bytes.restype = i64
         lib.kvq_oracle_nvfp4_global.argtypes = [ctypes.c_float]
@@ -105,7 +113,15 @@ def ceil_div(a: int, b: int) -> int:
 
 @dataclass
 class Packed:
-    """One encoded tensor: codes [rows, H, ceil(D/2)] u8, metadata planes, global scale, positions."""
+    """One encoded tensor: codes, metadata planes, global scale, positions.
+
+    codes: [rows, H, ceil(D/2)] u8 nibbles ([rows, H, D] one byte per element for fp8_row).
+    meta0: int4 f16 minimum bits (uint16); nvfp4 and nvfp4_row E4M3 block scales (uint8);
+           fp8_row FP32 row scales [rows, H].
+    meta1: int4 f16 scale bits (uint16); nvfp4_row FP32 row multipliers [rows, H]; else None.
+    global_scale: nvfp4 float32[1]; else None.
+    page_local / page_size: set by pack_paged when KEY groups were kept inside pages (the KEY
+    metadata then has ceil(page_size/G) rows per page)."""
 
     format: str
     kind: str
@@ -114,26 +130,42 @@ class Packed:
     H: int
     D: int
     codes: np.ndarray
-    meta0: np.ndarray  # int4: f16 minimum bits (uint16); nvfp4: E4M3 block scale bytes (uint8)
-    meta1: Optional[np.ndarray]  # int4: f16 scale bits (uint16); nvfp4: None
-    global_scale: Optional[np.ndarray]  # nvfp4: float32[1]
+    meta0: np.ndarray
+    meta1: Optional[np.ndarray]
+    global_scale: Optional[np.ndarray]
     positions: Optional[np.ndarray] = field(default=None)  # sparse residual: owned int32 copy
+    page_local: bool = False
+    page_size: int = 0
 
 
-def meta_shape(kind: str, G: int, rows: int, H: int, D: int):
+def meta_shape(kind: str, G: int, rows: int, H: int, D: int, fmt: str = "int4"):
+    if fmt == "nvfp4_row":
+        return (rows, H, ceil_div(D, 16))
+    if fmt == "fp8_row":
+        return (rows, H)
     return (ceil_div(rows, G), H, D) if kind == "key" else (rows, H, ceil_div(D, G))
 
 
-def _alloc(fmt: str, kind: str, G: int, rows: int, H: int, D: int) -> Packed:
-    codes = np.zeros((rows, H, ceil_div(D, 2)), np.uint8)
-    ms = meta_shape(kind, G, rows, H, D)
+def _alloc(fmt: str, kind: str, G: int, rows: int, H: int, D: int, key_meta_rows: Optional[int] = None) -> Packed:
+    codes = np.zeros((rows, H, D if fmt == "fp8_row" else ceil_div(D, 2)), np.uint8)
+    ms = meta_shape(kind, G, rows, H, D, fmt)
+    if key_meta_rows is not None:
+        ms = (key_meta_rows, H, D)
     if fmt == "int4":
         return Packed(fmt, kind, G, rows, H, D, codes, np.zeros(ms, np.uint16), np.zeros(ms, np.uint16), None)
-    return Packed(fmt, kind, G, rows, H, D, codes, np.zeros(ms, np.uint8), None, np.zeros(1, np.float32))
+    if fmt == "nvfp4":
+        return Packed(fmt, kind, G, rows, H, D, codes, np.zeros(ms, np.uint8), None, np.zeros(1, np.float32))
+    if fmt == "nvfp4_row":
+        return Packed(fmt, kind, G, rows, H, D, codes, np.zeros(ms, np.uint8), np.zeros((rows, H), np.float32), None)
+    return Packed(fmt, kind, G, rows, H, D, codes, np.zeros(ms, np.float32), None, None)
 
 
 def default_group(fmt: str) -> int:
-    return 64 if fmt == "int4" else 16
+    return {"int4": 64, "nvfp4": 16, "nvfp4_row": 16, "fp8_row": 0}[fmt]
+
+
+def _group(fmt: str, G: Optional[int]) -> int:
+    return default_group(fmt) if G is None or (G == 0 and fmt != "fp8_row") else int(G)
 
 
 def pack(x: np.ndarray, kind: str, fmt: str = "int4", G: Optional[int] = None,
@@ -141,7 +173,7 @@ def pack(x: np.ndarray, kind: str, fmt: str = "int4", G: Optional[int] = None,
     """pack_kv of a bf16 [T, H, D] view. ``global_scale`` (NVFP4 only) encodes these rows with
     the multiplier of a larger tensor they are a slice of; by default the rows are the whole
     encoded tensor and the multiplier is computed from their own amax."""
-    G = G or default_group(fmt)
+    G = _group(fmt, G)
     st, sh = _view_strides(x)
     T, H, D = x.shape
     out = _alloc(fmt, kind, G, T, H, D)
@@ -169,7 +201,7 @@ def encode_residual(cur: np.ndarray, prev: np.ndarray, kind: str, fmt: str = "in
                     positions: Optional[np.ndarray] = None, global_scale: Optional[float] = None) -> Packed:
     """encode_residual of cur against the reconstructed predecessor prev (both [T, H, D]).
     ``global_scale`` as in ``pack``."""
-    G = G or default_group(fmt)
+    G = _group(fmt, G)
     cst, csh = _view_strides(cur)
     pst, psh = _view_strides(prev)
     if cur.shape != prev.shape:
@@ -216,6 +248,76 @@ def tensor_amax(cur: np.ndarray, prev: Optional[np.ndarray] = None, positions: O
     pos = None if positions is None else np.ascontiguousarray(positions, dtype=np.int32)
     M = 0 if pos is None else int(pos.shape[0])
     return float(_lib().kvq_oracle_tensor_amax(_ptr(cur), cst, csh, _ptr(prev), pst, psh, T, H, D, _ptr(pos), M))
+
+
+def _paged_strides(x: np.ndarray):
+    if x.dtype != np.uint16 or x.ndim != 4:
+        raise ValueError("expected a uint16 [P, S, H, D] array of bf16 bits")
+    sp, ss, sh, sd = (s // 2 for s in x.strides)
+    if x.size and x.shape[3] > 1 and sd != 1:
+        raise ValueError("channel stride must be 1")
+    return sp, ss, sh
+
+
+def pack_paged(x: np.ndarray, kind: str, fmt: str = "int4", G: Optional[int] = None, page_local: bool = False) -> Packed:
+    """pack_paged of a bf16 paged view [P, S, H, D] (pages in page-major token order)."""
+    G = _group(fmt, G)
+    sp, ss, sh = _paged_strides(x)
+    P, S, H, D = x.shape
+    local = bool(page_local) and kind == "key" and fmt in ("int4", "nvfp4")
+    out = _alloc(fmt, kind, G, P * S, H, D, key_meta_rows=P * ceil_div(S, G) if local else None)
+    out.page_local, out.page_size = local, S
+    rc = _lib().kvq_oracle_pack_paged(_ptr(x), P, S, H, D, sp, ss, sh, KIND[kind], FORMAT[fmt], G, int(local),
+                                      _ptr(out.codes), _ptr(out.meta0), _ptr(out.meta1), _ptr(out.global_scale))
+    if rc:
+        raise ValueError(f"oracle pack_paged failed ({rc})")
+    return out
+
+
+def unpack_paged(p: Packed, P: int, S: int, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """unpack_paged: decoded bf16 bits written into a paged view [P, S, H, D]."""
+    if P * S != p.rows:
+        raise ValueError("pages x page_size != rows")
+    if out is None:
+        out = np.zeros((P, S, p.H, p.D), np.uint16)
+    sp, ss, sh = _paged_strides(out)
+    rc = _lib().kvq_oracle_unpack_paged(KIND[p.kind], FORMAT[p.format], p.group_size, int(p.page_local), P, S, p.H,
+                                        p.D, _ptr(p.codes), _ptr(p.meta0), _ptr(p.meta1), _ptr(p.global_scale),
+                                        _ptr(out), sp, ss, sh)
+    if rc:
+        raise ValueError(f"oracle unpack_paged failed ({rc})")
+    return out
+
+
+def store_rows(cache: Packed, x: np.ndarray, slots: np.ndarray) -> None:
+    """Quantize the rows x[N, H, D] and write row i into cache row slots[i] (in place)."""
+    st, sh = _view_strides(x)
+    N, H, D = x.shape
+    if (H, D) != (cache.H, cache.D):
+        raise ValueError("row shape mismatch")
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    if sl.shape != (N,):
+        raise ValueError("one slot per row")
+    rc = _lib().kvq_oracle_store_rows(_ptr(x), N, H, D, st, sh, _ptr(sl), KIND[cache.kind], FORMAT[cache.format],
+                                      cache.group_size, cache.rows, _ptr(cache.codes), _ptr(cache.meta0),
+                                      _ptr(cache.meta1))
+    if rc:
+        raise ValueError(f"oracle store_rows failed ({rc})")
+
+
+def load_rows(cache: Packed, slots: np.ndarray, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Decoded bf16 bits of cache rows slots[0..N) as [N, H, D]."""
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    N = int(sl.shape[0])
+    if out is None:
+        out = np.zeros((N, cache.H, cache.D), np.uint16)
+    st, sh = _view_strides(out)
+    rc = _lib().kvq_oracle_load_rows(KIND[cache.kind], FORMAT[cache.format], cache.group_size, cache.rows, cache.H,
+                                     cache.D, _ptr(cache.codes), _ptr(cache.meta0), _ptr(cache.meta1),
+                                     _ptr(cache.global_scale), _ptr(sl), N, _ptr(out), st, sh)
+    if rc:
+        raise ValueError(f"oracle load_rows failed ({rc})")
+    return out
 
 
 def storage_bytes(fmt: str, kind: str, G: int, rows: int, H: int, D: int, sparse: bool = False) -> int:

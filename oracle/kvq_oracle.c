@@ -14,8 +14,11 @@
  *            bits per element, FP32-before-FP16 metadata rule), and the second review
  *            ("Sharing one KV-quantization interface": storage_bytes counts payload only).
  *   [PR408]  FreeToken pull request #408, "feat(kvcache): add nvfp4 kv quantization".
- *            Sections used: "Summary" (76 B per D=128 row) and the nvfp4 codec-port commit
- *            message (nibbles low first, quantize against the stored block scale).
+ *            Sections used: "Summary" (76 B per D=128 row; packed E2M1, one E4M3 scale per 16
+ *            values, one FP32 row scale per token and KV head), the fp8 commit message (one
+ *            FP32 symmetric scale per (token, KV head) row; fused quantize + scatter with slot
+ *            ids) and the nvfp4 codec-port commit message (nibbles low first, quantize against
+ *            the stored block scale, 64 + 8 + 4 = 76 B).
  *
  * Numerics. Every floating-point step is one IEEE-754 binary32 operation rounded to nearest
  * even; build with -O2 -ffp-contract=off (no fused multiply-add) and without -ffast-math.
@@ -35,6 +38,8 @@
 #define KVQO_VALUE 1
 #define KVQO_INT4 0
 #define KVQO_NVFP4 1
+#define KVQO_NVFP4_ROW 2
+#define KVQO_FP8_ROW 3
 
 /* status codes (mirrors nothing; the oracle has its own) */
 #define KVQO_OK 0
@@ -211,16 +216,29 @@ static int64_t n_groups(int kind, int32_t G, int64_t rows, int64_t H, int64_t D)
 /* Exact payload bytes. [PR166] second review: storage counts payload only (codes, metadata,
  * the FP32 tensor scale and an owned position map), no allocator slack and no decode scratch.
  * INT4 metadata is an FP16 minimum and an FP16 scale per group ([PR166] "Purpose", second
- * bullet); NVFP4 metadata is one E4M3 byte per 16 values plus one FP32 scale per tensor. */
+ * bullet); NVFP4 metadata is one E4M3 byte per 16 values plus one FP32 scale per tensor.
+ * The row formats ([PR408]) carry one FP32 scale per (token, head) row: NVFP4-row adds one
+ * E4M3 byte per 16 channels, FP8-row stores one E4M3 byte per element. */
 int64_t kvq_oracle_storage_bytes(int format, int kind, int32_t G, int64_t rows, int64_t H, int64_t D,
                                  int sparse) {
-    if (rows < 0 || H < 0 || D < 0 || G < 1) return -1;
-    if (format == KVQO_NVFP4 && G != 16) return -1;
-    int64_t codes = rows * H * ceil_div(D, 2);
-    int64_t meta = n_groups(kind, G, rows, H, D) * (format == KVQO_INT4 ? 4 : 1);
-    int64_t glob = (format == KVQO_NVFP4) ? 4 : 0;
+    if (rows < 0 || H < 0 || D < 0) return -1;
     int64_t pos = sparse ? 4 * rows : 0;
-    return codes + meta + glob + pos;
+    switch (format) {
+        case KVQO_INT4:
+            if (G < 1) return -1;
+            return rows * H * ceil_div(D, 2) + 4 * n_groups(kind, G, rows, H, D) + pos;
+        case KVQO_NVFP4:
+            if (G != 16) return -1;
+            return rows * H * ceil_div(D, 2) + n_groups(kind, 16, rows, H, D) + 4 + pos;
+        case KVQO_NVFP4_ROW:
+            if (G != 16) return -1;
+            return rows * H * (ceil_div(D, 2) + ceil_div(D, 16) + 4) + pos;
+        case KVQO_FP8_ROW:
+            if (G != 0) return -1;
+            return rows * H * (D + 4) + pos;
+        default:
+            return -1;
+    }
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -471,21 +489,92 @@ static float nvfp4_decode_one(uint8_t code, uint8_t sc8, float g) {
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* Row formats: every (token, head) row is quantized on its own ([PR408])                     */
+/* ------------------------------------------------------------------------------------------ */
+
+/* NVFP4 with one FP32 multiplier per (token, head) row. [PR408] "Summary": packed E2M1 values,
+ * one E4M3 scale per 16 values, one FP32 row scale per token and KV head; nvfp4 port commit:
+ * nibbles low first, quantization against the stored block scale, 76 B per D=128 row.
+ * READING: the row scale is the tensor format's multiplier computed over the row alone
+ * (g_row = 2688 / row amax, with the same zero and overflow rules), and the 16-value blocks
+ * run along channels for K and V alike, so each row is encoded exactly as a one-row tensor. */
+static int nvfp4_row_encode(const float* dense, int64_t rows, int64_t H, int64_t D, uint8_t* codes, uint8_t* sc8,
+                            float* grow) {
+    int64_t nb = ceil_div(D, 16);
+    uint8_t* c = (uint8_t*)calloc((size_t)(rows * H * D) + 1, 1);
+    if (!c) return KVQO_NOMEM;
+    for (int64_t r = 0; r < rows * H; ++r) {
+        float g = kvq_oracle_nvfp4_global(dense_amax(dense + r * D, D));
+        grow[r] = g;
+        nvfp4_ctx ctx = {dense + r * D, c + r * D, sc8 + r * nb, g};
+        for_each_group(KVQO_VALUE, 16, 1, 1, D, nvfp4_group, &ctx);
+    }
+    pack_nibbles(c, rows, H, D, codes);
+    free(c);
+    return KVQO_OK;
+}
+
+/* FP8 E4M3 with one FP32 symmetric scale per (token, head) row. [PR408] fp8 commit: a row of
+ * head_dim E4M3 codes plus ONE FP32 scale; attention multiplies scores by the row scale, so the
+ * stored scale is the decode multiplier.
+ * READING: scale = fl(amax_row / 448); q = fl(x / scale) (IEEE division); code =
+ * e4m3(min(|q|, 448)) with sign bit signbit(x). A zero scale (an all-zero row, or an amax so
+ * small that amax / 448 underflows to 0) gives q = +-0. */
+static int fp8_row_encode(const float* dense, int64_t rows, int64_t H, int64_t D, uint8_t* codes, float* srow) {
+    for (int64_t r = 0; r < rows * H; ++r) {
+        const float* x = dense + r * D;
+        float s = dense_amax(x, D) / 448.0f;
+        srow[r] = s;
+        for (int64_t d = 0; d < D; ++d) {
+            float v = x[d];
+            float m = 0.0f;
+            if (s != 0.0f) {
+                m = fabsf(v / s);
+                if (!(m <= 448.0f)) m = 448.0f;
+            }
+            codes[r * D + d] = kvq_oracle_f32_to_e4m3(signbit(v) ? -m : m);
+        }
+    }
+    return KVQO_OK;
+}
+
+/* FP8-row decode: y = bf16(fl(e4m3(code) * scale)) (the code's sign included). */
+static float fp8_row_decode_one(uint8_t code, float s) {
+    float y = kvq_oracle_e4m3_to_f32(code) * s;
+    return kvq_oracle_bf16_to_f32(kvq_oracle_f32_to_bf16(y));
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Public oracle entry points                                                                 */
 /* ------------------------------------------------------------------------------------------ */
 
+/* Group sizes: INT4 any G >= 1; NVFP4 and NVFP4-row 16; FP8-row 0 (one scale per row). */
 static int check_common(int kind, int format, int32_t G, int64_t rows, int64_t H, int64_t D) {
     if (kind != KVQO_KEY && kind != KVQO_VALUE) return KVQO_BAD_ARG;
-    if (format != KVQO_INT4 && format != KVQO_NVFP4) return KVQO_BAD_ARG;
-    if (G < 1 || (format == KVQO_NVFP4 && G != 16)) return KVQO_BAD_ARG;
+    switch (format) {
+        case KVQO_INT4: if (G < 1) return KVQO_BAD_ARG; break;
+        case KVQO_NVFP4:
+        case KVQO_NVFP4_ROW: if (G != 16) return KVQO_BAD_ARG; break;
+        case KVQO_FP8_ROW: if (G != 0) return KVQO_BAD_ARG; break;
+        default: return KVQO_BAD_ARG;
+    }
     if (rows < 0 || H < 0 || D < 0) return KVQO_BAD_ARG;
     return KVQO_OK;
 }
 
+/* Metadata layouts: INT4 meta0 = f16 minimums, meta1 = f16 scales (K [ceil(rows/G), H, D],
+ * V [rows, H, ceil(D/G)]); NVFP4 meta0 = E4M3 block scales (same shapes with G = 16), one FP32
+ * multiplier in gscale; NVFP4-row meta0 = E4M3 block scales [rows, H, ceil(D/16)], meta1 = FP32
+ * row multipliers [rows, H]; FP8-row meta0 = FP32 row scales [rows, H]. Codes are nibbles
+ * [rows, H, ceil(D/2)] except FP8-row, one byte per element [rows, H, D]. */
 static int encode_dense(const float* dense, int kind, int format, int32_t G, int64_t rows, int64_t H, int64_t D,
                         uint8_t* codes, void* meta0, void* meta1, float* gscale, float g_given) {
-    if (format == KVQO_INT4) return int4_encode(dense, kind, G, rows, H, D, codes, (uint16_t*)meta0, (uint16_t*)meta1);
-    return nvfp4_encode(dense, kind, rows, H, D, codes, (uint8_t*)meta0, gscale, g_given);
+    switch (format) {
+        case KVQO_INT4: return int4_encode(dense, kind, G, rows, H, D, codes, (uint16_t*)meta0, (uint16_t*)meta1);
+        case KVQO_NVFP4: return nvfp4_encode(dense, kind, rows, H, D, codes, (uint8_t*)meta0, gscale, g_given);
+        case KVQO_NVFP4_ROW: return nvfp4_row_encode(dense, rows, H, D, codes, (uint8_t*)meta0, (float*)meta1);
+        default: return fp8_row_encode(dense, rows, H, D, codes, (float*)meta0);
+    }
 }
 
 /* pack_kv: encode the strided bf16 view x[T, H, D] (token stride st, head stride sh, channel
@@ -507,7 +596,11 @@ int kvq_oracle_pack(const uint16_t* x, int64_t T, int64_t H, int64_t D, int64_t 
 /* Decoded value of element (t, h, d) of a packed tensor, as float32 holding a bf16 value. */
 static float decode_at(int kind, int format, int32_t G, int64_t H, int64_t D, const uint8_t* codes, const void* meta0,
                        const void* meta1, float g, int64_t t, int64_t h, int64_t d) {
+    if (format == KVQO_FP8_ROW) return fp8_row_decode_one(codes[(t * H + h) * D + d], ((const float*)meta0)[t * H + h]);
     uint8_t c = nibble_at(codes, H, D, t, h, d);
+    if (format == KVQO_NVFP4_ROW)
+        return nvfp4_decode_one(c, ((const uint8_t*)meta0)[(t * H + h) * ceil_div(D, 16) + d / 16],
+                                ((const float*)meta1)[t * H + h]);
     int64_t gid = (kind == KVQO_KEY) ? ((t / G) * H + h) * D + d : (t * H + h) * ceil_div(D, G) + d / G;
     if (format == KVQO_INT4)
         return int4_decode_one(c, ((const uint16_t*)meta0)[gid], ((const uint16_t*)meta1)[gid]);
@@ -619,4 +712,173 @@ void kvq_oracle_f32_to_e4m3_n(const float* x, uint8_t* y, int64_t n) {
 }
 void kvq_oracle_e2m1_encode_n(const float* q, uint8_t* y, int64_t n) {
     for (int64_t i = 0; i < n; ++i) y[i] = kvq_oracle_e2m1_encode(q[i], q[i]);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Paged views and slot writes                                                                */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Bytes of one row's codes, and of one row's entry in each row-indexed metadata plane. */
+static int64_t code_row_bytes(int format, int64_t H, int64_t D) {
+    return (format == KVQO_FP8_ROW) ? H * D : H * ceil_div(D, 2);
+}
+
+/* Whether a format groups K over tokens (its metadata rows are not the token rows). */
+static int token_grouped(int kind, int format) {
+    return kind == KVQO_KEY && (format == KVQO_INT4 || format == KVQO_NVFP4);
+}
+
+/* Rows of a paged bf16 view x[P, S, H, D] (page stride sp, slot stride ss, head stride sh,
+ * channel stride 1) in page-major order: logical token p*S + s is slot s of page p. */
+static void materialize_paged(const uint16_t* x, int64_t P, int64_t S, int64_t H, int64_t D, int64_t sp, int64_t ss,
+                              int64_t sh, float* dense) {
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t s = 0; s < S; ++s)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t d = 0; d < D; ++d)
+                    dense[((p * S + s) * H + h) * D + d] = kvq_oracle_bf16_to_f32(x[p * sp + s * ss + h * sh + d]);
+}
+
+/* pack_paged over [pages, page_size, heads, dim] ([PR166] interface review, item 3, and the
+ * stacked-PR follow-up that adds pack_paged / unpack_paged). Flat grouping packs exactly what
+ * pack() packs for the page-major token sequence (a 64-token KEY group then spans four 16-token
+ * pages). Page-local grouping ([PR166] first review, "Group ownership vs 16-token pages") keeps
+ * every KEY group inside one page: page p is encoded as its own S-token range with KEY groups
+ * over slots [b*G, min(S, (b+1)*G)), metadata [P, ceil(S/G), H, D]; the NVFP4 multiplier stays
+ * one per call, over all pages. VALUE groups and the row formats are page-local by
+ * construction; for them the flag changes nothing. */
+int kvq_oracle_pack_paged(const uint16_t* x, int64_t P, int64_t S, int64_t H, int64_t D, int64_t sp, int64_t ss,
+                          int64_t sh, int kind, int format, int32_t G, int page_local, uint8_t* codes, void* meta0,
+                          void* meta1, float* gscale) {
+    if (P < 0 || S < 0) return KVQO_BAD_ARG;
+    int rc = check_common(kind, format, G, P * S, H, D);
+    if (rc) return rc;
+    int64_t rows = P * S;
+    float* dense = (float*)malloc(sizeof(float) * (size_t)(rows * H * D) + 4);
+    if (!dense) return KVQO_NOMEM;
+    materialize_paged(x, P, S, H, D, sp, ss, sh, dense);
+    if (page_local && token_grouped(kind, format)) {
+        float g = (format == KVQO_NVFP4) ? kvq_oracle_nvfp4_global(dense_amax(dense, rows * H * D)) : -1.0f;
+        int64_t mrows = ceil_div(S, G) * H * D; /* metadata entries per page */
+        for (int64_t p = 0; p < P && rc == KVQO_OK; ++p) {
+            float gp = 0.0f;
+            void* m0 = (format == KVQO_INT4) ? (void*)((uint16_t*)meta0 + p * mrows) : (void*)((uint8_t*)meta0 + p * mrows);
+            void* m1 = (format == KVQO_INT4) ? (void*)((uint16_t*)meta1 + p * mrows) : NULL;
+            rc = encode_dense(dense + p * S * H * D, kind, format, G, S, H, D, codes + p * S * code_row_bytes(format, H, D),
+                              m0, m1, &gp, g);
+        }
+        if (format == KVQO_NVFP4) *gscale = g;
+    } else {
+        rc = encode_dense(dense, kind, format, G, rows, H, D, codes, meta0, meta1, gscale, -1.0f);
+    }
+    free(dense);
+    return rc;
+}
+
+/* unpack_paged: the decoded bf16 rows written back into a paged view y[P, S, H, D]. */
+int kvq_oracle_unpack_paged(int kind, int format, int32_t G, int page_local, int64_t P, int64_t S, int64_t H, int64_t D,
+                            const uint8_t* codes, const void* meta0, const void* meta1, const float* gscale, uint16_t* y,
+                            int64_t sp, int64_t ss, int64_t sh) {
+    if (P < 0 || S < 0) return KVQO_BAD_ARG;
+    int rc = check_common(kind, format, G, P * S, H, D);
+    if (rc) return rc;
+    float g = (format == KVQO_NVFP4) ? *gscale : 0.0f;
+    int local = page_local && token_grouped(kind, format);
+    int64_t mrows = local ? ceil_div(S, G) * H * D : 0;
+    for (int64_t p = 0; p < P; ++p) {
+        const uint8_t* cp = local ? codes + p * S * code_row_bytes(format, H, D) : codes;
+        const void* m0 = meta0;
+        const void* m1 = meta1;
+        if (local) {
+            m0 = (format == KVQO_INT4) ? (const void*)((const uint16_t*)meta0 + p * mrows)
+                                       : (const void*)((const uint8_t*)meta0 + p * mrows);
+            m1 = (format == KVQO_INT4) ? (const void*)((const uint16_t*)meta1 + p * mrows) : NULL;
+        }
+        for (int64_t s = 0; s < S; ++s) {
+            int64_t t = local ? s : p * S + s;
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t d = 0; d < D; ++d) {
+                    float v = decode_at(kind, format, G, H, D, cp, m0, m1, g, t, h, d);
+                    y[p * sp + s * ss + h * sh + d] = (uint16_t)(f32_bits(v) >> 16);
+                }
+        }
+    }
+    return KVQO_OK;
+}
+
+/* Slot ids: every id in [0, n_slots) and no id twice. */
+static int check_slots(const int32_t* slots, int64_t N, int64_t n_slots) {
+    if (N == 0) return KVQO_OK;
+    uint8_t* seen = (uint8_t*)calloc((size_t)n_slots + 1, 1);
+    if (!seen) return KVQO_NOMEM;
+    int rc = KVQO_OK;
+    for (int64_t i = 0; i < N && rc == KVQO_OK; ++i) {
+        if (slots[i] < 0 || slots[i] >= n_slots || seen[slots[i]]) rc = KVQO_BAD_ARG;
+        else seen[slots[i]] = 1;
+    }
+    free(seen);
+    return rc;
+}
+
+/* Quantize N new rows src[N, H, D] and write row i into cache row slots[i] ([PR408] fp8
+ * commit: fused quantize + scatter, slot ids given as a tensor). Only formats whose rows are
+ * encoded independently qualify: INT4 VALUE (channel groups), NVFP4-row and FP8-row. The rows
+ * are encoded as one N-row tensor, then each row's codes and row metadata move to its slot;
+ * every other cache row is left as it was. */
+int kvq_oracle_store_rows(const uint16_t* src, int64_t N, int64_t H, int64_t D, int64_t st, int64_t sh,
+                          const int32_t* slots, int kind, int format, int32_t G, int64_t n_slots, uint8_t* codes,
+                          void* meta0, void* meta1) {
+    int rc = check_common(kind, format, G, N, H, D);
+    if (rc) return rc;
+    if (!((format == KVQO_INT4 && kind == KVQO_VALUE) || format == KVQO_NVFP4_ROW || format == KVQO_FP8_ROW))
+        return KVQO_BAD_ARG;
+    rc = check_slots(slots, N, n_slots);
+    if (rc) return rc;
+    int64_t cb = code_row_bytes(format, H, D);
+    /* bytes of one row in meta0 / meta1 */
+    int64_t m0b = 0, m1b = 0;
+    if (format == KVQO_INT4) m0b = m1b = 2 * H * ceil_div(D, G);
+    if (format == KVQO_NVFP4_ROW) { m0b = H * ceil_div(D, 16); m1b = 4 * H; }
+    if (format == KVQO_FP8_ROW) m0b = 4 * H;
+    float* dense = (float*)malloc(sizeof(float) * (size_t)(N * H * D) + 4);
+    uint8_t* c = (uint8_t*)malloc((size_t)(N * cb) + 1);
+    uint8_t* t0 = (uint8_t*)malloc((size_t)(N * m0b) + 1);
+    uint8_t* t1 = (uint8_t*)malloc((size_t)(N * m1b) + 1);
+    if (!dense || !c || !t0 || !t1) rc = KVQO_NOMEM;
+    if (rc == KVQO_OK) {
+        materialize(src, st, sh, NULL, 0, 0, NULL, N, H, D, dense);
+        rc = encode_dense(dense, kind, format, G, N, H, D, c, t0, t1, NULL, -1.0f);
+    }
+    if (rc == KVQO_OK)
+        for (int64_t i = 0; i < N; ++i) {
+            int64_t r = slots[i];
+            memcpy(codes + r * cb, c + i * cb, (size_t)cb);
+            memcpy((uint8_t*)meta0 + r * m0b, t0 + i * m0b, (size_t)m0b);
+            if (m1b) memcpy((uint8_t*)meta1 + r * m1b, t1 + i * m1b, (size_t)m1b);
+        }
+    free(dense);
+    free(c);
+    free(t0);
+    free(t1);
+    return rc;
+}
+
+/* Gather-and-decode: y row i = decoded cache row slots[i], for any format (a KEY row of a
+ * token-grouped format uses the metadata of its group, row slots[i] / G). */
+int kvq_oracle_load_rows(int kind, int format, int32_t G, int64_t n_slots, int64_t H, int64_t D, const uint8_t* codes,
+                         const void* meta0, const void* meta1, const float* gscale, const int32_t* slots, int64_t N,
+                         uint16_t* y, int64_t st, int64_t sh) {
+    int rc = check_common(kind, format, G, n_slots, H, D);
+    if (rc) return rc;
+    float g = (format == KVQO_NVFP4) ? *gscale : 0.0f;
+    for (int64_t i = 0; i < N; ++i) {
+        int64_t t = slots[i];
+        if (t < 0 || t >= n_slots) return KVQO_BAD_ARG;
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t d = 0; d < D; ++d) {
+                float v = decode_at(kind, format, G, H, D, codes, meta0, meta1, g, t, h, d);
+                y[i * st + h * sh + d] = (uint16_t)(f32_bits(v) >> 16);
+            }
+    }
+    return KVQO_OK;
 }

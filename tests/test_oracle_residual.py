@@ -24,7 +24,7 @@ def add_bf16(prev_bits, delta_bits):
     return bf16_bits(s)
 
 
-FORMS = [("int4", 64), ("int4", 16), ("nvfp4", 16)]
+FORMS = [("int4", 64), ("int4", 16), ("nvfp4", 16), ("nvfp4_row", 16), ("fp8_row", 0)]
 
 
 @pytest.mark.parametrize("fmt,G", FORMS)

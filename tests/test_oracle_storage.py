@@ -99,3 +99,27 @@ def test_storage_equals_real_array_bytes(fmt, Gs):
         p = oracle.pack(x, kind, fmt, Gs)
         real = sum(a.nbytes for a in (p.codes, p.meta0, p.meta1, p.global_scale) if a is not None)
         assert real == oracle.storage_bytes(fmt, kind, Gs, 100, 3, 40)
+
+
+def test_row_format_bytes():
+    # NVFP4 with one FP32 scale per (token, head) row: 64 + 8 + 4 = 76 B at D = 128, per row
+    parts = G["nvfp4_row_code_bytes_d128"] + G["nvfp4_row_block_scale_bytes_d128"] + G["nvfp4_row_scale_bytes"]
+    assert parts == G["nvfp4_row_bytes_d128"]
+    for kind in ("key", "value"):
+        assert oracle.storage_bytes("nvfp4_row", kind, 16, 1, 1, 128) == G["nvfp4_row_bytes_d128"]
+        assert oracle.storage_bytes("nvfp4_row", kind, 16, 2, 1, 128) == G["nvfp4_kv_pair_bytes_d128"]
+        # the per-row format scales linearly: no per-tensor term
+        assert oracle.storage_bytes("nvfp4_row", kind, 16, 4096, 8, 128) == 4096 * 8 * 76
+    # FP8 E4M3 with one FP32 scale per row: codes are half of bf16, plus a 4 B sidecar (~3%)
+    b = oracle.storage_bytes("fp8_row", "value", 0, 1, 1, 128)
+    assert b - G["fp8_row_scale_bytes"] == G["fp8_row_code_fraction_of_bf16"] * G["bf16_row_bytes_d128"]
+    assert round(100 * G["fp8_row_scale_bytes"] / 128) == G["fp8_row_scale_percent_d128"]
+    assert oracle.storage_bytes("fp8_row", "key", 0, 10, 4, 96, sparse=True) == 10 * 4 * (96 + 4) + 40
+    # array bytes equal the formula
+    from workloads import normal_kv
+    import numpy as np
+    x = normal_kv(np.random.default_rng(0), 9, 3, 40)
+    for fmt, g in (("nvfp4_row", 16), ("fp8_row", 0)):
+        p = oracle.pack(x, "value", fmt, g)
+        nb = p.codes.nbytes + p.meta0.nbytes + (p.meta1.nbytes if p.meta1 is not None else 0)
+        assert nb == oracle.storage_bytes(fmt, "value", g, 9, 3, 40)
