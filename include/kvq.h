@@ -3,7 +3,10 @@
  *
  * The library packs and unpacks one request/layer's logical [token, KV head, channel] K or V
  * tensor, and encodes/decodes cross-loop residuals against a reconstructed predecessor, in two
- * 4-bit formats. All compute runs in HIP kernels on the caller's stream.
+ * 4-bit per-tensor formats and two row formats (one FP32 scale per token and head). Paged
+ * views [pages, page_size, H, D] are packed and unpacked directly, and row formats can be
+ * written into, and read from, cache slots named by a device index array. All compute runs in
+ * HIP kernels on the caller's stream.
  *
  * Sources (by page title and section):
  *   [PR166] vllm-rlt pull request #166, "INT4 KV packing/unpacking and cross-loop residual
@@ -11,9 +14,11 @@
  *           first codec review (FP32 codes before FP16 metadata; 4.5 bits per element), the
  *           interface review (payload-only storage accounting; no device sync in validation).
  *   [PR408] FreeToken pull request #408, "feat(kvcache): add nvfp4 kv quantization":
- *           "Summary" (76 B per D=128 row; graph-safe writes with device-resident ids) and the
- *           nvfp4 codec-port commit (low-nibble-first packing; quantize against the stored,
- *           rounded block scale).
+ *           "Summary" (76 B per D=128 row; graph-safe writes with device-resident ids), the fp8
+ *           commit (E4M3 codes with one FP32 scale per token and KV head; one fused
+ *           quantize-and-scatter launch whose slot ids are a device tensor) and the nvfp4
+ *           codec-port commit (low-nibble-first packing; quantize against the stored, rounded
+ *           block scale; one FP32 row scale).
  *
  * Conventions shared by every entry point:
  *   - Tensors are bf16, logical [T, H, D] (token, KV head, channel), with channel stride 1 and
@@ -46,8 +51,9 @@ typedef enum kvq_status {
     KVQ_ERR_NULL = 1,      /* a required pointer is NULL */
     KVQ_ERR_SHAPE = 2,     /* negative or too large size, or shapes that disagree */
     KVQ_ERR_LAYOUT = 3,    /* negative stride, or out/prev partially overlapping */
-    KVQ_ERR_FORMAT = 4,    /* unknown format or kind */
-    KVQ_ERR_GROUP = 5,     /* group size invalid for the format (NVFP4 requires 16) */
+    KVQ_ERR_FORMAT = 4,    /* unknown format or kind, or a format the call does not take */
+    KVQ_ERR_GROUP = 5,     /* group size invalid for the format (NVFP4 and NVFP4-row require
+                              16, FP8-row 0) or for the page size */
     KVQ_ERR_DTYPE = 6,     /* tensor dtype other than bf16 */
     KVQ_ERR_MISMATCH = 7,  /* packed descriptor disagrees with the tensors it is used with */
     KVQ_ERR_HIP = 8,       /* a kernel launch failed */
@@ -60,8 +66,16 @@ typedef enum kvq_kind { KVQ_KEY = 0, KVQ_VALUE = 1 } kvq_kind;
 
 /* KVQ_INT4: affine groups, FP32 math, FP16 minimum and scale, default group size 64.
  * KVQ_NVFP4: E2M1 codes (nearest-even), one E4M3 scale per 16 values, one FP32 global
- * multiplier per encoded tensor; group size 16 only. ([PR166] "Purpose", second bullet.) */
-typedef enum kvq_format { KVQ_INT4 = 0, KVQ_NVFP4 = 1 } kvq_format;
+ * multiplier per encoded tensor; group size 16 only. ([PR166] "Purpose", second bullet.)
+ * KVQ_NVFP4_ROW: as NVFP4, but the FP32 multiplier belongs to each (token, head) row
+ * (g_row = 2688 / row amax) and the 16-value blocks run along channels for K and V alike, so
+ * every row is encoded exactly like a one-row NVFP4 tensor: 76 B per D=128 row ([PR408]
+ * "Summary", codec-port commit). Group size 16 only.
+ * KVQ_FP8_ROW: one E4M3 code per element and one FP32 scale per (token, head) row,
+ * scale = row amax / 448, code = e4m3(min(|x / scale|, 448)) with the sign of x, decoded as
+ * code * scale ([PR408] fp8 commit). Group size 0 only (no sub-row groups).
+ * The kind does not change the layout of the two row formats. */
+typedef enum kvq_format { KVQ_INT4 = 0, KVQ_NVFP4 = 1, KVQ_NVFP4_ROW = 2, KVQ_FP8_ROW = 3 } kvq_format;
 
 typedef enum kvq_dtype { KVQ_BF16 = 0 } kvq_dtype;
 
@@ -74,15 +88,31 @@ typedef struct kvq_tensor {
     int64_t stride_t, stride_h;
 } kvq_tensor;
 
+/* A paged bf16 view [pages, page_size, H, D] ([PR166] interface review, item 3): element
+ * (p, s, h, d) is at data + p*stride_page + s*stride_slot + h*stride_h + d (elements). Its
+ * logical token order is page-major: token p*page_size + s. When stride_page is not
+ * page_size*stride_slot (pages padded, or K and V interleaved per page) page_size must be a
+ * power of two. */
+typedef struct kvq_paged {
+    void* data;
+    int32_t dtype; /* kvq_dtype */
+    int32_t reserved;
+    int64_t pages, page_size, H, D;
+    int64_t stride_page, stride_slot, stride_h;
+} kvq_paged;
+
 /* One encoded tensor ([PR166] "Purpose", first bullet: packed objects carry format, axis and
  * group size). The caller owns every plane; the library fills the scalar fields on encode.
  *   codes        [rows, H, ceil(D/2)] u8: channel 2j in the low nibble, 2j+1 in the high
  *                nibble ([PR408] codec-port commit: low first); an odd D leaves the last
- *                high nibble 0.
- *   meta0        INT4: f16 group minimums; NVFP4: E4M3 block scales (u8).
- *   meta1        INT4: f16 group scales;   NVFP4: unused (NULL).
- *                Metadata shape: KEY [ceil(rows/G), H, D], VALUE [rows, H, ceil(D/G)].
- *   global_scale NVFP4: one float, the encoding multiplier g (decode scale = block/g).
+ *                high nibble 0. FP8-row: [rows, H, D], one E4M3 byte per element.
+ *   meta0        INT4: f16 group minimums; NVFP4: E4M3 block scales (u8), shape KEY
+ *                [ceil(rows/G), H, D], VALUE [rows, H, ceil(D/G)]; NVFP4-row: E4M3 block
+ *                scales [rows, H, ceil(D/16)] (u8); FP8-row: FP32 row scales [rows, H].
+ *   meta1        INT4: f16 group scales (shape as meta0); NVFP4-row: FP32 row multipliers
+ *                g_row [rows, H]; NVFP4 and FP8-row: unused (NULL).
+ *   global_scale NVFP4: one float, the encoding multiplier g (decode scale = block/g); the
+ *                other formats: unused (NULL).
  *   positions    sparse residual: the owned int32 copy of the position map, [rows]. A non-NULL
  *                pointer is what marks a residual sparse; with rows == 0 it is not read.
  *   rows         T for a dense tensor, M for a sparse residual; full_T is the row count of the
@@ -112,9 +142,10 @@ const char* kvq_version(void);
 const char* kvq_status_string(kvq_status status);
 
 /* Exact payload bytes of one encoded tensor ([PR166] interface review: payload only, no
- * allocator slack, no decode scratch): rows*H*ceil(D/2) code bytes + 4 B per INT4 group or
- * 1 B per NVFP4 block + 4 B global scale (NVFP4) + 4 B per row of an owned position map
- * (sparse != 0). group_size 0 selects the format default. Host-only; writes *bytes.
+ * allocator slack, no decode scratch): rows*H*ceil(D/2) code bytes (rows*H*D for FP8-row)
+ * + 4 B per INT4 group, or 1 B per NVFP4 / NVFP4-row block, + 4 B global scale (NVFP4) or 4 B
+ * per (row, head) (NVFP4-row, FP8-row) + 4 B per row of an owned position map (sparse != 0).
+ * group_size 0 selects the format default. Host-only; writes *bytes.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_FORMAT, KVQ_ERR_GROUP. */
 kvq_status kvq_storage_bytes(kvq_format format, kvq_kind kind, int32_t group_size, int64_t rows, int64_t H,
                              int64_t D, int32_t sparse, uint64_t* bytes);
@@ -165,6 +196,40 @@ kvq_status kvq_encode_residual(const kvq_tensor* cur, const kvq_tensor* prev, co
  * HIP. */
 kvq_status kvq_decode_residual(const kvq_packed* r, const kvq_tensor* prev, const kvq_tensor* out,
                                hipStream_t stream);
+
+/* pack_paged ([PR166] interface review, item 3, and the stacked-PR follow-up): encode the
+ * paged view x in its page-major token order into *out (rows = pages*page_size, as kvq_pack
+ * would for that token sequence). page_local != 0 keeps every KEY group of INT4 and NVFP4
+ * inside one page ([PR166] first review, "Group ownership vs 16-token pages"): INT4 then uses
+ * groups of min(G, page_size) tokens, which needs G and page_size to divide one another, and
+ * records that size in out->group_size; NVFP4 needs page_size % 16 == 0. VALUE groups and the
+ * row formats are page-local already. The NVFP4 multiplier is one per call (all pages).
+ * Workspace and errors as kvq_pack; KVQ_ERR_GROUP for sizes page-local grouping cannot take,
+ * KVQ_ERR_LAYOUT for a padded page stride with a non-power-of-two page size. */
+kvq_status kvq_pack_paged(const kvq_paged* x, kvq_kind kind, kvq_format format, int32_t group_size,
+                          int32_t page_local, kvq_packed* out, void* workspace, hipStream_t stream);
+
+/* unpack_paged: decode *p (rows = pages*page_size) into the paged bf16 view `out`.
+ * Errors as kvq_unpack. */
+kvq_status kvq_unpack_paged(const kvq_packed* p, const kvq_paged* out, hipStream_t stream);
+
+/* Quantize-and-scatter into cache slots ([PR408] fp8 commit: one launch, slot ids in device
+ * memory, so it can sit inside a captured graph). Row i of `rows` ([N, H, D], N = rows->T) is
+ * encoded exactly as kvq_pack would encode it among those N rows, and its codes and row
+ * metadata are written into packed row slots[i] of `cache` (a packed tensor of cache->rows
+ * slots whose format, kind and group size are taken from the descriptor). Every other slot is
+ * left untouched. Only formats whose rows are encoded on their own qualify: INT4 VALUE,
+ * NVFP4-row and FP8-row (KVQ_ERR_FORMAT otherwise). `slots`: device int32 [N], distinct and in
+ * [0, cache->rows) (precondition, not checked; kvq_validate_positions can check it with
+ * T = cache->rows). Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, DTYPE, MISMATCH, HIP. */
+kvq_status kvq_store_rows(const kvq_tensor* rows, const int32_t* slots, kvq_packed* cache, hipStream_t stream);
+
+/* Gather-and-decode: output row i ([N, H, D] view `out`, N = out->T) is the decoded packed row
+ * slots[i] of `cache`, for every format (a KEY row of INT4 or NVFP4 decodes with the metadata
+ * of its token group, slots[i] / G). `slots`: device int32 [N] in [0, cache->rows)
+ * (precondition, not checked). Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, DTYPE, MISMATCH,
+ * HIP. */
+kvq_status kvq_load_rows(const kvq_packed* cache, const int32_t* slots, const kvq_tensor* out, hipStream_t stream);
 
 /* Opt-in device-side check of a position map (the codec page's interface review asks that
  * validation never force a host sync). Writes *status (device int32): 0 = valid, bit 0 = some

@@ -12,6 +12,10 @@ Usage (the four-call form of the codec page's usage example)::
     previous = kvq.unpack(packed)
     residual = kvq.encode_residual(current, previous, kind="key", format="nvfp4")
     rebuilt = kvq.decode_residual(residual, previous)
+
+Paged caches: ``pack_paged`` / ``unpack_paged`` take [pages, page_size, H, D] views;
+``store_rows`` quantizes new rows straight into cache slots named by a device int32 tensor
+(row formats and INT4 VALUE) and ``load_rows`` decodes rows by slot.
 """
 
 from __future__ import annotations
@@ -29,14 +33,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 
 KIND = {"key": 0, "value": 1}
-FORMAT = {"int4": 0, "nvfp4": 1}
+FORMAT = {"int4": 0, "nvfp4": 1, "nvfp4_row": 2, "fp8_row": 3}
 KIND_NAME = {v: k for k, v in KIND.items()}
 FORMAT_NAME = {v: k for k, v in FORMAT.items()}
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_SHAPE", 3: "KVQ_ERR_LAYOUT", 4: "KVQ_ERR_FORMAT",
           5: "KVQ_ERR_GROUP", 6: "KVQ_ERR_DTYPE", 7: "KVQ_ERR_MISMATCH", 8: "KVQ_ERR_HIP", 9: "KVQ_ERR_WORKSPACE"}
 PLANES = ("codes", "meta0", "meta1", "global_scale", "positions")
 EXPORTS = ("kvq_version", "kvq_status_string", "kvq_storage_bytes", "kvq_plane_bytes", "kvq_workspace_bytes",
-           "kvq_pack", "kvq_unpack", "kvq_encode_residual", "kvq_decode_residual", "kvq_validate_positions")
+           "kvq_pack", "kvq_unpack", "kvq_encode_residual", "kvq_decode_residual", "kvq_validate_positions",
+           "kvq_pack_paged", "kvq_unpack_paged", "kvq_store_rows", "kvq_load_rows")
 
 
 class KvqError(RuntimeError):
@@ -49,6 +54,13 @@ class KvqTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class KvqPaged(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("pages", ctypes.c_int64), ("page_size", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("stride_page", ctypes.c_int64), ("stride_slot", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
 
 
 class KvqPacked(ctypes.Structure):
@@ -91,6 +103,15 @@ def library() -> ctypes.CDLL:
         lib.kvq_decode_residual.restype = ctypes.c_int
         lib.kvq_validate_positions.argtypes = [P, I64, I64, P, P, P]
         lib.kvq_validate_positions.restype = ctypes.c_int
+        GP = ctypes.POINTER(KvqPaged)
+        lib.kvq_pack_paged.argtypes = [GP, ctypes.c_int, ctypes.c_int, I32, I32, PP, P, P]
+        lib.kvq_pack_paged.restype = ctypes.c_int
+        lib.kvq_unpack_paged.argtypes = [PP, GP, P]
+        lib.kvq_unpack_paged.restype = ctypes.c_int
+        lib.kvq_store_rows.argtypes = [TP, P, PP, P]
+        lib.kvq_store_rows.restype = ctypes.c_int
+        lib.kvq_load_rows.argtypes = [PP, P, TP, P]
+        lib.kvq_load_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -105,7 +126,7 @@ def version() -> str:
 
 
 def default_group(fmt: str) -> int:
-    return 64 if fmt == "int4" else 16
+    return {"int4": 64, "nvfp4": 16, "nvfp4_row": 16, "fp8_row": 0}[fmt]
 
 
 def plane_bytes(fmt: str, kind: str, group_size: int, rows: int, H: int, D: int, sparse: bool = False) -> Dict[str, int]:
@@ -122,7 +143,11 @@ def storage_bytes(fmt: str, kind: str, group_size: int, rows: int, H: int, D: in
     return int(out.value)
 
 
-def meta_shape(kind: str, G: int, rows: int, H: int, D: int) -> Tuple[int, int, int]:
+def meta_shape(kind: str, G: int, rows: int, H: int, D: int, fmt: str = "int4") -> Tuple[int, ...]:
+    if fmt == "nvfp4_row":
+        return (rows, H, -(-D // 16))
+    if fmt == "fp8_row":
+        return (rows, H)
     return (-(-rows // G), H, D) if kind == "key" else (rows, H, -(-D // G))
 
 
@@ -137,9 +162,9 @@ class Packed:
     H: int
     D: int
     full_T: int
-    codes: torch.Tensor  # uint8 [rows, H, ceil(D/2)]
-    meta0: torch.Tensor  # int4: f16 minimums (int16 view); nvfp4: E4M3 bytes (uint8)
-    meta1: Optional[torch.Tensor]  # int4: f16 scales (int16 view)
+    codes: torch.Tensor  # uint8 [rows, H, ceil(D/2)] ([rows, H, D] for fp8_row)
+    meta0: torch.Tensor  # int4: f16 minimums (int16 view); nvfp4(_row): E4M3 bytes; fp8_row: float32 [rows, H]
+    meta1: Optional[torch.Tensor]  # int4: f16 scales (int16 view); nvfp4_row: float32 row multipliers [rows, H]
     global_scale: Optional[torch.Tensor]  # nvfp4: float32 [1]
     positions: Optional[torch.Tensor] = None  # sparse residual: owned int32 [rows]
     # storage behind `positions`, at least one element so that a sparse residual with no rows
@@ -211,16 +236,20 @@ def alloc_packed(fmt: str, kind: str, group_size: int, rows: int, H: int, D: int
                  dev: torch.device, sparse: bool = False) -> Packed:
     G = group_size or default_group(fmt)
     sizes = plane_bytes(fmt, kind, G, rows, H, D, sparse)
-    ms = meta_shape(kind, G, rows, H, D)
-    codes = torch.empty((rows, H, -(-D // 2)), dtype=torch.uint8, device=dev)
+    ms = meta_shape(kind, G, rows, H, D, fmt)
+    codes = torch.empty((rows, H, D if fmt == "fp8_row" else -(-D // 2)), dtype=torch.uint8, device=dev)
+    meta1, gs = None, None
     if fmt == "int4":
         meta0 = torch.empty(ms, dtype=torch.int16, device=dev)
         meta1 = torch.empty(ms, dtype=torch.int16, device=dev)
-        gs = None
-    else:
+    elif fmt == "nvfp4":
         meta0 = torch.empty(ms, dtype=torch.uint8, device=dev)
-        meta1 = None
         gs = torch.empty(1, dtype=torch.float32, device=dev)
+    elif fmt == "nvfp4_row":
+        meta0 = torch.empty(ms, dtype=torch.uint8, device=dev)
+        meta1 = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    else:
+        meta0 = torch.empty(ms, dtype=torch.float32, device=dev)
     pos_buf = torch.empty(max(rows, 1), dtype=torch.int32, device=dev) if sparse else None
     pos = pos_buf[:rows] if sparse else None
     p = Packed(fmt, kind, G, rows, H, D, full_T, codes, meta0, meta1, gs, pos, pos_buf)
@@ -293,6 +322,93 @@ def decode_residual(r: Packed, previous: torch.Tensor, out: Optional[torch.Tenso
     return out
 
 
+def _paged_view(x: torch.Tensor) -> KvqPaged:
+    if x.dtype != torch.bfloat16:
+        raise TypeError("kvq: tensors must be bfloat16")
+    if x.dim() != 4:
+        raise ValueError("kvq: paged tensors must be [pages, page_size, H, D]")
+    P, S, H, D = x.shape
+    if D > 1 and x.stride(3) != 1 and x.numel() > 0:
+        raise ValueError("kvq: channel stride must be 1")
+    return KvqPaged(ctypes.c_void_p(x.data_ptr()), 0, 0, P, S, H, D, x.stride(0), x.stride(1), x.stride(2))
+
+
+def page_local_group(fmt: str, kind: str, group_size: int, page_size: int) -> int:
+    """Group size a page-local packing records: INT4 KEY groups shrink to the page."""
+    G = group_size or default_group(fmt)
+    if fmt == "int4" and kind == "key" and 0 < page_size < G:
+        return page_size
+    return G
+
+
+def pack_paged(x: torch.Tensor, kind: str = "key", format: str = "int4", group_size: int = 0,
+               page_local: bool = False, out: Optional[Packed] = None) -> Packed:
+    """pack_paged: encode a bf16 [pages, page_size, H, D] view in page-major token order.
+    ``page_local`` keeps KEY groups inside pages."""
+    dev = _device_of(x)
+    P, S, H, D = x.shape
+    G = group_size or default_group(format)
+    Ge = page_local_group(format, kind, G, S) if page_local else G
+    if out is None:
+        out = alloc_packed(format, kind, Ge, P * S, H, D, P * S, dev)
+    desc = out.descriptor()
+    ws = workspace(dev) if format == "nvfp4" else None
+    _check("kvq_pack_paged", library().kvq_pack_paged(ctypes.byref(_paged_view(x)), KIND[kind], FORMAT[format], G,
+                                                      int(bool(page_local)), ctypes.byref(desc), _ptr(ws),
+                                                      _stream(dev)))
+    out.group_size = desc.group_size
+    return out
+
+
+def unpack_paged(p: Packed, out: Optional[torch.Tensor] = None, page_size: Optional[int] = None) -> torch.Tensor:
+    """unpack_paged: decode into a bf16 [pages, page_size, H, D] view (allocated when `out` is
+    None, from `page_size`)."""
+    dev = p.codes.device
+    if out is None:
+        if not page_size or p.rows % page_size:
+            raise ValueError("kvq: give `out` or a page_size dividing the row count")
+        out = torch.empty((p.rows // page_size, page_size, p.H, p.D), dtype=torch.bfloat16, device=dev)
+    desc = p.descriptor()
+    _check("kvq_unpack_paged", library().kvq_unpack_paged(ctypes.byref(desc), ctypes.byref(_paged_view(out)),
+                                                          _stream(dev)))
+    return out
+
+
+def alloc_cache(fmt: str, kind: str, group_size: int, n_slots: int, H: int, D: int, dev: torch.device) -> Packed:
+    """Planes of a slot cache of n_slots rows (contents undefined until written)."""
+    return alloc_packed(fmt, kind, group_size, n_slots, H, D, n_slots, dev)
+
+
+def _slots(slots: torch.Tensor, like: torch.Tensor, n: int) -> torch.Tensor:
+    if slots.dtype != torch.int32 or slots.device != like.device or slots.dim() != 1 or slots.numel() != n:
+        raise ValueError("kvq: slots must be a 1-D int32 tensor with one entry per row, on the cache's device")
+    return slots.contiguous()
+
+
+def store_rows(cache: Packed, rows: torch.Tensor, slots: torch.Tensor) -> Packed:
+    """Quantize rows [N, H, D] and write row i into cache slot slots[i] (one launch; slots are a
+    device int32 tensor, distinct and in range)."""
+    dev = _device_of(rows)
+    slots = _slots(slots, cache.codes, rows.shape[0])
+    desc = cache.descriptor()
+    _check("kvq_store_rows", library().kvq_store_rows(ctypes.byref(_view(rows)), _ptr(slots), ctypes.byref(desc),
+                                                      _stream(dev)))
+    return cache
+
+
+def load_rows(cache: Packed, slots: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode cache rows slots[0..N) into a bf16 [N, H, D] tensor (or the view `out`)."""
+    dev = cache.codes.device
+    N = slots.numel()
+    slots = _slots(slots, cache.codes, N)
+    if out is None:
+        out = torch.empty((N, cache.H, cache.D), dtype=torch.bfloat16, device=dev)
+    desc = cache.descriptor()
+    _check("kvq_load_rows", library().kvq_load_rows(ctypes.byref(desc), _ptr(slots), ctypes.byref(_view(out)),
+                                                    _stream(dev)))
+    return out
+
+
 def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
     """Device-side check of a position map; returns a device int32 status (0 = valid, bit 0 =
     out of range, bit 1 = repeated) without synchronizing."""
@@ -305,4 +421,5 @@ def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
 
 
 __all__ = ["pack", "unpack", "encode_residual", "decode_residual", "storage_bytes", "plane_bytes",
-           "validate_positions", "Packed", "KvqError", "library", "version", "workspace", "alloc_packed"]
+           "validate_positions", "pack_paged", "unpack_paged", "store_rows", "load_rows", "alloc_cache",
+           "Packed", "KvqError", "library", "version", "workspace", "alloc_packed"]

@@ -40,20 +40,24 @@ FastDiv fastdiv_make(uint32_t d) {
     return f;
 }
 
+bool row_format(int format) { return format == KVQ_NVFP4_ROW || format == KVQ_FP8_ROW; }
+
 kvq_status check_kind_format(int kind, int format) {
     if (kind != KVQ_KEY && kind != KVQ_VALUE) return KVQ_ERR_FORMAT;
-    if (format != KVQ_INT4 && format != KVQ_NVFP4) return KVQ_ERR_FORMAT;
+    if (format != KVQ_INT4 && format != KVQ_NVFP4 && !row_format(format)) return KVQ_ERR_FORMAT;
     return KVQ_OK;
 }
 
+// group_size 0 selects the default: INT4 64, NVFP4 and NVFP4-row 16, FP8-row 0 (its only value).
 int32_t resolve_group(int format, int32_t G) {
-    if (G == 0) return format == KVQ_INT4 ? 64 : 16;
+    if (G == 0) return format == KVQ_INT4 ? 64 : (format == KVQ_FP8_ROW ? 0 : 16);
     return G;
 }
 
 kvq_status check_group(int format, int32_t G) {
+    if (format == KVQ_FP8_ROW) return G == 0 ? KVQ_OK : KVQ_ERR_GROUP;
     if (G < 1) return KVQ_ERR_GROUP;
-    if (format == KVQ_NVFP4 && G != 16) return KVQ_ERR_GROUP;
+    if ((format == KVQ_NVFP4 || format == KVQ_NVFP4_ROW) && G != 16) return KVQ_ERR_GROUP;
     return KVQ_OK;
 }
 
@@ -64,11 +68,21 @@ kvq_status plane_sizes(int format, int kind, int32_t G, int64_t rows, int64_t H,
     G = resolve_group(format, G);
     if ((st = check_group(format, G))) return st;
     if (!dims_ok(rows, H, D)) return KVQ_ERR_SHAPE;
-    const uint64_t ng = (kind == KVQ_KEY) ? (uint64_t)cdiv(rows, G) * H * D : (uint64_t)rows * H * cdiv(D, G);
-    s[KVQ_PLANE_CODES] = (uint64_t)rows * H * cdiv(D, 2);
-    s[KVQ_PLANE_META0] = (format == KVQ_INT4) ? 2 * ng : ng;
-    s[KVQ_PLANE_META1] = (format == KVQ_INT4) ? 2 * ng : 0;
-    s[KVQ_PLANE_GLOBAL] = (format == KVQ_NVFP4) ? 4 : 0;
+    const uint64_t rh = (uint64_t)rows * H;
+    s[KVQ_PLANE_CODES] = (format == KVQ_FP8_ROW) ? rh * D : rh * cdiv(D, 2);
+    s[KVQ_PLANE_META1] = 0;
+    s[KVQ_PLANE_GLOBAL] = 0;
+    if (format == KVQ_NVFP4_ROW) {
+        s[KVQ_PLANE_META0] = rh * cdiv(D, 16);
+        s[KVQ_PLANE_META1] = 4 * rh;
+    } else if (format == KVQ_FP8_ROW) {
+        s[KVQ_PLANE_META0] = 4 * rh;
+    } else {
+        const uint64_t ng = (kind == KVQ_KEY) ? (uint64_t)cdiv(rows, G) * H * D : rh * cdiv(D, G);
+        s[KVQ_PLANE_META0] = (format == KVQ_INT4) ? 2 * ng : ng;
+        s[KVQ_PLANE_META1] = (format == KVQ_INT4) ? 2 * ng : 0;
+        s[KVQ_PLANE_GLOBAL] = (format == KVQ_NVFP4) ? 4 : 0;
+    }
     s[KVQ_PLANE_POSITIONS] = sparse ? 4 * (uint64_t)rows : 0;
     return KVQ_OK;
 }
@@ -97,6 +111,44 @@ bool view_vec_ok(const void* data, int64_t st, int64_t sh) {
     return aligned(data, 16) && (st % 8) == 0 && (sh % 8) == 0;
 }
 
+// A bf16 [T, H, D] view as the kernels address it: row t at
+// row_offset(t, pshift, pst, st) (pages of 2^pshift rows pst apart, or unpaged).
+struct View {
+    void* data;
+    int64_t T, H, D;
+    int64_t st, sh;
+    int32_t pshift;
+    int64_t pst;
+};
+
+View view_of(const kvq_tensor* x) { return View{x->data, x->T, x->H, x->D, x->stride_t, x->stride_h, kNoPaging, 0}; }
+
+bool view_vec_ok(const View& v) {
+    return view_vec_ok(v.data, v.st, v.sh) && (v.pshift == kNoPaging || v.pst % 8 == 0);
+}
+
+// Checks a paged view and turns it into a View in page-major token order.
+kvq_status view_of_paged(const kvq_paged* x, View* v) {
+    if (!x) return KVQ_ERR_NULL;
+    if (x->dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (x->pages < 0 || x->page_size < 0 || x->pages >= kMaxDim || x->page_size >= kMaxDim) return KVQ_ERR_SHAPE;
+    const int64_t T = x->pages * x->page_size;
+    if (!dims_ok(T, x->H, x->D)) return KVQ_ERR_SHAPE;
+    if (x->stride_page < 0 || x->stride_slot < 0 || x->stride_h < 0) return KVQ_ERR_LAYOUT;
+    if (T * x->H * x->D > 0 && !x->data) return KVQ_ERR_NULL;
+    *v = View{x->data, T, x->H, x->D, x->stride_slot, x->stride_h, kNoPaging, 0};
+    if (x->pages > 1 && x->stride_page != x->page_size * x->stride_slot) {
+        if (!is_pow2(x->page_size)) return KVQ_ERR_LAYOUT;
+        v->pshift = log2i(x->page_size);
+        v->pst = x->stride_page;
+    }
+    return KVQ_OK;
+}
+
+// Vector path of the row formats: head_dim a power of two from 8 to 512 (a (token, head) row
+// spans D/8 lanes of one wave).
+bool row_vec_dims(int64_t D) { return D % 8 == 0 && is_pow2(D / 8) && D / 8 <= 64; }
+
 // Geometry of the 8-channel vector path.
 template <typename Args>
 void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, int rows_per_task) {
@@ -113,22 +165,84 @@ void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, i
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-kvq_status encode_common(const kvq_tensor* cur, const kvq_tensor* prev, const int32_t* positions, int64_t M,
-                         int kind, int format, int32_t G, kvq_packed* out, void* workspace, hipStream_t stream) {
+// Fill the encoder arguments for `rows` encoded rows of `cur` (optionally minus prev, gathered
+// by positions, written to packed rows dst[r]) into the planes of `planes`, and launch.
+kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* positions, int64_t rows, int kind,
+                      int format, int32_t G, const kvq_packed* planes, void* workspace, const int32_t* dst,
+                      hipStream_t stream) {
+    const int64_t H = cur.H, D = cur.D;
+    const bool sparse = positions != nullptr;
+    EncArgs a;
+    memset(&a, 0, sizeof a);
+    a.cur = static_cast<const uint16_t*>(cur.data);
+    a.cst = cur.st;
+    a.csh = cur.sh;
+    a.cpshift = cur.pshift;
+    a.cpst = cur.pst;
+    if (prev) {
+        a.prev = static_cast<const uint16_t*>(prev->data);
+        a.pst = prev->stride_t;
+        a.psh = prev->stride_h;
+    }
+    a.pos = positions;
+    a.pos_out = sparse ? planes->positions : nullptr;
+    a.dst = dst;
+    a.rows = rows;
+    a.H = (int32_t)H;
+    a.D = (int32_t)D;
+    a.G = G;
+    a.codes = planes->codes;
+    a.meta0 = planes->meta0;
+    a.meta1 = planes->meta1;
+    a.gscale = planes->global_scale;
+    a.ws = static_cast<uint32_t*>(workspace);
+
+    // vector path eligibility
+    bool vec = (D % 8 == 0) && view_vec_ok(cur) && aligned(planes->codes, 4) &&
+               (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
+    if (prev) vec = vec && view_vec_ok(prev->data, prev->stride_t, prev->stride_h);
+    if (row_format(format)) {
+        vec = vec && row_vec_dims(D) &&
+              (format == KVQ_FP8_ROW ? aligned(planes->codes, 8) && aligned(planes->meta0, 4) : aligned(planes->meta1, 4));
+    } else if (kind == KVQ_VALUE) {
+        vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8) && (G / 8) <= 16;
+    } else if (format == KVQ_INT4) {
+        vec = vec && (G == 16 || G == 32 || G == 64 || G == 128) && aligned(planes->meta0, 16) &&
+              aligned(planes->meta1, 16);
+    } else {
+        vec = vec && aligned(planes->meta0, 8);
+    }
+    if (vec) {
+        if (row_format(format) || kind == KVQ_VALUE) {
+            fill_vec_geometry(a, rows, H, D, row_format(format) ? 8 : G, KVQ_ENCODE_ROWS_V);
+        } else {
+            fill_vec_geometry(a, rows, H, D, G, G);
+        }
+        a.div_C8 = fastdiv_make((uint32_t)a.C8);
+    }
+
+    hipError_t e = hipSuccess;
+    if (row_format(format)) return hip_status(launch_row_encode(format, a, prev != nullptr, sparse, vec, stream));
+    if (format == KVQ_NVFP4) e = launch_amax(a, prev != nullptr, sparse, vec, stream);
+    if (e == hipSuccess) e = launch_encode(format, kind, a, prev != nullptr, sparse, vec, stream);
+    return hip_status(e);
+}
+
+kvq_status encode_common(const View& cur, const kvq_tensor* prev, const int32_t* positions, int64_t M, int kind,
+                         int format, int32_t G, kvq_packed* out, void* workspace, hipStream_t stream) {
     kvq_status st = check_kind_format(kind, format);
     if (st) return st;
     G = resolve_group(format, G);
     if ((st = check_group(format, G))) return st;
-    if ((st = check_tensor(cur))) return st;
     if (prev) {
         if ((st = check_tensor(prev))) return st;
-        if (prev->T != cur->T || prev->H != cur->H || prev->D != cur->D) return KVQ_ERR_SHAPE;
+        if (prev->T != cur.T || prev->H != cur.H || prev->D != cur.D) return KVQ_ERR_SHAPE;
     }
     const bool sparse = positions != nullptr;
-    if (M < 0 || (sparse && M > cur->T)) return KVQ_ERR_SHAPE;
+    if (M < 0 || (sparse && M > cur.T)) return KVQ_ERR_SHAPE;
     if (!sparse && M != 0) return KVQ_ERR_SHAPE;
-    const int64_t rows = sparse ? M : cur->T;
-    const int64_t H = cur->H, D = cur->D;
+    const int64_t rows = sparse ? M : cur.T;
+    const int64_t H = cur.H, D = cur.D;
     if (!out) return KVQ_ERR_NULL;
     uint64_t sz[KVQ_NUM_PLANES];
     if ((st = plane_sizes(format, kind, G, rows, H, D, sparse ? 1 : 0, sz))) return st;
@@ -146,7 +260,7 @@ kvq_status encode_common(const kvq_tensor* cur, const kvq_tensor* prev, const in
     out->rows = rows;
     out->H = H;
     out->D = D;
-    out->full_T = cur->T;
+    out->full_T = cur.T;
     if (!sparse) out->positions = nullptr;
 
     const int64_t n = rows * H * D;
@@ -156,53 +270,7 @@ kvq_status encode_common(const kvq_tensor* cur, const kvq_tensor* prev, const in
         if (e == hipSuccess && sparse && M > 0) e = launch_copy_i32(out->positions, positions, M, stream);
         return hip_status(e);
     }
-
-    EncArgs a;
-    memset(&a, 0, sizeof a);
-    a.cur = static_cast<const uint16_t*>(cur->data);
-    a.cst = cur->stride_t;
-    a.csh = cur->stride_h;
-    if (prev) {
-        a.prev = static_cast<const uint16_t*>(prev->data);
-        a.pst = prev->stride_t;
-        a.psh = prev->stride_h;
-    }
-    a.pos = positions;
-    a.pos_out = sparse ? out->positions : nullptr;
-    a.rows = rows;
-    a.H = (int32_t)H;
-    a.D = (int32_t)D;
-    a.G = G;
-    a.codes = out->codes;
-    a.meta0 = out->meta0;
-    a.meta1 = out->meta1;
-    a.gscale = out->global_scale;
-    a.ws = static_cast<uint32_t*>(workspace);
-
-    // vector path eligibility
-    bool vec = (D % 8 == 0) && view_vec_ok(cur->data, cur->stride_t, cur->stride_h) && aligned(out->codes, 4) &&
-               (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
-    if (prev) vec = vec && view_vec_ok(prev->data, prev->stride_t, prev->stride_h);
-    if (kind == KVQ_VALUE) {
-        vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8) && (G / 8) <= 16;
-    } else if (format == KVQ_INT4) {
-        vec = vec && (G == 16 || G == 32 || G == 64 || G == 128) && aligned(out->meta0, 16) && aligned(out->meta1, 16);
-    } else {
-        vec = vec && aligned(out->meta0, 8);
-    }
-    if (vec) {
-        if (kind == KVQ_VALUE) {
-            fill_vec_geometry(a, rows, H, D, G, KVQ_ENCODE_ROWS_V);
-        } else {
-            fill_vec_geometry(a, rows, H, D, G, G);
-        }
-        a.div_C8 = fastdiv_make((uint32_t)a.C8);
-    }
-
-    hipError_t e = hipSuccess;
-    if (format == KVQ_NVFP4) e = launch_amax(a, prev != nullptr, sparse, vec, stream);
-    if (e == hipSuccess) e = launch_encode(format, kind, a, prev != nullptr, sparse, vec, stream);
-    return hip_status(e);
+    return encode_run(cur, prev, positions, rows, kind, format, G, out, workspace, nullptr, stream);
 }
 
 kvq_status check_packed(const kvq_packed* p) {
@@ -221,10 +289,11 @@ kvq_status check_packed(const kvq_packed* p) {
     return KVQ_OK;
 }
 
-// Decode p's rows into `out` (optionally adding prev), scattering by `positions` if given.
-kvq_status decode_common(const kvq_packed* p, const kvq_tensor* prev, const kvq_tensor* out,
-                         const int32_t* positions, hipStream_t stream) {
-    const int64_t rows = p->rows, H = p->H, D = p->D;
+// Decode `rows` rows of p into `out` (optionally adding prev): output row r reads packed row
+// src ? src[r] : r and lands in row positions ? positions[r] : r.
+kvq_status decode_run(const kvq_packed* p, int64_t rows, const kvq_tensor* prev, const View& out,
+                      const int32_t* positions, const int32_t* src, hipStream_t stream) {
+    const int64_t H = p->H, D = p->D;
     if (rows * H * D == 0) return KVQ_OK;
     DecArgs a;
     memset(&a, 0, sizeof a);
@@ -233,26 +302,35 @@ kvq_status decode_common(const kvq_packed* p, const kvq_tensor* prev, const kvq_
     a.meta1 = p->meta1;
     a.gscale = p->global_scale;
     a.pos = positions;
+    a.src = src;
     if (prev) {
         a.prev = static_cast<const uint16_t*>(prev->data);
         a.pst = prev->stride_t;
         a.psh = prev->stride_h;
     }
-    a.out = static_cast<uint16_t*>(out->data);
-    a.ost = out->stride_t;
-    a.osh = out->stride_h;
+    a.out = static_cast<uint16_t*>(out.data);
+    a.ost = out.st;
+    a.osh = out.sh;
+    a.opshift = out.pshift;
+    a.opst = out.pst;
     a.rows = rows;
     a.H = (int32_t)H;
     a.D = (int32_t)D;
     a.G = p->group_size;
     const int32_t G = p->group_size;
-    bool vec = (D % 8 == 0) && view_vec_ok(out->data, out->stride_t, out->stride_h) && aligned(p->codes, 4) &&
+    bool vec = (D % 8 == 0) && view_vec_ok(out) && aligned(p->codes, 4) &&
                (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
     if (prev) vec = vec && view_vec_ok(prev->data, prev->stride_t, prev->stride_h);
+    if (row_format(p->format)) {
+        vec = vec && row_vec_dims(D) && (p->format != KVQ_FP8_ROW || aligned(p->codes, 8));
+        if (vec) fill_vec_geometry(a, rows, H, D, 8, KVQ_DECODE_ROWS);
+        return hip_status(launch_row_decode(p->format, a, prev != nullptr, positions != nullptr, vec, stream));
+    }
     if (p->kind == KVQ_VALUE) {
         vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8);
     } else {
-        vec = vec && (G % 8 == 0) && (G % KVQ_DECODE_ROWS == 0) &&
+        // a KEY task loads its token group's metadata once, so slot reads take the generic path
+        vec = vec && !src && (G % 8 == 0) && (G % KVQ_DECODE_ROWS == 0) &&
               (p->format == KVQ_INT4 ? (aligned(p->meta0, 16) && aligned(p->meta1, 16)) : aligned(p->meta0, 8));
     }
     if (vec) fill_vec_geometry(a, rows, H, D, G, KVQ_DECODE_ROWS);
@@ -301,7 +379,9 @@ size_t kvq_workspace_bytes(void) { return kWorkspaceBytes; }
 
 kvq_status kvq_pack(const kvq_tensor* x, kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out,
                     void* workspace, hipStream_t stream) {
-    return encode_common(x, nullptr, nullptr, 0, kind, format, group_size, out, workspace, stream);
+    kvq_status st = check_tensor(x);
+    if (st) return st;
+    return encode_common(view_of(x), nullptr, nullptr, 0, kind, format, group_size, out, workspace, stream);
 }
 
 kvq_status kvq_encode_residual(const kvq_tensor* cur, const kvq_tensor* prev, const int32_t* positions, int64_t M,
@@ -309,7 +389,9 @@ kvq_status kvq_encode_residual(const kvq_tensor* cur, const kvq_tensor* prev, co
                                void* workspace, hipStream_t stream) {
     if (!prev) return KVQ_ERR_NULL;
     if (!positions && M != 0) return KVQ_ERR_SHAPE;
-    return encode_common(cur, prev, positions, M, kind, format, group_size, out, workspace, stream);
+    kvq_status st = check_tensor(cur);
+    if (st) return st;
+    return encode_common(view_of(cur), prev, positions, M, kind, format, group_size, out, workspace, stream);
 }
 
 kvq_status kvq_unpack(const kvq_packed* p, const kvq_tensor* out, hipStream_t stream) {
@@ -317,7 +399,7 @@ kvq_status kvq_unpack(const kvq_packed* p, const kvq_tensor* out, hipStream_t st
     if (st) return st;
     if ((st = check_tensor(out))) return st;
     if (out->T != p->rows || out->H != p->H || out->D != p->D) return KVQ_ERR_MISMATCH;
-    return decode_common(p, nullptr, out, nullptr, stream);
+    return decode_run(p, p->rows, nullptr, view_of(out), nullptr, nullptr, stream);
 }
 
 kvq_status kvq_decode_residual(const kvq_packed* r, const kvq_tensor* prev, const kvq_tensor* out,
@@ -364,7 +446,64 @@ kvq_status kvq_decode_residual(const kvq_packed* r, const kvq_tensor* prev, cons
             if (e != hipSuccess) return KVQ_ERR_HIP;
         }
     }
-    return decode_common(r, prev, out, r->positions, stream);
+    return decode_run(r, r->rows, prev, view_of(out), r->positions, nullptr, stream);
+}
+
+kvq_status kvq_pack_paged(const kvq_paged* x, kvq_kind kind, kvq_format format, int32_t group_size,
+                          int32_t page_local, kvq_packed* out, void* workspace, hipStream_t stream) {
+    View v;
+    kvq_status st = view_of_paged(x, &v);
+    if (st) return st;
+    if ((st = check_kind_format(kind, format))) return st;
+    int32_t G = resolve_group(format, group_size);
+    if ((st = check_group(format, G))) return st;
+    if (page_local && kind == KVQ_KEY && x->page_size > 0) {
+        // keep every KEY group inside one page: groups of min(G, page_size) tokens that tile it
+        const int64_t S = x->page_size;
+        if (format == KVQ_INT4) {
+            if (G % S != 0 && S % G != 0) return KVQ_ERR_GROUP;
+            if (S < G) G = (int32_t)S;
+        } else if (format == KVQ_NVFP4) {
+            if (S % 16 != 0) return KVQ_ERR_GROUP;
+        }
+    }
+    return encode_common(v, nullptr, nullptr, 0, kind, format, G, out, workspace, stream);
+}
+
+kvq_status kvq_unpack_paged(const kvq_packed* p, const kvq_paged* out, hipStream_t stream) {
+    kvq_status st = check_packed(p);
+    if (st) return st;
+    View v;
+    if ((st = view_of_paged(out, &v))) return st;
+    if (v.T != p->rows || v.H != p->H || v.D != p->D) return KVQ_ERR_MISMATCH;
+    return decode_run(p, p->rows, nullptr, v, nullptr, nullptr, stream);
+}
+
+kvq_status kvq_store_rows(const kvq_tensor* rows, const int32_t* slots, kvq_packed* cache, hipStream_t stream) {
+    kvq_status st = check_tensor(rows);
+    if (st) return st;
+    if ((st = check_packed(cache))) return st;
+    if (!((cache->format == KVQ_INT4 && cache->kind == KVQ_VALUE) || row_format(cache->format))) return KVQ_ERR_FORMAT;
+    if (cache->positions) return KVQ_ERR_MISMATCH;  // a sparse residual is not a slot cache
+    if (rows->H != cache->H || rows->D != cache->D) return KVQ_ERR_MISMATCH;
+    const int64_t N = rows->T;
+    if (N > cache->rows) return KVQ_ERR_SHAPE;  // slots are distinct
+    if (N * rows->H * rows->D == 0) return KVQ_OK;
+    if (!slots) return KVQ_ERR_NULL;
+    return encode_run(view_of(rows), nullptr, nullptr, N, cache->kind, cache->format, cache->group_size, cache,
+                      nullptr, slots, stream);
+}
+
+kvq_status kvq_load_rows(const kvq_packed* cache, const int32_t* slots, const kvq_tensor* out, hipStream_t stream) {
+    kvq_status st = check_packed(cache);
+    if (st) return st;
+    if ((st = check_tensor(out))) return st;
+    if (out->H != cache->H || out->D != cache->D) return KVQ_ERR_MISMATCH;
+    const int64_t N = out->T;
+    if (N * out->H * out->D == 0) return KVQ_OK;
+    if (!slots) return KVQ_ERR_NULL;
+    if (cache->rows == 0) return KVQ_ERR_SHAPE;  // no slot to read
+    return decode_run(cache, N, nullptr, view_of(out), nullptr, slots, stream);
 }
 
 kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,

@@ -50,17 +50,19 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     const int64_t r0 = (int64_t)rtile * RW;
     const int nr = (int)min<int64_t>(RW, a.rows - r0);
 
-    // all loads first (tail rows re-read the last row; only stores are masked)
-    int64_t rr[RW], tt[RW];
+    // all loads first (tail rows re-read the last row; only stores are masked). Output row i
+    // reads packed row rs[i] (slot reads; KEY only without a source map) and writes row tt[i].
+    int64_t rs[RW], tt[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-        rr[i] = min<int64_t>(r0 + i, a.rows - 1);
-        tt[i] = SCATTER ? (int64_t)a.pos[rr[i]] : rr[i];
+        const int64_t rr = min<int64_t>(r0 + i, a.rows - 1);
+        rs[i] = a.src ? (int64_t)a.src[rr] : rr;
+        tt[i] = SCATTER ? (int64_t)a.pos[rr] : rr;
     }
     uint32_t cw[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i)
-        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.codes) + (size_t)rr[i] * (uint32_t)a.C8 + c8);
+        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.codes) + (size_t)rs[i] * (uint32_t)a.C8 + c8);
     u32x4 pv[RW];
     if constexpr (ADD) {
 #pragma unroll
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     if constexpr (KIND == KIND_VALUE) {
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
-            const size_t midx = (size_t)rr[i] * (uint32_t)a.ngr + (c8 >> a.lpg_shift);
+            const size_t midx = (size_t)rs[i] * (uint32_t)a.ngr + (c8 >> a.lpg_shift);
             if constexpr (FMT == FMT_INT4) {
                 vs[i] = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta1)[midx]);
                 vm[i] = f16_to_f32(reinterpret_cast<const uint16_t*>(a.meta0)[midx]);
@@ -140,7 +142,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
         o.y = finish_pair<ADD>(y[2], y[3], ADD ? pv[i].y : 0u);
         o.z = finish_pair<ADD>(y[4], y[5], ADD ? pv[i].z : 0u);
         o.w = finish_pair<ADD>(y[6], y[7], ADD ? pv[i].w : 0u);
-        if (i < nr && valid) *reinterpret_cast<u32x4*>(a.out + tt[i] * a.ost + (int64_t)h * a.osh + d) = o;
+        if (i < nr && valid)
+            *reinterpret_cast<u32x4*>(a.out + row_offset(tt[i], a.opshift, a.opst, a.ost) + (int64_t)h * a.osh + d) = o;
     }
 }
 
@@ -158,12 +161,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
     const int64_t h = rem / Dp;
     const int j = (int)(rem - h * Dp);
     const int64_t t = SCATTER ? (int64_t)a.pos[r] : r;
-    const uint32_t byte = a.codes[(size_t)(r * a.H + h) * Dp + j];
+    const int64_t rs = a.src ? (int64_t)a.src[r] : r;  // packed row read
+    const uint32_t byte = a.codes[(size_t)(rs * a.H + h) * Dp + j];
     for (int k = 0; k < 2; ++k) {
         const int dd = 2 * j + k;
         if (dd >= D) break;
-        const size_t midx = (KIND == KIND_KEY) ? (size_t)((r / G) * a.H + h) * D + dd
-                                               : (size_t)(r * a.H + h) * ((D + G - 1) / G) + dd / G;
+        const size_t midx = (KIND == KIND_KEY) ? (size_t)((rs / G) * a.H + h) * D + dd
+                                               : (size_t)(rs * a.H + h) * ((D + G - 1) / G) + dd / G;
         const uint32_t c = (byte >> (4 * k)) & 0xFu;
         float y;
         if constexpr (FMT == FMT_INT4) {
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
             const float p = bf16_to_f32(a.prev[t * a.pst + h * a.psh + dd]);
             outb = bf16_bits(__fadd_rn(p, bf16_to_f32(outb)));
         }
-        a.out[t * a.ost + h * a.osh + dd] = (uint16_t)outb;
+        a.out[row_offset(t, a.opshift, a.opst, a.ost) + h * a.osh + dd] = (uint16_t)outb;
     }
 }
 

@@ -365,6 +365,34 @@ __device__ __forceinline__ uint32_t fp4_code(float x, const Fp4Block& b) {
     return e2m1_pair<0>(0u, fp4_scaled(x, b), 0.0f) & 0xFu;
 }
 
+// 8 NVFP4 codes of one chunk: scaled values, then 4 packed E2M1 conversions. One (rarely
+// taken) branch per chunk applies the direct division where a block's 1/s_dec overflowed.
+__device__ __forceinline__ uint32_t fp4_word(const u32x4& v, const Fp4Block* fb, int stride) {
+    float q[8];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    bool div = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        q[2 * j] = __fmul_rn(bf16lo(w4[j]), fb[(2 * j) * stride].rcp);
+        q[2 * j + 1] = __fmul_rn(bf16hi(w4[j]), fb[(2 * j + 1) * stride].rcp);
+        div |= fb[(2 * j) * stride].div | fb[(2 * j + 1) * stride].div;
+    }
+    if (__builtin_expect(div, 0)) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (fb[k * stride].div) {
+                const uint32_t w = w4[k >> 1];
+                q[k] = ((k & 1) ? bf16hi(w) : bf16lo(w)) / fb[k * stride].s_dec;
+            }
+        }
+    }
+    uint32_t word = e2m1_pair<0>(0u, q[0], q[1]);
+    word = e2m1_pair<1>(word, q[2], q[3]);
+    word = e2m1_pair<2>(word, q[4], q[5]);
+    word = e2m1_pair<3>(word, q[6], q[7]);
+    return word;
+}
+
 // NVFP4 global multiplier from the tensor amax (bf16 magnitude bits): fl(2688 / amax);
 // amax == 0 -> 1; an overflowing quotient -> FLT_MAX.
 __device__ __forceinline__ float fp4_global(uint32_t amax_bits) {
@@ -372,6 +400,78 @@ __device__ __forceinline__ float fp4_global(uint32_t amax_bits) {
     if (amax == 0.0f) return 1.0f;
     float g = 2688.0f / amax;
     return __builtin_isinf(g) ? 3.4028234663852886e38f : g;
+}
+
+// Block constants for a multiplier that changes from row to row (NVFP4-row): the same values
+// as fp4_block, with the decode scale and its reciprocal divided out directly instead of
+// looked up in a per-launch table.
+__device__ __forceinline__ Fp4Block fp4_block_direct(uint32_t bamax_bits, float g) {
+    Fp4Block b;
+    const float t6 = div_const<6>(bf16_to_f32(bamax_bits));
+    float s = __fmul_rn(g, t6);
+    s = (s <= 448.0f) ? s : 448.0f;
+    b.code = e4m3_encode(s);
+    const f32x2 e = fp4_code_scales(b.code, g);
+    b.s_dec = e[0];
+    b.rcp = e[1];
+    b.div = __builtin_isinf(e[1]);
+    return b;
+}
+
+// ---- FP8-row ---------------------------------------------------------------------------------
+
+// Row constants: scale = fl(amax / 448) (IEEE division) and, for the branch-free quotient, the
+// Markstein reciprocal pair of the INT4 codes (y = RN(1/scale), ylo its low part). `fast`
+// covers scales in [2^-90, 2^100]: there x * ylo, the FMA remainder and the correction neither
+// underflow nor overflow for any |x / scale| >= 2^-11, so the corrected quotient is
+// fl(x / scale) exactly (tests/probes/cvt_probe.hip sweeps this range at and next to float
+// midpoints); smaller quotients stay below 2^-10, where E4M3 rounds to zero either way. A zero
+// scale uses y = ylo = 0 (every quotient is +-0); other scales divide.
+struct Fp8Row {
+    float s, y, ylo;
+    bool slow;
+};
+
+__device__ __forceinline__ Fp8Row fp8_row_scale(float s) {
+    Fp8Row r;
+    r.s = s;
+    const bool fast = r.s >= 8.077935669463161e-28f && r.s <= 1.2676506002282294e30f;  // 2^-90, 2^100
+    const float y = rcp_rn(r.s);
+    const float ylo = __fmul_rn(__builtin_fmaf(-r.s, y, 1.0f), y);
+    r.y = fast ? y : 0.0f;
+    r.ylo = fast ? ylo : 0.0f;
+    r.slow = !fast && r.s != 0.0f;
+    return r;
+}
+
+__device__ __forceinline__ Fp8Row fp8_row(float amax) { return fp8_row_scale(amax / 448.0f); }
+
+// fl(x / s) for a fast row (sign of zero not kept: callers re-attach the sign of x).
+__device__ __forceinline__ float fp8_quot(float x, const Fp8Row& r) {
+    const float q0 = __builtin_fmaf(x, r.y, __fmul_rn(x, r.ylo));
+    const float rem = __builtin_fmaf(-r.s, q0, x);
+    return __builtin_fmaf(rem, r.y, q0);
+}
+
+// Scaled value to convert: min(|q|, 448) with the sign bit of x.
+__device__ __forceinline__ float fp8_clamped(float q, float x) {
+    const float m = __builtin_fminf(__builtin_fabsf(q), 448.0f);
+    return __uint_as_float(__float_as_uint(m) | (__float_as_uint(x) & 0x80000000u));
+}
+
+// Two clamped values -> two E4M3 codes in the low (HI false) or high half of `word`:
+// v_cvt_pk_fp8_f32, which the device probe shows equal to e4m3_encode(|v|) with the sign bit of
+// v for every binary32 |v| <= 448 (signed zeros included).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t word, float v0, float v1) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, (int)word, HI);
+}
+
+// The two E4M3 values of the low (HI false) or high half of `word`: v_cvt_pk_f32_fp8, equal to
+// the signed e4m3_decode for every finite code (device probe).
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8_values(uint32_t word) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
 }
 
 }  // namespace kvq

@@ -34,7 +34,7 @@ constexpr uint32_t kAmaxMaxBlocks = KVQ_AMAX_MAX_BLOCKS;  // partial maxima held
 // bf16 bits of the encoded value of element (t, h, d) (generic path)
 template <bool DIFF>
 __device__ __forceinline__ uint32_t load_one(const EncArgs& a, int64_t t, int64_t h, int64_t d) {
-    uint32_t c = a.cur[t * a.cst + h * a.csh + d];
+    uint32_t c = a.cur[row_offset(t, a.cpshift, a.cpst, a.cst) + h * a.csh + d];
     if constexpr (DIFF) {
         uint32_t p = a.prev[t * a.pst + h * a.psh + d];
         return bf16_bits(__fsub_rn(bf16_to_f32(c), bf16_to_f32(p)));
@@ -52,7 +52,7 @@ __device__ __forceinline__ void load_rows8(const EncArgs& a, int64_t r0, uint32_
         t[i] = GATHER ? (int64_t)a.pos[r] : r;
     }
 #pragma unroll
-    for (int i = 0; i < RW; ++i) v[i] = ld_stream(a.cur + t[i] * a.cst + (int64_t)h * a.csh + d);
+    for (int i = 0; i < RW; ++i) v[i] = ld_stream(a.cur + row_offset(t[i], a.cpshift, a.cpst, a.cst) + (int64_t)h * a.csh + d);
     if constexpr (DIFF) {
         u32x4 p[RW];
 #pragma unroll
@@ -105,33 +105,6 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
     return even | (odd << 4);
 }
 
-// 8 NVFP4 codes of one chunk: scaled values, then 4 packed E2M1 conversions. One (rarely
-// taken) branch per chunk applies the direct division where a block's 1/s_dec overflowed.
-__device__ __forceinline__ uint32_t fp4_word(const u32x4& v, const Fp4Block* fb, int stride) {
-    float q[8];
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    bool div = false;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        q[2 * j] = __fmul_rn(bf16lo(w4[j]), fb[(2 * j) * stride].rcp);
-        q[2 * j + 1] = __fmul_rn(bf16hi(w4[j]), fb[(2 * j + 1) * stride].rcp);
-        div |= fb[(2 * j) * stride].div | fb[(2 * j + 1) * stride].div;
-    }
-    if (__builtin_expect(div, 0)) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (fb[k * stride].div) {
-                const uint32_t w = w4[k >> 1];
-                q[k] = ((k & 1) ? bf16hi(w) : bf16lo(w)) / fb[k * stride].s_dec;
-            }
-        }
-    }
-    uint32_t word = e2m1_pair<0>(0u, q[0], q[1]);
-    word = e2m1_pair<1>(word, q[2], q[3]);
-    word = e2m1_pair<2>(word, q[4], q[5]);
-    word = e2m1_pair<3>(word, q[6], q[7]);
-    return word;
-}
 
 // ---- VALUE, vector path ------------------------------------------------------------------------
 
@@ -166,7 +139,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
         const int64_t r = r0 + i;
-        const size_t midx = (size_t)r * (uint32_t)a.ngr + (c8 >> a.lpg_shift);
+        // packed row written (slot writes map it; tail rows read an in-range entry, never store)
+        const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
+        const size_t midx = (size_t)wr * (uint32_t)a.ngr + (c8 >> a.lpg_shift);
         uint32_t word;
         if constexpr (FMT == FMT_INT4) {
             short2_t k = keys2(v[i].x), mn = k, mx = k;
@@ -192,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
             if (i < nr && leader) reinterpret_cast<uint8_t*>(a.meta0)[midx] = (uint8_t)fb.code;
         }
         if (i < nr) {
-            if (valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)r * (uint32_t)a.C8 + c8] = word;
+            if (valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)wr * (uint32_t)a.C8 + c8] = word;
             if constexpr (GATHER) {
                 if (c8raw == 0) a.pos_out[r] = a.pos[r];
             }
@@ -368,14 +343,15 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_gen(EncArgs a) {
     const int64_t r = idx / a.H;
     const int64_t h = idx - r * a.H;
     const int64_t t = GATHER ? (int64_t)a.pos[r] : r;
+    const int64_t wr = a.dst ? (int64_t)a.dst[r] : r;  // packed row written
     const int D = a.D, G = a.G;
     const int ngr = (D + G - 1) / G;
     const int Dp = (D + 1) / 2;
-    uint8_t* crow = a.codes + (size_t)(r * a.H + h) * Dp;
+    uint8_t* crow = a.codes + (size_t)(wr * a.H + h) * Dp;
     uint32_t pending = 0;
     for (int c = 0; c < ngr; ++c) {
         const int d0 = c * G, d1 = min(D, d0 + G);
-        const size_t midx = (size_t)(r * a.H + h) * ngr + c;
+        const size_t midx = (size_t)(wr * a.H + h) * ngr + c;
         if constexpr (FMT == FMT_INT4) {
             int kmn = 0x7FFF, kmx = -32768;
             for (int dd = d0; dd < d1; ++dd) {

@@ -8,7 +8,15 @@
 
 namespace kvq {
 
-enum : int { FMT_INT4 = 0, FMT_NVFP4 = 1 };
+enum : int { FMT_INT4 = 0, FMT_NVFP4 = 1, FMT_NVFP4_ROW = 2, FMT_FP8_ROW = 3 };
+
+// Row offset of row t in a (possibly paged) view: rows come in pages of 2^pshift rows,
+// consecutive rows of a page `st` apart and pages `pst` apart. An unpaged view uses pshift 62
+// (every row in page 0), so the offset is t * st.
+__host__ __device__ __forceinline__ int64_t row_offset(int64_t t, int32_t pshift, int64_t pst, int64_t st) {
+    return (t >> pshift) * pst + (t & (((int64_t)1 << pshift) - 1)) * st;
+}
+constexpr int32_t kNoPaging = 62;
 
 // The NVFP4 amax pass writes one partial maximum per block into the workspace.
 #define KVQ_AMAX_MAX_BLOCKS 4096u
@@ -40,10 +48,13 @@ enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 struct EncArgs {
     const uint16_t* cur;
     int64_t cst, csh;
+    int32_t cpshift;       // paging of `cur` (kNoPaging when unpaged)
+    int64_t cpst;
     const uint16_t* prev;  // residual only
     int64_t pst, psh;
     const int32_t* pos;    // sparse residual only
     int32_t* pos_out;      // owned copy of pos
+    const int32_t* dst;    // slot writes: encoded row r lands in packed row dst[r] (NULL: row r)
     int64_t rows;
     int32_t H, D, G;
     // vector-path geometry: C8 = H*D/8 chunks of 8 channels per row; a VALUE group spans
@@ -58,18 +69,21 @@ struct EncArgs {
     uint32_t* ws;  // NVFP4: per-block partial maxima of the amax pass
 };
 
-// Rows being decoded: packed row r goes to output row t = pos ? pos[r] : r; with `prev`
-// the output is bf16(prev[t] + bf16(decoded)).
+// Rows being decoded: output row r reads packed row src ? src[r] : r and goes to output row
+// t = pos ? pos[r] : r; with `prev` the output is bf16(prev[t] + bf16(decoded)).
 struct DecArgs {
     const uint8_t* codes;
     const void* meta0;
     const void* meta1;
     const float* gscale;
     const int32_t* pos;
+    const int32_t* src;    // slot reads (NULL: identity)
     const uint16_t* prev;
     int64_t pst, psh;
     uint16_t* out;
     int64_t ost, osh;
+    int32_t opshift;       // paging of `out` (kNoPaging when unpaged)
+    int64_t opst;
     int64_t rows;
     int32_t H, D, G;
     int32_t C8, D8, n_slabs, lpg, lpg_shift, ngr;
@@ -95,6 +109,9 @@ hipError_t launch_set_global(float* gscale, uint32_t value_bits, hipStream_t s);
 hipError_t launch_encode(int fmt, int kind, const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
 hipError_t launch_decode(int fmt, int kind, const DecArgs& a, bool add, bool scatter, bool vec, hipStream_t s);
 hipError_t launch_copy_rows(const CopyArgs& a, bool vec, hipStream_t s);
+// Row formats (NVFP4-row, FP8-row): encode / decode of rows that each carry their own scale.
+hipError_t launch_row_encode(int fmt, const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
+hipError_t launch_row_decode(int fmt, const DecArgs& a, bool add, bool scatter, bool vec, hipStream_t s);
 hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 hipError_t launch_validate_positions(const int32_t* pos, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,
                                      hipStream_t s);

@@ -35,6 +35,8 @@ def planes(p) -> dict:
             a = a.cpu().numpy()
         if name in ("meta0", "meta1") and a.dtype == np.int16:
             a = a.view(np.uint16)
+        if name in ("meta0", "meta1") and a.dtype == np.float32:
+            a = np.ascontiguousarray(a).view(np.uint32)  # FP32 row scales compare as bits
         if name == "global_scale":
             a = np.asarray(a, np.float32).view(np.uint32)
         out[name] = np.asarray(a)

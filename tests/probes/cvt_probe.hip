@@ -17,12 +17,20 @@
 //       reciprocal is normal
 //   [9] kvq::rcp_rn(x) (v_rcp_f32 plus one Newton step) equal to the IEEE 1 / x, every x in
 //       [2^-100, 2^100]
+//   [11] v_cvt_pk_fp8_f32 with kvq::e4m3_encode(|x|) plus the sign bit of x, every |x| <= 448
+//        (signed zeros included), in both halves of the packed word
+//   [12] v_cvt_pk_f32_fp8 with the signed kvq::e4m3_decode, every finite E4M3 code, both halves
 // and, in a second kernel, the INT4 quotient kvq::int4_quot_raw(d, group(scale)) against the
 // IEEE d / scale for every scale significand (2^23) at eight exponents from 2^-100 to 2^99:
 //   [10] d = RN(m * scale) and its two neighbours for the 512 points m = h + k * ulp(h) / 2
 //        (h = 0.5 ... 15.5, k = -16 ... 15), i.e. quotients at and next to every half-integer
 //        and float midpoint near it, plus one pseudo-random d in [scale / 2, 16 scale): the
 //        quotient bits must match; for d = RN(scale * 2^-j), j = 3 ... 40, the code (rint) must
+// and, in a third kernel, the FP8-row quotient kvq::fp8_quot(x, fp8_row_scale(scale)) against
+// the IEEE x / scale for every scale significand at eight exponents from 2^-90 to 2^99:
+//   [13] signed x = RN(m * scale) and its two neighbours, m a float midpoint in a pseudo-random
+//        binade from 2^-12 to 2^9 with a pseudo-random significand: the quotient bits must
+//        match; for tiny quotients (scale * 2^-11 ... 2^-48) the E4M3 code must
 // counting mismatches and recording the smallest mismatching input of each check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,7 +41,7 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kChecks = 11;
+constexpr int kChecks = 14;
 
 __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint32_t* first) {
     unsigned long long c[kChecks] = {};
@@ -70,6 +78,15 @@ __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint3
                 if (__float_as_uint(rcp_rn(x)) != __float_as_uint(1.0f / x)) { ++c[9]; f[9] = min(f[9], bits); }
             }
         }
+        if (__builtin_fabsf(x) <= 448.0f) {
+            const uint32_t want = e4m3_encode(__builtin_fabsf(x)) | ((bits >> 24) & 0x80u);
+            const uint32_t lo = fp8_pair<false>(0xA5A5A5A5u, x, x);  // bytes 0, 1; bytes 2, 3 kept
+            const uint32_t hi = fp8_pair<true>(0xA5A5A5A5u, x, x);   // bytes 2, 3; bytes 0, 1 kept
+            if (lo != (0xA5A50000u | want | (want << 8)) || hi != (0x0000A5A5u | (want << 16) | (want << 24))) {
+                ++c[11];
+                f[11] = min(f[11], bits);
+            }
+        }
         if (bits < 65536u) {
             // binary16 -> binary32 widening, compared with the exact value h * 2^-24 (subnormal)
             // or the rebiased pattern (normal, inf)
@@ -96,6 +113,14 @@ __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint3
             for (uint32_t k = 0; k < 16u; ++k) {
                 const uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32((float)k, 2, 0xAABBCCDDu);
                 if (b != ((0xAABBCCDDu & 0xFF00FFFFu) | (k << 16))) { ++c[5]; f[5] = min(f[5], 0x100u + k); }
+            }
+        }
+        if (bits < 256u && (bits & 0x7Fu) != 0x7Fu) {
+            const float want = __uint_as_float(__float_as_uint(e4m3_decode(bits & 0x7Fu)) | ((bits & 0x80u) << 24));
+            const f32x2 lo = fp8_values<false>(bits << 8), hi = fp8_values<true>(bits << 16);
+            if (__float_as_uint(lo[1]) != __float_as_uint(want) || __float_as_uint(hi[0]) != __float_as_uint(want)) {
+                ++c[12];
+                f[12] = min(f[12], bits);
             }
         }
         if (bits < 16u) {
@@ -150,6 +175,47 @@ __global__ __launch_bounds__(256) void k_probe_div(unsigned long long* counts, u
     }
 }
 
+// FP8-row quotient: one scale significand and one (binade, sign) choice per thread, eight
+// scale exponents.
+__global__ __launch_bounds__(256) void k_probe_fp8div(unsigned long long* counts, uint32_t* first) {
+    unsigned long long c = 0;
+    uint32_t f = 0xFFFFFFFFu;
+    const int kExp[8] = {-90, -89, -50, -1, 0, 1, 60, 99};
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < (1ull << 32); u += stride) {
+        const uint32_t sig = (uint32_t)u & 0x7FFFFFu, j = (uint32_t)(u >> 23);
+        const uint32_t hsh = (uint32_t)((u * 0x9E3779B97F4A7C15ull) >> 32);
+        const int em = (int)(j % 22u) - 12;                     // quotient binade 2^-12 .. 2^9
+        const double neg = ((j / 22u) & 1u) ? -1.0 : 1.0;
+        const double m0 = __builtin_ldexp(1.0 + (double)(hsh & 0x7FFFFFu) * 0x1p-23, em);
+        const double m = neg * (m0 + __builtin_ldexp(1.0, em - 24));  // a float midpoint
+        for (int ei = 0; ei < 8; ++ei) {
+            const float s = __builtin_ldexpf(__uint_as_float(0x3F800000u | sig), kExp[ei]);
+            const Fp8Row r = fp8_row_scale(s);
+            if (r.slow || r.y == 0.0f) { ++c; f = min(f, (uint32_t)u); continue; }
+            const float x0 = (float)(m * (double)s);
+            const uint32_t xb = __float_as_uint(x0);
+            const float xs[3] = {x0, __uint_as_float(xb - 1u), __uint_as_float(xb + 1u)};
+            for (int t = 0; t < 3; ++t) {
+                if (__float_as_uint(fp8_quot(xs[t], r)) != __float_as_uint(xs[t] / s)) {
+                    ++c;
+                    f = min(f, (uint32_t)u);
+                }
+            }
+            if (j < 38u) {  // tiny quotients: only the E4M3 code is specified
+                const float xt = (float)neg * __builtin_ldexpf(s, -(int)j - 11);
+                const uint32_t a = e4m3_encode(__builtin_fabsf(fp8_clamped(fp8_quot(xt, r), xt)));
+                const uint32_t b = e4m3_encode(__builtin_fabsf(fp8_clamped(xt / s, xt)));
+                if (a != b) { ++c; f = min(f, (uint32_t)u); }
+            }
+        }
+    }
+    if (c) {
+        atomicAdd(&counts[13], c);
+        atomicMin(&first[13], f);
+    }
+}
+
 }  // namespace
 
 extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_host) {
@@ -162,6 +228,8 @@ extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_ho
     hipLaunchKernelGGL(k_probe, dim3(4096), dim3(256), 0, 0, counts, first);
     if (hipGetLastError() != hipSuccess) return 3;
     hipLaunchKernelGGL(k_probe_div, dim3(4096), dim3(256), 0, 0, counts, first);
+    if (hipGetLastError() != hipSuccess) return 3;
+    hipLaunchKernelGGL(k_probe_fp8div, dim3(4096), dim3(256), 0, 0, counts, first);
     if (hipGetLastError() != hipSuccess) return 3;
     if (hipDeviceSynchronize() != hipSuccess) return 4;
     hipMemcpy(counts_host, counts, kChecks * sizeof(unsigned long long), hipMemcpyDeviceToHost);

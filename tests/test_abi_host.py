@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = kvq.library()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert sorted(kvq.EXPORTS) == names
@@ -43,7 +43,8 @@ def test_version_and_status_strings():
     assert lib.kvq_workspace_bytes() >= 8
 
 
-@pytest.mark.parametrize("fmt,G", [("int4", 64), ("int4", 16), ("int4", 32), ("int4", 3), ("nvfp4", 16)])
+@pytest.mark.parametrize("fmt,G", [("int4", 64), ("int4", 16), ("int4", 32), ("int4", 3), ("nvfp4", 16),
+                                   ("nvfp4_row", 16), ("fp8_row", 0)])
 @pytest.mark.parametrize("kind", ["key", "value"])
 @pytest.mark.parametrize("shape", [(131072, 8, 128), (4096, 8, 128), (1000, 4, 256), (7, 3, 5), (0, 8, 128), (1, 1, 128)])
 def test_storage_matches_oracle(fmt, G, kind, shape):
@@ -60,6 +61,11 @@ def test_pages_storage_figures():
     assert kvq.storage_bytes("int4", "value", 64, 1, 8, 128) == 576
     assert kvq.storage_bytes("nvfp4", "key", 16, 4096, 8, 128) == 2359300
     assert kvq.storage_bytes("int4", "value", 0, 1, 1, 128) == 72  # group size 0 = default 64
+    # the row formats: 76 B per NVFP4 row (64 + 8 + 4), FP8 half of bf16 plus a 4 B scale
+    for kind in ("key", "value"):
+        assert kvq.storage_bytes("nvfp4_row", kind, 16, 1, 1, 128) == 76
+        assert kvq.storage_bytes("nvfp4_row", kind, 0, 2, 1, 128) == 152
+        assert kvq.storage_bytes("fp8_row", kind, 0, 1, 1, 128) == 132
 
 
 def _status(fn, *args):
@@ -78,6 +84,9 @@ def test_storage_errors():
     assert lib.kvq_storage_bytes(0, 0, 64, 1 << 20, 1 << 10, 1 << 10, 0, ctypes.byref(out)) == 2  # 2^40 elements
     assert lib.kvq_storage_bytes(0, 0, 64, 1 << 20, 1 << 8, 1 << 7, 0, ctypes.byref(out)) == 0  # 2^35 elements
     assert lib.kvq_storage_bytes(0, 0, 64, 1 << 20, 1 << 10, 1 << 7, 0, None) == 1
+    assert lib.kvq_storage_bytes(2, 0, 32, 4, 1, 16, 0, ctypes.byref(out)) == 5   # NVFP4-row needs 16
+    assert lib.kvq_storage_bytes(3, 0, 16, 4, 1, 16, 0, ctypes.byref(out)) == 5   # FP8-row takes only 0
+    assert lib.kvq_storage_bytes(3, 1, 0, 4, 2, 16, 0, ctypes.byref(out)) == 0 and out.value == 4 * 2 * 20
 
 
 def _tensor(T, H, D, data=0x1000, st=None, sh=None, dtype=0):
@@ -149,6 +158,48 @@ def test_residual_and_decode_argument_errors():
     assert lib.kvq_validate_positions(None, 4, 16, ctypes.c_void_p(0x100), ctypes.c_void_p(0x200), None) == 1
     assert lib.kvq_validate_positions(ctypes.c_void_p(0x100), -1, 16, ctypes.c_void_p(0x100),
                                       ctypes.c_void_p(0x200), None) == 2
+
+
+def _paged(P, S, H, D, data=0x1000, sp=None, ss=None, sh=None, dtype=0):
+    ss = H * D if ss is None else ss
+    sp = S * ss if sp is None else sp
+    sh = D if sh is None else sh
+    return kvq.KvqPaged(ctypes.c_void_p(data), dtype, 0, P, S, H, D, sp, ss, sh)
+
+
+def test_paged_and_slot_argument_errors():
+    lib = kvq.library()
+    p = _packed()
+    x4 = _paged(4, 16, 2, 16)
+    # pack_paged: NULL view, bad dtype, negative page stride, padded pages of a non-power-of-two size
+    assert lib.kvq_pack_paged(None, 0, 0, 64, 0, ctypes.byref(p), None, None) == 1
+    assert lib.kvq_pack_paged(ctypes.byref(_paged(4, 16, 2, 16, dtype=2)), 0, 0, 64, 0, ctypes.byref(p), None, None) == 6
+    assert lib.kvq_pack_paged(ctypes.byref(_paged(4, 16, 2, 16, sp=-1)), 0, 0, 64, 0, ctypes.byref(p), None, None) == 3
+    assert lib.kvq_pack_paged(ctypes.byref(_paged(4, 12, 2, 16, sp=12 * 32 + 32)), 0, 0, 64, 0, ctypes.byref(p), None,
+                              None) == 3
+    # page-local KEY groups: G and page size must divide one another; NVFP4 needs pages of 16k
+    assert lib.kvq_pack_paged(ctypes.byref(_paged(4, 24, 2, 16)), 0, 0, 16, 1, ctypes.byref(p), None, None) == 5
+    assert lib.kvq_pack_paged(ctypes.byref(_paged(4, 8, 2, 16)), 0, 1, 16, 1, ctypes.byref(p),
+                              ctypes.c_void_p(0x6000), None) == 5
+    # unpack_paged: descriptor rows != pages * page_size
+    d = _packed(format=0, kind=1, group_size=16, dtype=0, rows=60, H=2, D=16, full_T=60)
+    assert lib.kvq_unpack_paged(ctypes.byref(d), ctypes.byref(x4), None) == 7
+    # store_rows: formats whose rows are not independent, shape mismatch, too many rows, no slots
+    rows = _tensor(8, 2, 16)
+    for fmt, kind, G in ((0, 0, 64), (1, 1, 16), (1, 0, 16)):
+        c = _packed(format=fmt, kind=kind, group_size=G, dtype=0, rows=32, H=2, D=16, full_T=32)
+        assert lib.kvq_store_rows(ctypes.byref(rows), ctypes.c_void_p(0x8000), ctypes.byref(c), None) == 4
+    c = _packed(format=3, kind=1, group_size=0, dtype=0, rows=32, H=2, D=16, full_T=32)
+    assert lib.kvq_store_rows(ctypes.byref(_tensor(8, 3, 16)), ctypes.c_void_p(0x8000), ctypes.byref(c), None) == 7
+    assert lib.kvq_store_rows(ctypes.byref(_tensor(33, 2, 16)), ctypes.c_void_p(0x8000), ctypes.byref(c), None) == 2
+    assert lib.kvq_store_rows(ctypes.byref(rows), None, ctypes.byref(c), None) == 1
+    c8 = _packed(format=3, kind=1, group_size=16, dtype=0, rows=32, H=2, D=16, full_T=32)
+    assert lib.kvq_store_rows(ctypes.byref(rows), ctypes.c_void_p(0x8000), ctypes.byref(c8), None) == 5
+    # load_rows: shape mismatch, no slots, an empty cache
+    assert lib.kvq_load_rows(ctypes.byref(c), ctypes.c_void_p(0x8000), ctypes.byref(_tensor(8, 2, 8)), None) == 7
+    assert lib.kvq_load_rows(ctypes.byref(c), None, ctypes.byref(rows), None) == 1
+    e = _packed(format=3, kind=1, group_size=0, dtype=0, rows=0, H=2, D=16, full_T=0)
+    assert lib.kvq_load_rows(ctypes.byref(e), ctypes.c_void_p(0x8000), ctypes.byref(rows), None) == 2
 
 
 def test_binding_has_no_cpu_path():

@@ -10,7 +10,10 @@ quotient (every finite non-negative input), v_rcp_f32 against the IEEE reciproca
 bound, normal range), its one-Newton-step refinement against the IEEE reciprocal (exact, every
 scale in [2^-100, 2^100]), and the branch-free INT4 quotient against the IEEE division on
 quotients at and next to every half-integer and float midpoint, for every scale significand at
-eight exponents (about 1.5e11 cases). The software formulations are written from the format definitions and are pinned
+eight exponents (about 1.5e11 cases); the E4M3 conversion instructions against the integer E4M3
+rounding (every binary32 of magnitude up to 448) and decode (every finite code); and the
+branch-free FP8-row quotient against the IEEE division on signed quotients at and next to float
+midpoints from 2^-12 to 2^9 for every scale significand at eight exponents. The software formulations are written from the format definitions and are pinned
 against the oracle end to end by the parity tests.
 """
 
@@ -25,7 +28,9 @@ LIB = os.path.join(os.path.dirname(__file__), "probes", "libkvq_cvt_probe.so")
 NAMES = ["bf16", "f16", "fp4 encode (all finite)", "fp4 encode (|x| <= 8)", "fp4 decode",
          "nibble order / f16 widening", "x/15 by FMA correction", "x/6 by FMA correction",
          "v_rcp_f32 within 1 ulp", "reciprocal + Newton step == RN(1/x)",
-         "INT4 quotient (Markstein) == IEEE d / scale"]
+         "INT4 quotient (Markstein) == IEEE d / scale",
+         "v_cvt_pk_fp8_f32 == E4M3 encode (|x| <= 448)", "v_cvt_pk_f32_fp8 == E4M3 decode",
+         "FP8-row quotient (Markstein) == IEEE x / scale"]
 
 
 def test_conversion_instructions_match_software_rounding():
