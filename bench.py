@@ -14,6 +14,16 @@ INT4 4.5625, NVFP4 8.5625 (+4 B); residual decode 4.5625 (+4 B). NVFP4 encodes r
 twice (tensor amax first, then the codes), which the method's per-tensor scale requires.
 
 Prints one JSON line on stdout; per-op timings go to stderr (and --detail FILE).
+
+After the timed region, "extras" times the rows beyond the bulk step on the same K/V tensors
+(p50 of 20 event-timed calls each, not part of `value`): the row formats NVFP4-row and FP8-row
+(one FP32 scale per token and head; pack, unpack, residual encode/decode), pack_paged /
+unpack_paged of K with page-local groups (16-token pages of a pool that interleaves K and V per
+page, so the page stride is padded), and store_rows / load_rows of 16384 rows into and out of
+a 131072-slot cache. Algorithmic bytes per element for a row format with c code bytes and
+m = block-scale bytes + 4/D row-scale bytes per element: pack and unpack 2 + c + m, residual
+encode and decode 4 + c + m; page-local INT4 G16 K 2.75; a slot write or read of N rows moves
+N*H*D*(2 + c + m) bytes plus 4 B per slot id.
 """
 
 from __future__ import annotations
@@ -50,6 +60,80 @@ def algo_bytes(op: str, fmt: str, n: int) -> float:
     if op == "decode_residual":
         return n * (code + meta + 2 + 2) + extra
     raise ValueError(op)
+
+
+def row_format_bytes(fmt: str) -> tuple:
+    """(code bytes, metadata bytes) per element of a row format at head_dim D."""
+    if fmt == "nvfp4_row":
+        return 0.5, 1.0 / 16 + 4.0 / D
+    return 1.0, 4.0 / D
+
+
+def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
+    """Row formats, paged views and slot writes/reads on the bulk tensors (see the module
+    docstring); returns {name: {us, GBps, pct_peak}}."""
+    n = T * H * D
+    x0, x1 = X["key"]
+    calls = []
+    for fmt, G in (("nvfp4_row", 16), ("fp8_row", 0)):
+        c, m = row_format_bytes(fmt)
+        p = kvq.alloc_packed(fmt, "key", G, T, H, D, T, dev)
+        r = kvq.alloc_packed(fmt, "key", G, T, H, D, T, dev)
+        R0 = torch.empty_like(x0)
+        R1 = torch.empty_like(x0)
+        calls += [
+            (f"{fmt}-key-pack", n * (2 + c + m), lambda p=p, fmt=fmt, G=G: kvq.pack(x0, "key", fmt, G, out=p)),
+            (f"{fmt}-key-unpack", n * (2 + c + m), lambda p=p, R0=R0: kvq.unpack(p, out=R0)),
+            (f"{fmt}-key-encode_residual", n * (4 + c + m),
+             lambda r=r, R0=R0, fmt=fmt, G=G: kvq.encode_residual(x1, R0, "key", fmt, G, out=r)),
+            (f"{fmt}-key-decode_residual", n * (4 + c + m), lambda r=r, R0=R0, R1=R1: kvq.decode_residual(r, R0, out=R1)),
+        ]
+    # paged: a pool [pages, 2 (K, V), 16, H, D]; K pages are 2*16 rows apart
+    S = 16
+    pool = torch.empty((T // S, 2, S, H, D), dtype=torch.bfloat16, device=dev)
+    pool[:, 0] = x0.view(T // S, S, H, D)
+    pool[:, 1] = X["value"][0].view(T // S, S, H, D)
+    pp = kvq.alloc_packed("int4", "key", 16, T, H, D, T, dev)
+    pout = torch.empty_like(pool)
+    calls += [
+        ("int4-key-pack_paged-page_local", n * 2.75,
+         lambda: kvq.pack_paged(pool[:, 0], "key", "int4", 64, page_local=True, out=pp)),
+        ("int4-key-unpack_paged-page_local", n * 2.75, lambda: kvq.unpack_paged(pp, out=pout[:, 0])),
+    ]
+    # slot writes and reads: 16384 rows into / out of a 131072-slot cache
+    N = min(16384, T)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    slots = torch.randperm(T, generator=g)[:N].to(torch.int32).to(dev)
+    rows = x1[:N]
+    for fmt, G in (("nvfp4_row", 16), ("fp8_row", 0)):
+        c, m = row_format_bytes(fmt)
+        cache = kvq.pack(x0, "key", fmt, G)
+        outr = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+        nb = N * H * D * (2 + c + m) + 4 * N
+        calls += [
+            (f"{fmt}-store_rows-16384", nb, lambda cache=cache: kvq.store_rows(cache, rows, slots)),
+            (f"{fmt}-load_rows-16384", nb, lambda cache=cache, outr=outr: kvq.load_rows(cache, slots, out=outr)),
+        ]
+    stream = torch.cuda.current_stream(dev)
+    for _, _, fn in calls:  # warmup
+        fn()
+    torch.cuda.synchronize()
+    out = {}
+    for name, nbytes, fn in calls:
+        ev = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.percentile([a.elapsed_time(b) for a, b in ev], 50) * 1e3)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1)}
+        print(f"extra {name:34s} p50 {us:8.1f} us  {gbs:7.1f} GB/s  {100 * gbs / PEAK_HBM_GBS:5.1f}% of peak",
+              file=sys.stderr)
+    return out
 
 
 def measured_traffic(kernel_name: str):
@@ -107,6 +191,7 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=T_FULL, help="T (default: the bulk workload)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the row-format / paged / slot timings")
     ap.add_argument("--detail", default="")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain copy kernel of a known size (268 MB) after warmup, for counter scaling")
@@ -225,6 +310,10 @@ def main() -> int:
         print(f"{name:34s} mean {v['mean_us']:8.1f} us  p50 {v['p50_us']:8.1f}  p90 {v['p90_us']:8.1f}  "
               f"{v['gbs']:7.1f} GB/s  {100 * v['gbs'] / PEAK_HBM_GBS:5.1f}% of peak", file=sys.stderr)
 
+    extras = None
+    if not args.no_extras:
+        extras = run_extras(kvq, torch, X, T, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(min(args.cpu_sample_tokens, T))
@@ -260,6 +349,7 @@ def main() -> int:
             "traffic": measured_traffic(dom_name),
         },
         "cpu_baseline": cpu,
+        "extras": extras,
     }
     if args.detail:
         with open(args.detail, "w") as f:
