@@ -75,6 +75,12 @@ def _lib():
         lib.kvq_oracle_store_rows.restype = ci
         lib.kvq_oracle_load_rows.argtypes = [ci, ci, i32, i64, i64, i64, p, p, p, p, p, i64, p, i64, i64]
         lib.kvq_oracle_load_rows.restype = ci
+        lib.kvq_oracle_encode_window.argtypes = [p, i64, i64, p, i64, i64, i64, i64, i64, i64, i64, ci, ci, i32,
+                                                 p, p, p, p, p]
+        lib.kvq_oracle_encode_window.restype = ci
+        lib.kvq_oracle_decode_window.argtypes = [ci, ci, i32, i64, i64, i64, i64, i64, p, p, p, p, p, p, i64, i64,
+                                                 p, i64, i64]
+        lib.kvq_oracle_decode_window.restype = ci
         lib.kvq_oracle_storage_bytes.argtypes = [ci, ci, i32, i64, i64, i64, ci]
         lib.kvq_oracle_storage_bytes.restype = i64
         lib.kvq_oracle_nvfp4_global.argtypes = [ctypes.c_float]
@@ -317,6 +323,60 @@ def load_rows(cache: Packed, slots: np.ndarray, out: Optional[np.ndarray] = None
                                      _ptr(cache.global_scale), _ptr(sl), N, _ptr(out), st, sh)
     if rc:
         raise ValueError(f"oracle load_rows failed ({rc})")
+    return out
+
+
+def window_split(T: int, sink: int, recent: int):
+    """(rows kept at the front, rows kept at the end) of a BF16 window over T tokens."""
+    ns = min(sink, T)
+    return ns, min(recent, T - ns)
+
+
+@dataclass
+class Windowed:
+    """A tensor encoded with a BF16 window: the quantized middle rows and the raw protected rows."""
+
+    packed: Packed
+    window: np.ndarray  # uint16 bf16 bits [n_sink + n_recent, H, D]
+    T: int
+    sink: int
+    recent: int
+
+
+def encode_window(cur: np.ndarray, kind: str, fmt: str = "int4", G: Optional[int] = None, sink: int = 4,
+                  recent: int = 16, prev: Optional[np.ndarray] = None) -> Windowed:
+    """Pack (prev None) or residual-encode cur with its first `sink` and latest `recent` rows kept
+    in BF16."""
+    G = _group(fmt, G)
+    cst, csh = _view_strides(cur)
+    pst, psh = _view_strides(prev) if prev is not None else (0, 0)
+    if prev is not None and prev.shape != cur.shape:
+        raise ValueError("cur/prev shape mismatch")
+    T, H, D = cur.shape
+    ns, nr = window_split(T, sink, recent)
+    out = _alloc(fmt, kind, G, T - ns - nr, H, D)
+    win = np.zeros((ns + nr, H, D), np.uint16)
+    rc = _lib().kvq_oracle_encode_window(_ptr(cur), cst, csh, _ptr(prev), pst, psh, T, H, D, sink, recent,
+                                         KIND[kind], FORMAT[fmt], G, _ptr(out.codes), _ptr(out.meta0),
+                                         _ptr(out.meta1), _ptr(out.global_scale), _ptr(win))
+    if rc:
+        raise ValueError(f"oracle encode_window failed ({rc})")
+    return Windowed(out, win, T, sink, recent)
+
+
+def decode_window(w: Windowed, prev: Optional[np.ndarray] = None, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Decode a windowed tensor (adding to prev for a residual) into bf16 bits [T, H, D]."""
+    p = w.packed
+    if out is None:
+        out = np.zeros((w.T, p.H, p.D), np.uint16)
+    ost, osh = _view_strides(out)
+    pst, psh = _view_strides(prev) if prev is not None else (0, 0)
+    win = np.ascontiguousarray(w.window)  # kept alive across the call
+    rc = _lib().kvq_oracle_decode_window(KIND[p.kind], FORMAT[p.format], p.group_size, w.T, p.H, p.D, w.sink,
+                                         w.recent, _ptr(p.codes), _ptr(p.meta0), _ptr(p.meta1),
+                                         _ptr(p.global_scale), _ptr(win), _ptr(prev), pst, psh, _ptr(out), ost, osh)
+    if rc:
+        raise ValueError(f"oracle decode_window failed ({rc})")
     return out
 
 

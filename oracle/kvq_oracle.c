@@ -882,3 +882,82 @@ int kvq_oracle_load_rows(int kind, int format, int32_t G, int64_t n_slots, int64
     }
     return KVQO_OK;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* BF16 protected window                                                                      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Rows kept in BF16 by a window of the first `sink` and the latest `recent` tokens of T:
+ * n_sink = min(sink, T) rows at the front and n_recent = min(recent, T - n_sink) at the end;
+ * the rest, [n_sink, T - n_recent), is quantized. */
+static void window_split(int64_t T, int64_t sink, int64_t recent, int64_t* n_sink, int64_t* n_recent) {
+    *n_sink = sink < T ? sink : T;
+    *n_recent = recent < T - *n_sink ? recent : T - *n_sink;
+}
+
+/* Encode with a BF16 window ([PR166] "Real Ouro numerical comparison": the first 4 and the
+ * latest 16 tokens kept in BF16; protected rows are left out of the quantized payload, and a
+ * passthrough row reconstructs bitwise). READING: the quantized rows [n_sink, T - n_recent) are
+ * encoded as one tensor of their own (KEY groups start at the first quantized row, the NVFP4
+ * multiplier covers only them) -- exactly the sparse residual whose positions are that range;
+ * the protected rows of `cur` are stored raw in `window` ([n_sink + n_recent, H, D] bf16,
+ * front rows first). With prev == NULL the quantized rows are cur itself (pack); otherwise they
+ * are bf16(cur - prev) (residual), while the window still stores cur, so the protected rows of
+ * a reconstruction equal cur exactly. */
+int kvq_oracle_encode_window(const uint16_t* cur, int64_t cst, int64_t csh, const uint16_t* prev, int64_t pst,
+                             int64_t psh, int64_t T, int64_t H, int64_t D, int64_t sink, int64_t recent, int kind,
+                             int format, int32_t G, uint8_t* codes, void* meta0, void* meta1, float* gscale,
+                             uint16_t* window) {
+    if (sink < 0 || recent < 0) return KVQO_BAD_ARG;
+    int64_t ns, nr;
+    window_split(T, sink, recent, &ns, &nr);
+    int64_t rows = T - ns - nr;
+    int rc = check_common(kind, format, G, rows, H, D);
+    if (rc) return rc;
+    float* dense = (float*)malloc(sizeof(float) * (size_t)(rows * H * D) + 4);
+    if (!dense) return KVQO_NOMEM;
+    materialize(cur + ns * cst, cst, csh, prev ? prev + ns * pst : NULL, pst, psh, NULL, rows, H, D, dense);
+    rc = encode_dense(dense, kind, format, G, rows, H, D, codes, meta0, meta1, gscale, -1.0f);
+    free(dense);
+    for (int64_t i = 0; i < ns + nr; ++i) {
+        int64_t t = (i < ns) ? i : T - nr + (i - ns);
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t d = 0; d < D; ++d) window[(i * H + h) * D + d] = cur[t * cst + h * csh + d];
+    }
+    return rc;
+}
+
+/* Decode with a BF16 window: quantized rows decoded (prev == NULL) or added to prev in the
+ * input dtype (residual), protected rows copied bit for bit from `window`. out is [T, H, D]. */
+int kvq_oracle_decode_window(int kind, int format, int32_t G, int64_t T, int64_t H, int64_t D, int64_t sink,
+                             int64_t recent, const uint8_t* codes, const void* meta0, const void* meta1,
+                             const float* gscale, const uint16_t* window, const uint16_t* prev, int64_t pst,
+                             int64_t psh, uint16_t* out, int64_t ost, int64_t osh) {
+    if (sink < 0 || recent < 0) return KVQO_BAD_ARG;
+    int64_t ns, nr;
+    window_split(T, sink, recent, &ns, &nr);
+    int64_t rows = T - ns - nr;
+    int rc = check_common(kind, format, G, rows, H, D);
+    if (rc) return rc;
+    float g = (format == KVQO_NVFP4) ? *gscale : 0.0f;
+    for (int64_t i = 0; i < rows; ++i) {
+        int64_t t = ns + i;
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t d = 0; d < D; ++d) {
+                float v = decode_at(kind, format, G, H, D, codes, meta0, meta1, g, i, h, d);
+                if (prev) {
+                    float p = kvq_oracle_bf16_to_f32(prev[t * pst + h * psh + d]);
+                    float sum = p + v;
+                    out[t * ost + h * osh + d] = kvq_oracle_f32_to_bf16(sum);
+                } else {
+                    out[t * ost + h * osh + d] = (uint16_t)(f32_bits(v) >> 16);
+                }
+            }
+    }
+    for (int64_t i = 0; i < ns + nr; ++i) {
+        int64_t t = (i < ns) ? i : T - nr + (i - ns);
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t d = 0; d < D; ++d) out[t * ost + h * osh + d] = window[(i * H + h) * D + d];
+    }
+    return KVQO_OK;
+}
