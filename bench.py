@@ -20,10 +20,12 @@ After the timed region, "extras" times the rows beyond the bulk step on the same
 (one FP32 scale per token and head; pack, unpack, residual encode/decode), pack_paged /
 unpack_paged of K with page-local groups (16-token pages of a pool that interleaves K and V per
 page, so the page stride is padded), and store_rows / load_rows of 16384 rows into and out of
-a 131072-slot cache. Algorithmic bytes per element for a row format with c code bytes and
+a 131072-slot cache, and the BF16 window (first 4 / latest 16 rows raw) around INT4 G64 K
+pack and residual encode/decode. Algorithmic bytes per element for a row format with c code bytes and
 m = block-scale bytes + 4/D row-scale bytes per element: pack and unpack 2 + c + m, residual
 encode and decode 4 + c + m; page-local INT4 G16 K 2.75; a slot write or read of N rows moves
-N*H*D*(2 + c + m) bytes plus 4 B per slot id.
+N*H*D*(2 + c + m) bytes plus 4 B per slot id; a windowed op moves the codec bytes of its
+T - 20 middle rows plus the 20 protected rows read and written in bf16.
 """
 
 from __future__ import annotations
@@ -99,6 +101,19 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
         ("int4-key-pack_paged-page_local", n * 2.75,
          lambda: kvq.pack_paged(pool[:, 0], "key", "int4", 64, page_local=True, out=pp)),
         ("int4-key-unpack_paged-page_local", n * 2.75, lambda: kvq.unpack_paged(pp, out=pout[:, 0])),
+    ]
+    # BF16 window (first 4 / latest 16 rows raw): INT4 G64 K pack, residual encode, residual decode
+    nmid = (T - 20) * H * D
+    nwin = 20 * H * D * 4  # window rows read and written
+    wp = kvq.encode_window(x0, "key", "int4", 64, 4, 16)
+    wr = kvq.encode_window(x1, "key", "int4", 64, 4, 16, previous=x0)
+    wout = torch.empty_like(x0)
+    calls += [
+        ("int4-key-window_pack", nmid * 2.5625 + nwin, lambda: kvq.encode_window(x0, "key", "int4", 64, 4, 16, out=wp)),
+        ("int4-key-window_encode_residual", nmid * 4.5625 + nwin,
+         lambda: kvq.encode_window(x1, "key", "int4", 64, 4, 16, previous=x0, out=wr)),
+        ("int4-key-window_decode_residual", nmid * 4.5625 + nwin,
+         lambda: kvq.decode_window(wr, previous=x0, out=wout)),
     ]
     # slot writes and reads: 16384 rows into / out of a 131072-slot cache
     N = min(16384, T)

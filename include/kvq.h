@@ -231,6 +231,27 @@ kvq_status kvq_store_rows(const kvq_tensor* rows, const int32_t* slots, kvq_pack
  * HIP. */
 kvq_status kvq_load_rows(const kvq_packed* cache, const int32_t* slots, const kvq_tensor* out, hipStream_t stream);
 
+/* Encode with a BF16 protected window ([PR166] "Real Ouro numerical comparison": the first 4
+ * and latest 16 tokens kept in BF16, protected rows left out of the quantized payload and
+ * passed through bitwise). Of cur's T rows, n_sink = min(sink, T) front rows and
+ * n_recent = min(recent, T - n_sink) end rows are copied raw into `window` (device bf16,
+ * contiguous [n_sink + n_recent, H, D], front rows first); the middle rows are encoded into
+ * *out as a tensor of their own (out->rows = T - n_sink - n_recent, out->full_T = T): packed
+ * when prev == NULL, as the residual bf16(cur - prev) otherwise (the window still holds cur,
+ * so protected rows reconstruct exactly). The middle encode is the same as kvq_encode_residual
+ * with positions = [n_sink, T - n_recent). Workspace rule and errors as kvq_pack /
+ * kvq_encode_residual; KVQ_ERR_SHAPE for a negative window. */
+kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int64_t sink, int64_t recent,
+                             kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out, void* window,
+                             void* workspace, hipStream_t stream);
+
+/* Decode a windowed tensor into `out` ([T, H, D], T = p->full_T): the middle rows are decoded
+ * (prev == NULL) or added to prev in the input dtype (residual), the protected rows are copied
+ * bit for bit from `window`. out may be exactly prev. Errors as kvq_unpack /
+ * kvq_decode_residual. */
+kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
+                             const kvq_tensor* prev, const kvq_tensor* out, hipStream_t stream);
+
 /* Opt-in device-side check of a position map (the codec page's interface review asks that
  * validation never force a host sync). Writes *status (device int32): 0 = valid, bit 0 = some
  * position outside [0, T), bit 1 = some position repeated. `scratch` is a device buffer of

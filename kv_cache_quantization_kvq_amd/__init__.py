@@ -41,7 +41,8 @@ STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_SHAPE", 3: "KVQ_ERR_LAYOUT
 PLANES = ("codes", "meta0", "meta1", "global_scale", "positions")
 EXPORTS = ("kvq_version", "kvq_status_string", "kvq_storage_bytes", "kvq_plane_bytes", "kvq_workspace_bytes",
            "kvq_pack", "kvq_unpack", "kvq_encode_residual", "kvq_decode_residual", "kvq_validate_positions",
-           "kvq_pack_paged", "kvq_unpack_paged", "kvq_store_rows", "kvq_load_rows")
+           "kvq_pack_paged", "kvq_unpack_paged", "kvq_store_rows", "kvq_load_rows", "kvq_encode_window",
+           "kvq_decode_window")
 
 
 class KvqError(RuntimeError):
@@ -112,6 +113,10 @@ def library() -> ctypes.CDLL:
         lib.kvq_store_rows.restype = ctypes.c_int
         lib.kvq_load_rows.argtypes = [PP, P, TP, P]
         lib.kvq_load_rows.restype = ctypes.c_int
+        lib.kvq_encode_window.argtypes = [TP, TP, I64, I64, ctypes.c_int, ctypes.c_int, I32, PP, P, P, P]
+        lib.kvq_encode_window.restype = ctypes.c_int
+        lib.kvq_decode_window.argtypes = [PP, P, I64, I64, TP, TP, P]
+        lib.kvq_decode_window.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -409,6 +414,58 @@ def load_rows(cache: Packed, slots: torch.Tensor, out: Optional[torch.Tensor] = 
     return out
 
 
+def window_split(T: int, sink: int, recent: int) -> Tuple[int, int]:
+    """(rows kept in front, rows kept at the end) of a BF16 window over T tokens."""
+    ns = min(sink, T)
+    return ns, min(recent, T - ns)
+
+
+@dataclass
+class Windowed:
+    """A tensor encoded with a BF16 window: the quantized middle rows and the raw protected rows."""
+
+    packed: Packed
+    window: torch.Tensor  # bf16 [n_sink + n_recent, H, D]
+    T: int
+    sink: int
+    recent: int
+
+
+def encode_window(current: torch.Tensor, kind: str = "key", format: str = "int4", group_size: int = 0,
+                  sink: int = 4, recent: int = 16, previous: Optional[torch.Tensor] = None,
+                  out: Optional[Windowed] = None) -> Windowed:
+    """Pack (previous None) or residual-encode `current` with its first `sink` and latest `recent`
+    rows kept in BF16."""
+    dev = _device_of(current)
+    T, H, D = current.shape
+    G = group_size or default_group(format)
+    ns, nr = window_split(T, sink, recent)
+    if out is None:
+        out = Windowed(alloc_packed(format, kind, G, T - ns - nr, H, D, T, dev),
+                       torch.empty((ns + nr, H, D), dtype=torch.bfloat16, device=dev), T, sink, recent)
+    desc = out.packed.descriptor()
+    ws = workspace(dev) if format == "nvfp4" else None
+    pv = ctypes.byref(_view(previous)) if previous is not None else None
+    _check("kvq_encode_window", library().kvq_encode_window(ctypes.byref(_view(current)), pv, sink, recent, KIND[kind],
+                                                            FORMAT[format], G, ctypes.byref(desc), _ptr(out.window),
+                                                            _ptr(ws), _stream(dev)))
+    return out
+
+
+def decode_window(w: Windowed, previous: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode a windowed tensor into bf16 [T, H, D] (adding to `previous` for a residual)."""
+    p = w.packed
+    dev = p.codes.device
+    if out is None:
+        out = torch.empty((w.T, p.H, p.D), dtype=torch.bfloat16, device=dev)
+    desc = p.descriptor()
+    pv = ctypes.byref(_view(previous)) if previous is not None else None
+    _check("kvq_decode_window", library().kvq_decode_window(ctypes.byref(desc), _ptr(w.window), w.sink, w.recent, pv,
+                                                            ctypes.byref(_view(out)), _stream(dev)))
+    return out
+
+
 def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
     """Device-side check of a position map; returns a device int32 status (0 = valid, bit 0 =
     out of range, bit 1 = repeated) without synchronizing."""
@@ -422,4 +479,5 @@ def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
 
 __all__ = ["pack", "unpack", "encode_residual", "decode_residual", "storage_bytes", "plane_bytes",
            "validate_positions", "pack_paged", "unpack_paged", "store_rows", "load_rows", "alloc_cache",
+           "encode_window", "decode_window", "Windowed",
            "Packed", "KvqError", "library", "version", "workspace", "alloc_packed"]

@@ -337,6 +337,45 @@ kvq_status decode_run(const kvq_packed* p, int64_t rows, const kvq_tensor* prev,
     return hip_status(launch_decode(p->format, p->kind, a, prev != nullptr, positions != nullptr, vec, stream));
 }
 
+// Copy `rows` rows of one strided bf16 view into another (the row-copy kernel).
+kvq_status copy_view_rows(const void* src, int64_t sst, int64_t ssh, void* dst, int64_t dst_t, int64_t dsh,
+                          int64_t rows, int64_t H, int64_t D, hipStream_t stream) {
+    if (rows * H * D == 0) return KVQ_OK;
+    CopyArgs c;
+    memset(&c, 0, sizeof c);
+    c.src = static_cast<const uint16_t*>(src);
+    c.sst = sst;
+    c.ssh = ssh;
+    c.dst = static_cast<uint16_t*>(dst);
+    c.dst_t = dst_t;
+    c.dsh = dsh;
+    c.T = rows;
+    c.H = (int32_t)H;
+    c.D = (int32_t)D;
+    const bool vec = (D % 8 == 0) && view_vec_ok(src, sst, ssh) && view_vec_ok(dst, dst_t, dsh) &&
+                     (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
+    if (vec) {
+        c.C8 = (int32_t)(H * D / 8);
+        c.div_C8 = fastdiv_make((uint32_t)c.C8);
+        c.div_D8 = fastdiv_make((uint32_t)(D / 8));
+    }
+    return hip_status(launch_copy_rows(c, vec, stream));
+}
+
+// Rows kept by a BF16 window over T tokens: min(sink, T) in front, then up to `recent` at the end.
+void window_split(int64_t T, int64_t sink, int64_t recent, int64_t* ns, int64_t* nr) {
+    *ns = sink < T ? sink : T;
+    *nr = recent < T - *ns ? recent : T - *ns;
+}
+
+// Rows [r0, r0 + n) of a view, as a view.
+kvq_tensor row_slice(const kvq_tensor* x, int64_t r0, int64_t n) {
+    kvq_tensor v = *x;
+    v.data = static_cast<uint16_t*>(x->data) + r0 * x->stride_t;
+    v.T = n;
+    return v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -504,6 +543,64 @@ kvq_status kvq_load_rows(const kvq_packed* cache, const int32_t* slots, const kv
     if (!slots) return KVQ_ERR_NULL;
     if (cache->rows == 0) return KVQ_ERR_SHAPE;  // no slot to read
     return decode_run(cache, N, nullptr, view_of(out), nullptr, slots, stream);
+}
+
+kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int64_t sink, int64_t recent,
+                             kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out, void* window,
+                             void* workspace, hipStream_t stream) {
+    kvq_status st = check_tensor(cur);
+    if (st) return st;
+    if (sink < 0 || recent < 0) return KVQ_ERR_SHAPE;
+    if (prev) {
+        if ((st = check_tensor(prev))) return st;
+        if (prev->T != cur->T || prev->H != cur->H || prev->D != cur->D) return KVQ_ERR_SHAPE;
+    }
+    int64_t ns, nr;
+    window_split(cur->T, sink, recent, &ns, &nr);
+    const int64_t T = cur->T, H = cur->H, D = cur->D, mid = T - ns - nr;
+    if ((ns + nr) * H * D > 0 && !window) return KVQ_ERR_NULL;
+    const kvq_tensor cm = row_slice(cur, ns, mid);
+    kvq_tensor pm;
+    if (prev) pm = row_slice(prev, ns, mid);
+    if ((st = encode_common(view_of(&cm), prev ? &pm : nullptr, nullptr, 0, kind, format, group_size, out, workspace,
+                            stream)))
+        return st;
+    out->full_T = T;
+    if ((st = copy_view_rows(cur->data, cur->stride_t, cur->stride_h, window, H * D, D, ns, H, D, stream))) return st;
+    return copy_view_rows(static_cast<const uint16_t*>(cur->data) + (T - nr) * cur->stride_t, cur->stride_t,
+                          cur->stride_h, static_cast<uint16_t*>(window) + ns * H * D, H * D, D, nr, H, D, stream);
+}
+
+kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
+                             const kvq_tensor* prev, const kvq_tensor* out, hipStream_t stream) {
+    kvq_status st = check_packed(p);
+    if (st) return st;
+    if ((st = check_tensor(out))) return st;
+    if (sink < 0 || recent < 0) return KVQ_ERR_SHAPE;
+    int64_t ns, nr;
+    window_split(out->T, sink, recent, &ns, &nr);
+    const int64_t T = out->T, H = out->H, D = out->D, mid = T - ns - nr;
+    if (p->positions || p->rows != mid || p->full_T != T || p->H != H || p->D != D) return KVQ_ERR_MISMATCH;
+    if ((ns + nr) * H * D > 0 && !window) return KVQ_ERR_NULL;
+    if (prev) {
+        if ((st = check_tensor(prev))) return st;
+        if (prev->T != T || prev->H != H || prev->D != D) return KVQ_ERR_SHAPE;
+        const bool same = out->data == prev->data && out->stride_t == prev->stride_t && out->stride_h == prev->stride_h;
+        if (!same) {
+            uintptr_t plo, phi, olo, ohi;
+            view_span(prev, &plo, &phi);
+            view_span(out, &olo, &ohi);
+            if (plo < ohi && olo < phi) return KVQ_ERR_LAYOUT;  // partial overlap
+        }
+    }
+    const kvq_tensor om = row_slice(out, ns, mid);
+    kvq_tensor pm;
+    if (prev) pm = row_slice(prev, ns, mid);
+    if ((st = decode_run(p, mid, prev ? &pm : nullptr, view_of(&om), nullptr, nullptr, stream))) return st;
+    if ((st = copy_view_rows(window, H * D, D, out->data, out->stride_t, out->stride_h, ns, H, D, stream))) return st;
+    return copy_view_rows(static_cast<const uint16_t*>(window) + ns * H * D, H * D, D,
+                          static_cast<uint16_t*>(out->data) + (T - nr) * out->stride_t, out->stride_t, out->stride_h,
+                          nr, H, D, stream);
 }
 
 kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,

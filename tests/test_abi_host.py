@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = kvq.library()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert sorted(kvq.EXPORTS) == names
@@ -200,6 +200,25 @@ def test_paged_and_slot_argument_errors():
     assert lib.kvq_load_rows(ctypes.byref(c), None, ctypes.byref(rows), None) == 1
     e = _packed(format=3, kind=1, group_size=0, dtype=0, rows=0, H=2, D=16, full_T=0)
     assert lib.kvq_load_rows(ctypes.byref(e), ctypes.c_void_p(0x8000), ctypes.byref(rows), None) == 2
+
+
+def test_window_argument_errors():
+    lib = kvq.library()
+    x = _tensor(40, 2, 16)
+    p = _packed()
+    assert lib.kvq_encode_window(ctypes.byref(x), None, -1, 16, 0, 0, 64, ctypes.byref(p), ctypes.c_void_p(0x9000),
+                                 None, None) == 2
+    assert lib.kvq_encode_window(ctypes.byref(x), None, 4, 16, 0, 0, 64, ctypes.byref(p), None, None, None) == 1
+    assert lib.kvq_encode_window(ctypes.byref(x), ctypes.byref(_tensor(39, 2, 16)), 4, 16, 0, 0, 64, ctypes.byref(p),
+                                 ctypes.c_void_p(0x9000), None, None) == 2
+    # decode: the descriptor must hold exactly the middle rows of out (40 - 4 - 16 = 20)
+    d = _packed(format=0, kind=0, group_size=64, dtype=0, rows=21, H=2, D=16, full_T=40)
+    assert lib.kvq_decode_window(ctypes.byref(d), ctypes.c_void_p(0x9000), 4, 16, None, ctypes.byref(x), None) == 7
+    d.rows = 20
+    assert lib.kvq_decode_window(ctypes.byref(d), None, 4, 16, None, ctypes.byref(x), None) == 1
+    shifted = _tensor(40, 2, 16, data=0x1000 + 64)
+    assert lib.kvq_decode_window(ctypes.byref(d), ctypes.c_void_p(0x9000), 4, 16, ctypes.byref(x),
+                                 ctypes.byref(shifted), None) == 3
 
 
 def test_binding_has_no_cpu_path():

@@ -182,3 +182,33 @@ def test_store_rows_into_slots_of_a_paged_pool_round_trip():
     kvq.store_rows(cache, to_dev(new), torch.from_numpy(slots).to(dev()))
     oracle.store_rows(ocache, new, slots)
     assert_bits_equal(to_host(kvq.unpack_paged(cache, page_size=S)), oracle.unpack_paged(ocache, P, S), "pool")
+
+
+WIN_FORMS = [("int4", 64), ("int4", 16), ("nvfp4", 16), ("nvfp4_row", 16), ("fp8_row", 0)]
+
+
+@pytest.mark.parametrize("fmt,G", WIN_FORMS)
+@pytest.mark.parametrize("kind", ["key", "value"])
+@pytest.mark.parametrize("T,sink,recent", [(300, 4, 16), (97, 4, 16), (20, 4, 16), (7, 4, 16), (64, 0, 0)])
+def test_window_pack_and_residual(fmt, G, kind, T, sink, recent):
+    rng = np.random.default_rng(T + 3)
+    H, D = 4, 128
+    x0 = normal_kv(rng, T, H, D)
+    x1 = bf16_bits(oracle.bf16_to_f32(x0).astype(np.float64) + 0.1 * rng.standard_normal((T, H, D)))
+    x0d, x1d = to_dev(x0), to_dev(x1)
+    # plain pack with a window
+    gw = kvq.encode_window(x0d, kind, fmt, G, sink, recent)
+    ow = oracle.encode_window(x0, kind, fmt, G, sink, recent)
+    assert_same_packed(gw.packed, ow.packed, "window payload")
+    assert_bits_equal(to_host(gw.window), ow.window, "window rows")
+    R0d = kvq.decode_window(gw)
+    R0o = oracle.decode_window(ow)
+    assert_bits_equal(to_host(R0d), R0o, "window decode")
+    # residual with a window, decoded in place into a copy of prev
+    gr = kvq.encode_window(x1d, kind, fmt, G, sink, recent, previous=R0d)
+    orr = oracle.encode_window(x1, kind, fmt, G, sink, recent, prev=R0o)
+    assert_same_packed(gr.packed, orr.packed, "window residual payload")
+    assert_bits_equal(to_host(gr.window), orr.window, "window residual rows")
+    buf = R0d.clone()
+    kvq.decode_window(gr, previous=buf, out=buf)
+    assert_bits_equal(to_host(buf), oracle.decode_window(orr, prev=R0o), "window residual decode")
