@@ -252,6 +252,33 @@ kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int6
 kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
                              const kvq_tensor* prev, const kvq_tensor* out, hipStream_t stream);
 
+/* Bytes of device workspace kvq_decode_attention needs for T cached tokens, H KV heads and Hq
+ * query heads (per-block partial maxima, sums and unnormalized outputs); 0 for invalid sizes.
+ * No initialization is needed. Calls that may run concurrently need distinct workspaces. */
+size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq);
+
+/* Decode attention that reads the packed cache directly ([PR166] reviews of the codec: the
+ * hot-path option of dequantizing to BF16 in registers and keeping a BF16 matrix multiply, and
+ * the comparison after fusing dequantization and residual reconstruction into attention). One
+ * query token per query head: out[hq, :] = softmax(scale * q[hq] . K[:, hk]^T) V[:, hk] over
+ * all T = k->rows cached tokens, with KV head hk = hq / (Hq / H). K and V are reconstructed in
+ * registers exactly as kvq_unpack decodes them, or, with k_res and v_res, as kvq_decode_residual
+ * of those dense residuals on top (both or neither). Scores and softmax run in FP32, the
+ * probabilities are rounded to bf16 for the PV product (bf16 MFMA, FP32 accumulation), so the
+ * output matches float64 attention over the decoded cache to within about 2^-9 of max |V|.
+ *   q        device bf16 [Hq, 128], contiguous, 16-byte aligned
+ *   k, v     packed KEY / VALUE tensors of one layer: rows = T >= 1, the same H, head_dim 128,
+ *            dense, the same format (INT4 or NVFP4); INT4 K groups a multiple of 16 tokens,
+ *            INT4 V groups a multiple of 8 dividing 128; planes 16-byte aligned
+ *   k_res, v_res  optional dense residuals of the same shape (formats may differ from k, v)
+ *   Hq       a multiple of H with Hq / H <= 16
+ *   out      device float [Hq, 128]
+ *   workspace  device memory of at least kvq_attention_workspace_bytes(T, H, Hq) bytes
+ * Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, MISMATCH, WORKSPACE, HIP. */
+kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, const kvq_packed* v,
+                                const kvq_packed* k_res, const kvq_packed* v_res, float softmax_scale, float* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Opt-in device-side check of a position map (the codec page's interface review asks that
  * validation never force a host sync). Writes *status (device int32): 0 = valid, bit 0 = some
  * position outside [0, T), bit 1 = some position repeated. `scratch` is a device buffer of

@@ -42,7 +42,7 @@ PLANES = ("codes", "meta0", "meta1", "global_scale", "positions")
 EXPORTS = ("kvq_version", "kvq_status_string", "kvq_storage_bytes", "kvq_plane_bytes", "kvq_workspace_bytes",
            "kvq_pack", "kvq_unpack", "kvq_encode_residual", "kvq_decode_residual", "kvq_validate_positions",
            "kvq_pack_paged", "kvq_unpack_paged", "kvq_store_rows", "kvq_load_rows", "kvq_encode_window",
-           "kvq_decode_window")
+           "kvq_decode_window", "kvq_attention_workspace_bytes", "kvq_decode_attention")
 
 
 class KvqError(RuntimeError):
@@ -117,6 +117,10 @@ def library() -> ctypes.CDLL:
         lib.kvq_encode_window.restype = ctypes.c_int
         lib.kvq_decode_window.argtypes = [PP, P, I64, I64, TP, TP, P]
         lib.kvq_decode_window.restype = ctypes.c_int
+        lib.kvq_attention_workspace_bytes.argtypes = [I64, I64, I64]
+        lib.kvq_attention_workspace_bytes.restype = ctypes.c_size_t
+        lib.kvq_decode_attention.argtypes = [P, I64, PP, PP, PP, PP, ctypes.c_float, P, P, ctypes.c_size_t, P]
+        lib.kvq_decode_attention.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -466,6 +470,37 @@ def decode_window(w: Windowed, previous: Optional[torch.Tensor] = None,
     return out
 
 
+_attn_ws: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def decode_attention(q: torch.Tensor, k: Packed, v: Packed, k_res: Optional[Packed] = None,
+                     v_res: Optional[Packed] = None, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step of attention over the packed cache (K, V, optionally one residual each):
+    q bf16 [Hq, 128] -> float32 [Hq, 128]; query head hq reads KV head hq // (Hq // H)."""
+    dev = _device_of(q)
+    if q.dtype != torch.bfloat16 or q.dim() != 2:
+        raise ValueError("kvq: q must be a bf16 [Hq, head_dim] tensor")
+    q = q.contiguous()
+    Hq, Dq = q.shape
+    if out is None:
+        out = torch.empty((Hq, Dq), dtype=torch.float32, device=dev)
+    need = int(library().kvq_attention_workspace_bytes(k.rows, k.H, Hq))
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), torch.cuda.current_stream(dev).cuda_stream)
+    ws = _attn_ws.get(key)
+    if ws is None or ws.numel() < max(need, 4):
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+        _attn_ws[key] = ws
+    dk, dv = k.descriptor(), v.descriptor()
+    drk = k_res.descriptor() if k_res is not None else None
+    drv = v_res.descriptor() if v_res is not None else None
+    scale = (1.0 / Dq ** 0.5) if scale is None else float(scale)
+    _check("kvq_decode_attention", library().kvq_decode_attention(
+        _ptr(q), Hq, ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(drk) if drk is not None else None,
+        ctypes.byref(drv) if drv is not None else None, scale, _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
 def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
     """Device-side check of a position map; returns a device int32 status (0 = valid, bit 0 =
     out of range, bit 1 = repeated) without synchronizing."""
@@ -479,5 +514,5 @@ def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
 
 __all__ = ["pack", "unpack", "encode_residual", "decode_residual", "storage_bytes", "plane_bytes",
            "validate_positions", "pack_paged", "unpack_paged", "store_rows", "load_rows", "alloc_cache",
-           "encode_window", "decode_window", "Windowed",
+           "encode_window", "decode_window", "Windowed", "decode_attention",
            "Packed", "KvqError", "library", "version", "workspace", "alloc_packed"]

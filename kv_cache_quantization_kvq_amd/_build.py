@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_abi.hip", "kvq_encode.hip", "kvq_decode.hip", "kvq_rowfmt.hip"]
+SOURCES = ["kvq_abi.hip", "kvq_encode.hip", "kvq_decode.hip", "kvq_rowfmt.hip", "kvq_attn.hip"]
 HEADERS = ["kvq_device.hpp", "kvq_launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

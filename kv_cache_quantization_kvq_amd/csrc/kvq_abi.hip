@@ -376,6 +376,42 @@ kvq_tensor row_slice(const kvq_tensor* x, int64_t r0, int64_t n) {
     return v;
 }
 
+// Token split of decode attention: blocks of a multiple of 64 tokens, about 2048 blocks in all.
+void attn_split(int64_t T, int64_t H, int32_t* n_split, int64_t* tc) {
+    const int64_t target = (2048 / (H > 0 ? H : 1)) > 0 ? 2048 / (H > 0 ? H : 1) : 1;
+    int64_t per = cdiv(T > 0 ? T : 1, 64 * target);
+    *tc = 64 * (per > 0 ? per : 1);
+    *n_split = (int32_t)cdiv(T > 0 ? T : 1, *tc);
+}
+
+size_t attn_workspace(int64_t T, int64_t H, int64_t rep) {
+    int32_t ns;
+    int64_t tc;
+    attn_split(T, H, &ns, &tc);
+    return (size_t)H * ns * rep * (KVQ_ATTN_D + 2) * sizeof(float);
+}
+
+// One packed tensor of an attention call: dense, the expected kind, head_dim 128, and a group
+// size the kernel's tiling takes (INT4 K: G % 16 == 0; INT4 V: G % 8 == 0 and G | 128).
+kvq_status attn_operand(const kvq_packed* p, int kind, int64_t T, int64_t H, AttnPlanes* out) {
+    kvq_status st = check_packed(p);
+    if (st) return st;
+    if (p->kind != kind || p->positions) return KVQ_ERR_MISMATCH;
+    if (p->format != KVQ_INT4 && p->format != KVQ_NVFP4) return KVQ_ERR_FORMAT;
+    if (p->D != KVQ_ATTN_D) return KVQ_ERR_SHAPE;
+    if (p->rows != T || p->H != H) return KVQ_ERR_MISMATCH;
+    const int32_t G = p->group_size;
+    if (p->format == KVQ_INT4) {
+        if (kind == KVQ_KEY ? (G % 16 != 0) : (G % 8 != 0 || KVQ_ATTN_D % G != 0)) return KVQ_ERR_GROUP;
+        if (!aligned(p->meta0, 16) || !aligned(p->meta1, 16)) return KVQ_ERR_LAYOUT;
+    } else if (!aligned(p->meta0, 16)) {
+        return KVQ_ERR_LAYOUT;
+    }
+    if (!aligned(p->codes, 16)) return KVQ_ERR_LAYOUT;
+    *out = AttnPlanes{p->codes, p->meta0, p->meta1, p->global_scale, G};
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -601,6 +637,46 @@ kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t si
     return copy_view_rows(static_cast<const uint16_t*>(window) + ns * H * D, H * D, D,
                           static_cast<uint16_t*>(out->data) + (T - nr) * out->stride_t, out->stride_t, out->stride_h,
                           nr, H, D, stream);
+}
+
+size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq) {
+    if (T < 1 || H < 1 || Hq < H || Hq % H != 0 || T >= kMaxDim || H >= kMaxDim) return 0;
+    return attn_workspace(T, H, Hq / H);
+}
+
+kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, const kvq_packed* v,
+                                const kvq_packed* k_res, const kvq_packed* v_res, float softmax_scale, float* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !out || !k || !v || !workspace) return KVQ_ERR_NULL;
+    if ((k_res == nullptr) != (v_res == nullptr)) return KVQ_ERR_NULL;
+    const int64_t T = k->rows, H = k->H;
+    if (T < 1 || H < 1 || Hq < 1 || Hq % H != 0 || Hq / H > 16) return KVQ_ERR_SHAPE;
+    AttnArgs a;
+    memset(&a, 0, sizeof a);
+    kvq_status st = attn_operand(k, KVQ_KEY, T, H, &a.k);
+    if (!st) st = attn_operand(v, KVQ_VALUE, T, H, &a.v);
+    if (st) return st;
+    if (k->format != v->format) return KVQ_ERR_FORMAT;
+    int rfmt = KVQ_ATTN_NO_RESIDUAL;
+    if (k_res) {
+        if ((st = attn_operand(k_res, KVQ_KEY, T, H, &a.rk))) return st;
+        if ((st = attn_operand(v_res, KVQ_VALUE, T, H, &a.rv))) return st;
+        if (k_res->format != v_res->format) return KVQ_ERR_FORMAT;
+        rfmt = k_res->format;
+    }
+    if (!aligned(q, 16) || !aligned(out, 4) || !aligned(workspace, 4)) return KVQ_ERR_LAYOUT;
+    const int64_t rep = Hq / H;
+    if (workspace_bytes < attn_workspace(T, H, rep)) return KVQ_ERR_WORKSPACE;
+    a.q = static_cast<const uint16_t*>(q);
+    a.T = T;
+    a.H = (int32_t)H;
+    a.rep = (int32_t)rep;
+    attn_split(T, H, &a.n_split, &a.tc);
+    a.qscale = softmax_scale * 1.4426950408889634f;  // scores in log2 units: exp(x) = exp2(x log2 e)
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = a.part_o + (size_t)H * a.n_split * rep * KVQ_ATTN_D;
+    a.out = out;
+    return hip_status(launch_attention(k->format, rfmt, a, stream));
 }
 
 kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,

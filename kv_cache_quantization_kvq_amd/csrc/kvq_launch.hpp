@@ -101,6 +101,29 @@ struct CopyArgs {
     FastDiv div_C8, div_D8;
 };
 
+// Decode attention over packed K/V (head_dim 128; KVQ_ATTN_NO_RESIDUAL: no residual).
+#define KVQ_ATTN_D 128
+#define KVQ_ATTN_NO_RESIDUAL (-1)
+struct AttnPlanes {
+    const uint8_t* codes;
+    const void* meta0;
+    const void* meta1;
+    const float* gscale;
+    int32_t G;
+};
+struct AttnArgs {
+    const uint16_t* q;  // [H * rep, 128] bf16
+    AttnPlanes k, v, rk, rv;
+    int64_t T;
+    int32_t H, rep;
+    int32_t n_split;
+    int64_t tc;         // tokens per block (a multiple of 64)
+    float qscale;       // softmax scale * log2(e)
+    float* part_o;      // [H, n_split, rep, 128]
+    float* part_ml;     // [H, n_split, rep, 2]
+    float* out;         // [H * rep, 128] fp32
+};
+
 // ---- launchers (return hipGetLastError() of the launch) ----
 // vec: the 8-channel vector path is legal for these arguments (alignment, strides, G).
 
@@ -112,6 +135,8 @@ hipError_t launch_copy_rows(const CopyArgs& a, bool vec, hipStream_t s);
 // Row formats (NVFP4-row, FP8-row): encode / decode of rows that each carry their own scale.
 hipError_t launch_row_encode(int fmt, const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
 hipError_t launch_row_decode(int fmt, const DecArgs& a, bool add, bool scatter, bool vec, hipStream_t s);
+// Decode attention: base format of K and V, residual format (or KVQ_ATTN_NO_RESIDUAL).
+hipError_t launch_attention(int fmt, int rfmt, const AttnArgs& a, hipStream_t s);
 hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 hipError_t launch_validate_positions(const int32_t* pos, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,
                                      hipStream_t s);

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = kvq.library()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert sorted(kvq.EXPORTS) == names
@@ -219,6 +219,37 @@ def test_window_argument_errors():
     shifted = _tensor(40, 2, 16, data=0x1000 + 64)
     assert lib.kvq_decode_window(ctypes.byref(d), ctypes.c_void_p(0x9000), 4, 16, ctypes.byref(x),
                                  ctypes.byref(shifted), None) == 3
+
+
+def test_attention_argument_errors():
+    lib = kvq.library()
+    assert lib.kvq_attention_workspace_bytes(0, 8, 64) == 0
+    assert lib.kvq_attention_workspace_bytes(100, 8, 60) == 0
+    assert lib.kvq_attention_workspace_bytes(131072, 8, 64) > 0
+    k = _packed(format=0, kind=0, group_size=64, dtype=0, rows=256, H=2, D=128, full_T=256)
+    v = _packed(format=0, kind=1, group_size=64, dtype=0, rows=256, H=2, D=128, full_T=256)
+    for obj in (k, v):
+        obj.codes, obj.meta0, obj.meta1 = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)
+    q, out, ws = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000), ctypes.c_void_p(0x60000)
+    big = 1 << 30
+    call = lambda kk, vv, Hq=16, rk=None, rv=None, wsb=big: lib.kvq_decode_attention(  # noqa: E731
+        q, Hq, ctypes.byref(kk), ctypes.byref(vv), rk, rv, ctypes.c_float(0.1), out, ws, wsb, None)
+    assert lib.kvq_decode_attention(None, 16, ctypes.byref(k), ctypes.byref(v), None, None, ctypes.c_float(0.1), out,
+                                    ws, big, None) == 1
+    assert call(k, v, Hq=15) == 2            # Hq not a multiple of H
+    assert call(k, v, Hq=34) == 2            # more than 16 query heads per KV head
+    assert call(v, k) == 7                   # kinds swapped
+    assert call(k, v, rk=ctypes.byref(k)) == 1  # one residual without the other
+    assert call(k, v, wsb=16) == 9           # workspace too small
+    k64 = _packed(format=0, kind=0, group_size=8, dtype=0, rows=256, H=2, D=128, full_T=256)
+    k64.codes, k64.meta0, k64.meta1 = k.codes, k.meta0, k.meta1
+    assert call(k64, v) == 5                 # INT4 K groups must be a multiple of 16 tokens
+    k96 = _packed(format=0, kind=0, group_size=64, dtype=0, rows=256, H=2, D=96, full_T=256)
+    k96.codes, k96.meta0, k96.meta1 = k.codes, k.meta0, k.meta1
+    assert call(k96, v) == 2                 # head_dim 128 only
+    vt = _packed(format=0, kind=1, group_size=64, dtype=0, rows=255, H=2, D=128, full_T=255)
+    vt.codes, vt.meta0, vt.meta1 = v.codes, v.meta0, v.meta1
+    assert call(k, vt) == 7                  # token counts differ
 
 
 def test_binding_has_no_cpu_path():
