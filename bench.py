@@ -21,7 +21,9 @@ After the timed region, "extras" times the rows beyond the bulk step on the same
 unpack_paged of K with page-local groups (16-token pages of a pool that interleaves K and V per
 page, so the page stride is padded), and store_rows / load_rows of 16384 rows into and out of
 a 131072-slot cache, and the BF16 window (first 4 / latest 16 rows raw) around INT4 G64 K
-pack and residual encode/decode. Algorithmic bytes per element for a row format with c code bytes and
+pack and residual encode/decode, and decode attention of 64 query heads over the packed K/V
+(INT4 G64 with and without one fused residual, NVFP4 G16), whose algorithmic bytes are the
+packed planes it reads. Algorithmic bytes per element for a row format with c code bytes and
 m = block-scale bytes + 4/D row-scale bytes per element: pack and unpack 2 + c + m, residual
 encode and decode 4 + c + m; page-local INT4 G16 K 2.75; a slot write or read of N rows moves
 N*H*D*(2 + c + m) bytes plus 4 B per slot id; a windowed op moves the codec bytes of its
@@ -115,6 +117,22 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
         ("int4-key-window_decode_residual", nmid * 4.5625 + nwin,
          lambda: kvq.decode_window(wr, previous=x0, out=wout)),
     ]
+    # decode attention over the packed cache: 64 query heads (GQA 8) over all T tokens, K/V
+    # reconstructed in registers; algorithmic bytes = the packed K and V planes (+ residuals)
+    Hq = 64
+    qv = torch.randn((Hq, D), generator=torch.Generator(device="cpu").manual_seed(3)).to(torch.bfloat16).to(dev)
+    aout = torch.empty((Hq, D), dtype=torch.float32, device=dev)
+    for fmt, G in (("int4", 64), ("nvfp4", 16)):
+        pk = kvq.pack(x0, "key", fmt, G)
+        pv = kvq.pack(X["value"][0], "value", fmt, G)
+        pbytes = pk.nbytes() + pv.nbytes()
+        calls.append((f"{fmt}-decode_attention-Hq64", pbytes,
+                      lambda pk=pk, pv=pv: kvq.decode_attention(qv, pk, pv, out=aout)))
+        if fmt == "int4":
+            rk = kvq.encode_residual(x1, kvq.unpack(pk), "key", fmt, G)
+            rv = kvq.encode_residual(X["value"][1], kvq.unpack(pv), "value", fmt, G)
+            calls.append((f"{fmt}-decode_attention-residual-Hq64", pbytes + rk.nbytes() + rv.nbytes(),
+                          lambda pk=pk, pv=pv, rk=rk, rv=rv: kvq.decode_attention(qv, pk, pv, rk, rv, out=aout)))
     # slot writes and reads: 16384 rows into / out of a 131072-slot cache
     N = min(16384, T)
     g = torch.Generator(device="cpu").manual_seed(7)

@@ -33,10 +33,15 @@ FLAGS = [
     "-I", CSRC,
 ]
 
+# Attention keeps its MFMA accumulators in ordinary VGPRs: the online softmax rescales them with
+# vector instructions, and accumulators in AGPRs would be copied out and back on every tile.
+SOURCE_FLAGS = {"kvq_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
-def _compile(src: str, build_dir: str, defines=()) -> str:
+
+def _compile(src: str, build_dir: str, defines=(), flags=None) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *("-D" + d for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = SOURCE_FLAGS.get(src, []) if flags is None else flags.get(src, [])
+    cmd = [HIPCC, *FLAGS, *extra, *("-D" + d for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -49,13 +54,14 @@ def _compile(src: str, build_dir: str, defines=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=(), flags=None) -> str:
     """Compile every source and link the library (default ``libkvq.so`` in the package
-    directory; ``out``/``defines`` build a variant elsewhere). Always rebuilds."""
+    directory; ``out``/``defines``/``flags`` (per-source extra flags in place of
+    ``SOURCE_FLAGS``) build a variant elsewhere). Always rebuilds."""
     build_dir = os.path.join(PKG, "_build") if out == LIB else out + ".build"
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines, flags), SOURCES))
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -2,6 +2,8 @@
 // stream. Nothing here allocates, frees or synchronizes.
 #include <string.h>
 
+#include <algorithm>
+
 #include "kvq.h"
 #include "kvq_launch.hpp"
 
@@ -376,23 +378,22 @@ kvq_tensor row_slice(const kvq_tensor* x, int64_t r0, int64_t n) {
     return v;
 }
 
-// Token split of decode attention: blocks of a multiple of 64 tokens, about 2048 blocks in all.
-void attn_split(int64_t T, int64_t H, int32_t* n_split, int64_t* tc) {
-    const int64_t target = (2048 / (H > 0 ? H : 1)) > 0 ? 2048 / (H > 0 ? H : 1) : 1;
-    int64_t per = cdiv(T > 0 ? T : 1, 64 * target);
-    *tc = 64 * (per > 0 ? per : 1);
-    *n_split = (int32_t)cdiv(T > 0 ? T : 1, *tc);
+// Token blocks of decode attention per KV head, at most: blocks of at least 64 tokens, never
+// more than KVQ_ATTN_MAX_SPLIT per head (the combine kernel's bound). The launcher picks the
+// split it runs (one round of resident blocks on the device) within this bound, which sizes the
+// workspace.
+int32_t attn_split_bound(int64_t T, int64_t H) {
+    const int64_t per_head = KVQ_ATTN_MAX_SPLIT / (H > 0 ? H : 1);
+    const int64_t n = std::min<int64_t>(per_head > 0 ? per_head : 1, cdiv(T > 0 ? T : 1, 64));
+    return (int32_t)n;
 }
 
 size_t attn_workspace(int64_t T, int64_t H, int64_t rep) {
-    int32_t ns;
-    int64_t tc;
-    attn_split(T, H, &ns, &tc);
-    return (size_t)H * ns * rep * (KVQ_ATTN_D + 2) * sizeof(float);
+    return (size_t)H * attn_split_bound(T, H) * rep * (KVQ_ATTN_D + 2) * sizeof(float);
 }
 
 // One packed tensor of an attention call: dense, the expected kind, head_dim 128, and a group
-// size the kernel's tiling takes (INT4 K: G % 16 == 0; INT4 V: G % 8 == 0 and G | 128).
+// size the kernel's tiling takes (INT4: a power of two, K at least 16, V from 8 to 128).
 kvq_status attn_operand(const kvq_packed* p, int kind, int64_t T, int64_t H, AttnPlanes* out) {
     kvq_status st = check_packed(p);
     if (st) return st;
@@ -402,13 +403,14 @@ kvq_status attn_operand(const kvq_packed* p, int kind, int64_t T, int64_t H, Att
     if (p->rows != T || p->H != H) return KVQ_ERR_MISMATCH;
     const int32_t G = p->group_size;
     if (p->format == KVQ_INT4) {
-        if (kind == KVQ_KEY ? (G % 16 != 0) : (G % 8 != 0 || KVQ_ATTN_D % G != 0)) return KVQ_ERR_GROUP;
+        // powers of two: a K group holds whole 16-token sub-tiles, a V group whole 8-channel lanes
+        if (!is_pow2(G) || (kind == KVQ_KEY ? G < 16 : (G < 8 || G > KVQ_ATTN_D))) return KVQ_ERR_GROUP;
         if (!aligned(p->meta0, 16) || !aligned(p->meta1, 16)) return KVQ_ERR_LAYOUT;
     } else if (!aligned(p->meta0, 16)) {
         return KVQ_ERR_LAYOUT;
     }
     if (!aligned(p->codes, 16)) return KVQ_ERR_LAYOUT;
-    *out = AttnPlanes{p->codes, p->meta0, p->meta1, p->global_scale, G};
+    *out = AttnPlanes{p->codes, p->meta0, p->meta1, p->global_scale, log2i(G)};
     return KVQ_OK;
 }
 
@@ -671,10 +673,9 @@ kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, 
     a.T = T;
     a.H = (int32_t)H;
     a.rep = (int32_t)rep;
-    attn_split(T, H, &a.n_split, &a.tc);
+    a.n_split = attn_split_bound(T, H);  // the launcher chooses the split within this bound
     a.qscale = softmax_scale * 1.4426950408889634f;  // scores in log2 units: exp(x) = exp2(x log2 e)
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = a.part_o + (size_t)H * a.n_split * rep * KVQ_ATTN_D;
+    a.part_o = static_cast<float*>(workspace);      // the launcher places part_ml after its split
     a.out = out;
     return hip_status(launch_attention(k->format, rfmt, a, stream));
 }

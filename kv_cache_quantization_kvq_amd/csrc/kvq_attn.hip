@@ -21,6 +21,8 @@
 // holds S[row l % 16][token 4q + j], which is exactly the B operand P^T of O^T = V^T P^T; there
 // A = V^T (lane: channels 8 (l % 16) + N of the output tile N, tokens 4q + j, one 4-byte load per
 // token), and the accumulator holds O[row l % 16][channel 32q + 8j + N].
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "kvq_launch.hpp"
@@ -46,75 +48,200 @@ __device__ __forceinline__ float lane_max(float v) {
 template <bool ON>
 using TableT = std::conditional_t<ON, Fp4Table, char>;
 
-// --- K: 32 channels (32q .. 32q + 31) of one token, as 8 MFMA operands (4 channels each) ---
+// --- K metadata in LDS ---------------------------------------------------------------------
+//
+// A K group's metadata is shared by all its tokens: each wave keeps the current group's (and,
+// loaded one sub-tile ahead, the next group's) metadata of its KV head in two LDS slots of 512
+// bytes. INT4: 128 f16 minimums, then 128 f16 scales; NVFP4: the 128 decoded f32 block scales
+// e4m3(s) / g of one 16-token block. Lane group q reads its 32 channels with broadcast reads.
+constexpr int kMetaWords = 128;  // 32-bit words per slot
 
-// Decoded bf16 values of the lane's 32 K channels for token t, one float per channel.
+// The lane's share of one group's metadata on its way to LDS (lanes 0..31 only).
+struct MetaStage {
+    u2_t w;
+};
+
 template <int FMT>
-__device__ __forceinline__ void k_values(const AttnPlanes& p, const Fp4Table* tab, int64_t t, int H, int h, int q,
-                                        float (&y)[32]) {
-    const size_t row = (size_t)t * H + h;
-    const u32x4 cw = *reinterpret_cast<const u32x4*>(p.codes + row * (kD / 2) + 16 * q);
-    const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+__device__ __forceinline__ void meta_fetch(const AttnPlanes& p, int64_t t0, int H, int h, int lane, MetaStage& m) {
+    m.w = (u2_t){0u, 0u};
     if constexpr (FMT == FMT_INT4) {
-        const size_t mb = ((size_t)(t / p.G) * H + h) * kD + 32 * q;
-        const u32x4* mn = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.meta0) + mb);
-        const u32x4* sc = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.meta1) + mb);
+        const size_t row = ((size_t)(t0 >> p.gshift) * H + h) * kD;  // f16 elements
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(lane < 32 ? p.meta0 : p.meta1) + row;
+        m.w = *reinterpret_cast<const u2_t*>(src + 4 * (lane & 31));
+    } else {
+        if (lane < 32) m.w.x = reinterpret_cast<const uint32_t*>(
+                               reinterpret_cast<const uint8_t*>(p.meta0) + ((size_t)(t0 >> 4) * H + h) * kD)[lane];
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void meta_store(uint32_t* slot, const MetaStage& m, int lane, const Fp4Table* tab) {
+    if constexpr (FMT == FMT_INT4) {
+        reinterpret_cast<u2_t*>(slot)[lane] = m.w;  // lane l: words 2l, 2l + 1
+    } else if (lane < 32) {
+        const uint32_t b = m.w.x;  // scale bytes of channels 4 lane .. 4 lane + 3
+        const u32x4 f = {__float_as_uint(tab->e[b & 0x7Fu][0]), __float_as_uint(tab->e[(b >> 8) & 0x7Fu][0]),
+                         __float_as_uint(tab->e[(b >> 16) & 0x7Fu][0]), __float_as_uint(tab->e[(b >> 24) & 0x7Fu][0])};
+        reinterpret_cast<u32x4*>(slot)[lane] = f;
+    }
+}
+
+// --- raw loads (issued one sub-tile ahead) and in-register decoding ---
+
+// Codes of one sub-tile for this lane: K of token l % 16, channels 32q .. 32q + 31 (16 bytes);
+// V of tokens 4q + j, channels 8r .. 8r + 7 (4 bytes each) with their group's metadata
+// (INT4: f16 scale << 16 | f16 minimum; NVFP4: the E4M3 block-scale byte).
+struct TileRaw {
+    u32x4 kc;
+    uint32_t vc[4];
+    uint32_t vm[4];
+};
+
+// Loop-invariant lane byte offsets of one packed tensor (K codes of token l % 16, channel
+// group q; V codes and metadata of tokens 4q + j, channels 8r .. 8r + 7), relative to the
+// sub-tile's first row, whose addresses are wave-uniform.
+struct LaneOffsets {
+    uint32_t kc;
+    uint32_t vc[4], vm[4];
+};
+
+template <int FMT>
+__device__ __forceinline__ void lane_offsets(const AttnPlanes& pk, const AttnPlanes& pv, int H, int h, int r, int q,
+                                             int64_t dt_k, const int64_t (&dt_v)[4], LaneOffsets& o) {
+    o.kc = (uint32_t)(((uint64_t)dt_k * H + h) * (kD / 2) + 16 * q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {  // word i: channels 8i .. 8i + 7
-            const u32x4 m4 = mn[i], s4 = sc[i];
-            const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
-            const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t row = (uint64_t)dt_v[j] * H + h;
+        o.vc[j] = (uint32_t)(row * (kD / 2) + 4 * r);
+        if constexpr (FMT == FMT_INT4)  // f16 entries [row][channel group]
+            o.vm[j] = (uint32_t)(2 * ((row << (7 - pv.gshift)) + ((8u * r) >> pv.gshift)));
+        else  // E4M3 bytes [row][16-channel block]
+            o.vm[j] = (uint32_t)(row * (kD / 16) + (r >> 1));
+    }
+}
+
+// A wave-uniform global address kept in SGPRs and opaque to the optimizer, so that a lane's
+// 32-bit byte offset is added by the load itself (the scalar-base form of global loads).
+typedef const __attribute__((address_space(1))) uint8_t* gptr;
+
+__device__ __forceinline__ gptr sbase(const void* p, size_t off) {
+    const uint64_t v = reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(p) + off);
+    // readfirstlane returns a signed int: widen through uint32_t, never by sign extension
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+    gptr b = (gptr)u;
+    asm("" : "+s"(b));
+    return b;
+}
+
+template <class T>
+__device__ __forceinline__ T ld_at(gptr base, uint32_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(1))) T*>(base + off);
+}
+
+template <class T>
+__device__ __forceinline__ T ld_nt_at(gptr base, uint32_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) T*>(base + off));
+}
+
+template <int FMT>
+__device__ __forceinline__ void tile_load(const AttnPlanes& pk, const AttnPlanes& pv, int64_t t0, int H,
+                                          const LaneOffsets& o, TileRaw& x) {
+    const size_t crow = (size_t)t0 * H * (kD / 2);
+    x.kc = ld_nt_at<u32x4>(sbase(pk.codes, crow), o.kc);
+    gptr vcb = sbase(pv.codes, crow);
+    if constexpr (FMT == FMT_INT4) {
+        const size_t g = 2 * ((size_t)t0 * H << (7 - pv.gshift));
+        gptr mb = sbase(pv.meta0, g);
+        gptr sb = sbase(pv.meta1, g);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {  // byte b: channels 8i + 2b, 8i + 2b + 1
-                const float c0 = (float)((lo >> (8 * b)) & 0xFFu), c1 = (float)((hi >> (8 * b)) & 0xFFu);
-                y[8 * i + 2 * b] = int4_value_f(c0, f16_to_f32(ss[b] & 0xFFFFu), f16_to_f32(mm[b] & 0xFFFFu));
-                y[8 * i + 2 * b + 1] = int4_value_f(c1, f16_to_f32(ss[b] >> 16), f16_to_f32(mm[b] >> 16));
-            }
+        for (int j = 0; j < 4; ++j) {
+            x.vc[j] = ld_nt_at<uint32_t>(vcb, o.vc[j]);
+            x.vm[j] = (uint32_t)ld_at<uint16_t>(mb, o.vm[j]) | ((uint32_t)ld_at<uint16_t>(sb, o.vm[j]) << 16);
         }
     } else {
-        const size_t sb = ((size_t)(t / 16) * H + h) * kD + 32 * q;
-        const u32x4* s8 = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.meta0) + sb);
-        const u32x4 sa = s8[0], sbv = s8[1];
-        const uint32_t sw[8] = {sa.x, sa.y, sa.z, sa.w, sbv.x, sbv.y, sbv.z, sbv.w};
+        gptr mb = sbase(pv.meta0, (size_t)t0 * H * (kD / 16));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x2 e0 = e2m1_values<0>(w[i]), e1 = e2m1_values<1>(w[i]);
-            const f32x2 e2 = e2m1_values<2>(w[i]), e3 = e2m1_values<3>(w[i]);
-            const float e[8] = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = 8 * i + k;
-                const uint32_t code = (sw[c >> 2] >> (8 * (c & 3))) & 0x7Fu;
-                y[c] = __fmul_rn(e[k], tab->e[code][0]);
-            }
+        for (int j = 0; j < 4; ++j) {
+            x.vc[j] = ld_nt_at<uint32_t>(vcb, o.vc[j]);
+            x.vm[j] = ld_at<uint8_t>(mb, o.vm[j]);
         }
     }
 }
 
-// --- V: channels 8m .. 8m + 7 of one token ---
+// Keep the optimizer from merging the nibble masks into the byte extraction, so that the four
+// bytes convert with v_cvt_f32_ubyte0..3.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
 
+// The lane's 8 decoded K values of word i (channels 32q + 8i .. 32q + 8i + 7) from the LDS slot.
 template <int FMT>
-__device__ __forceinline__ void v_values(const AttnPlanes& p, const Fp4Table* tab, int64_t t, int H, int h, int m,
-                                        float (&y)[8]) {
-    const size_t row = (size_t)t * H + h;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p.codes + row * (kD / 2) + 4 * m);
+__device__ __forceinline__ void k_decode8(uint32_t w, const uint32_t* slot, int q, int i, float (&y)[8]) {
     if constexpr (FMT == FMT_INT4) {
-        const size_t mi = row * (size_t)(kD / p.G) + (8 * m) / p.G;
-        const float s = f16_to_f32(reinterpret_cast<const uint16_t*>(p.meta1)[mi]);
-        const float mn = f16_to_f32(reinterpret_cast<const uint16_t*>(p.meta0)[mi]);
-        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+        const u32x4 m4 = reinterpret_cast<const u32x4*>(slot)[4 * q + i];
+        const u32x4 s4 = reinterpret_cast<const u32x4*>(slot + kMetaWords / 2)[4 * q + i];
+        const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+        const uint32_t lo = opaque(w & 0x0F0F0F0Fu), hi = opaque((w >> 4) & 0x0F0F0F0Fu);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            y[2 * b] = int4_value_f((float)((lo >> (8 * b)) & 0xFFu), s, mn);
-            y[2 * b + 1] = int4_value_f((float)((hi >> (8 * b)) & 0xFFu), s, mn);
+            const float c0 = (float)((lo >> (8 * b)) & 0xFFu), c1 = (float)((hi >> (8 * b)) & 0xFFu);
+            y[2 * b] = int4_value_f(c0, f16_to_f32(ss[b] & 0xFFFFu), f16_to_f32(mm[b] & 0xFFFFu));
+            y[2 * b + 1] = int4_value_f(c1, f16_to_f32(ss[b] >> 16), f16_to_f32(mm[b] >> 16));
         }
     } else {
-        const uint32_t code = reinterpret_cast<const uint8_t*>(p.meta0)[row * (kD / 16) + (m >> 1)] & 0x7Fu;
-        const float s_dec = tab->e[code][0];
+        const u32x4 f0 = reinterpret_cast<const u32x4*>(slot)[8 * q + 2 * i];
+        const u32x4 f1 = reinterpret_cast<const u32x4*>(slot)[8 * q + 2 * i + 1];
+        const float sd[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
+                             __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
+                             __uint_as_float(f1.z), __uint_as_float(f1.w)};
         const f32x2 e0 = e2m1_values<0>(w), e1 = e2m1_values<1>(w), e2 = e2m1_values<2>(w), e3 = e2m1_values<3>(w);
         const float e[8] = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(e[k], s_dec);
+        for (int n = 0; n < 8; ++n) y[n] = __fmul_rn(e[n], sd[n]);
+    }
+}
+
+// V of one sub-tile prepared for decoding: the masked nibble words (INT4: low nibbles of the
+// four tokens' words, then high) or the raw words (NVFP4), with each token's scale and minimum.
+struct VPrep {
+    uint32_t w[8];
+    float s[4], m[4];
+};
+
+template <int FMT>
+__device__ __forceinline__ void v_prep(const TileRaw& x, const Fp4Table* tab, VPrep& v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (FMT == FMT_INT4) {
+            v.w[j] = opaque(x.vc[j] & 0x0F0F0F0Fu);
+            v.w[4 + j] = opaque((x.vc[j] >> 4) & 0x0F0F0F0Fu);
+            v.m[j] = f16_to_f32(x.vm[j] & 0xFFFFu);
+            v.s[j] = f16_to_f32(x.vm[j] >> 16);
+        } else {
+            v.w[j] = x.vc[j];
+            v.s[j] = tab->e[x.vm[j] & 0x7Fu][0];
+        }
+    }
+}
+
+// The decoded V values of channel 8r + n for the four tokens.
+template <int FMT>
+__device__ __forceinline__ void v_decode_n(const VPrep& v, int n, float (&y)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (FMT == FMT_INT4) {
+            const uint32_t w = v.w[(n & 1) ? 4 + j : j];  // nibble n: byte n / 2, low or high half
+            y[j] = int4_value_f((float)((w >> (8 * (n >> 1))) & 0xFFu), v.s[j], v.m[j]);
+        } else {
+            const f32x2 e = (n >> 1) == 0   ? e2m1_values<0>(v.w[j])
+                            : (n >> 1) == 1 ? e2m1_values<1>(v.w[j])
+                            : (n >> 1) == 2 ? e2m1_values<2>(v.w[j])
+                                            : e2m1_values<3>(v.w[j]);
+            y[j] = __fmul_rn(e[n & 1], v.s[j]);
+        }
     }
 }
 
@@ -132,6 +259,115 @@ __device__ __forceinline__ s4_t as_s4(uint32_t lo, uint32_t hi) {
     return __builtin_bit_cast(s4_t, v);
 }
 
+// Raw data of one 16-token sub-tile (base and, for a residual, the residual planes).
+template <bool RES>
+struct SubRaw {
+    TileRaw b;
+    std::conditional_t<RES, TileRaw, char> r;
+};
+
+// Per-wave running state of the online softmax. m is the offset subtracted from the scores
+// (log2 units) before exp2; it is raised only when a score passes it by more than kLazy, so
+// that the accumulators are rarely rescaled and every p stays below 2^kLazy.
+constexpr float kLazy = 8.0f;
+struct WaveState {
+    float m, l;
+    f4_t o[8];
+};
+
+// Offsets of every tensor of a call for one sub-tile: `full` sub-tiles use the precomputed
+// lane offsets; the last, partial one clamps its tokens to the final row first.
+template <int RFMT>
+struct CallOffsets {
+    LaneOffsets b, r;
+};
+
+template <int FMT, int RFMT>
+__device__ __forceinline__ void call_offsets(const AttnArgs& a, int h, int r, int q, int64_t t0, int64_t t_end,
+                                             CallOffsets<RFMT>& o) {
+    const int64_t last = t_end - 1 - t0;  // offset of the final row from t0
+    const int64_t dk = min<int64_t>(r, last);
+    int64_t dv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dv[j] = min<int64_t>(4 * q + j, last);
+    lane_offsets<FMT>(a.k, a.v, a.H, h, r, q, dk, dv, o.b);
+    if constexpr (RFMT != kNone) lane_offsets<RFMT>(a.rk, a.rv, a.H, h, r, q, dk, dv, o.r);
+}
+
+template <int FMT, int RFMT>
+__device__ __forceinline__ void sub_load(const AttnArgs& a, int64_t t0, const CallOffsets<RFMT>& o,
+                                         SubRaw<RFMT != kNone>& s) {
+    tile_load<FMT>(a.k, a.v, t0, a.H, o.b, s.b);
+    if constexpr (RFMT != kNone) tile_load<RFMT>(a.rk, a.rv, t0, a.H, o.r, s.r);
+}
+
+template <int FMT, int RFMT, bool TAIL>
+__device__ __forceinline__ void sub_compute(const AttnArgs& a, int n_valid, int q, const uint32_t (&qw)[16],
+                                            const SubRaw<RFMT != kNone>& s, const uint32_t* kslot,
+                                            const uint32_t* rkslot, const Fp4Table* ptv, const Fp4Table* ptrv,
+                                            WaveState& st) {
+    constexpr bool RES = RFMT != kNone;
+    // ---- scores S^T = K Q^T, 8 channels (two MFMA steps) at a time ----
+    f4_t sacc = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t kw[4] = {s.b.kc.x, s.b.kc.y, s.b.kc.z, s.b.kc.w};
+    uint32_t rw[4] = {0u, 0u, 0u, 0u};
+    if constexpr (RES) {
+        rw[0] = s.r.kc.x; rw[1] = s.r.kc.y; rw[2] = s.r.kc.z; rw[3] = s.r.kc.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float kv[8], kr[8];
+        k_decode8<FMT>(kw[i], kslot, q, i, kv);
+        if constexpr (RES) k_decode8<RFMT>(rw[i], rkslot, q, i, kr);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int c = 4 * h2, st4 = 2 * i + h2;
+            const uint32_t k01 = rebuild2(kv[c], kv[c + 1], RES ? kr[c] : 0.0f, RES ? kr[c + 1] : 0.0f, RES);
+            const uint32_t k23 = rebuild2(kv[c + 2], kv[c + 3], RES ? kr[c + 2] : 0.0f, RES ? kr[c + 3] : 0.0f, RES);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s4(k01, k23), as_s4(qw[2 * st4], qw[2 * st4 + 1]),
+                                                             sacc, 0, 0, 0);
+        }
+    }
+    // ---- online softmax: lane holds S[row r][token t0 + 4q + j] ----
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[j] = (!TAIL || 4 * q + j < n_valid) ? sacc[j] * a.qscale : -__builtin_inff();
+    const float m_tile = lane_max(__builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3])));
+    const bool up = m_tile > st.m + kLazy;  // always for the first sub-tile (m = -inf; token 0 is valid)
+    if (__any(up)) {
+        const float m_new = up ? m_tile : st.m;
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 from m = -inf
+        st.l *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
+        st.m = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - st.m);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    const s4_t pb = as_s4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    // ---- O^T += V^T P^T, one 16-channel output tile (channel 8r + n of each lane) at a time ----
+    VPrep vb, vr;
+    v_prep<FMT>(s.b, ptv, vb);
+    if constexpr (RES) v_prep<RFMT>(s.r, ptrv, vr);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        float yb[4], yr[4];
+        v_decode_n<FMT>(vb, n, yb);
+        if constexpr (RES) v_decode_n<RFMT>(vr, n, yr);
+        const uint32_t v01 = rebuild2(yb[0], yb[1], RES ? yr[0] : 0.0f, RES ? yr[1] : 0.0f, RES);
+        const uint32_t v23 = rebuild2(yb[2], yb[3], RES ? yr[2] : 0.0f, RES ? yr[3] : 0.0f, RES);
+        st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s4(v01, v23), pb, st.o[n], 0, 0, 0);
+    }
+}
+
+// log2 of the tokens per K metadata group (NVFP4 K blocks are 16 tokens)
+template <int FMT>
+__device__ __forceinline__ int kgroup_shift(const AttnPlanes& p) {
+    return FMT == FMT_INT4 ? p.gshift : 4;
+}
+
 template <int FMT, int RFMT>
 __global__ __launch_bounds__(64 * kWaves) void k_attn_split(AttnArgs a) {
     constexpr bool RES = RFMT != kNone;
@@ -139,6 +375,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_attn_split(AttnArgs a) {
     __shared__ TableT<RFMT == FMT_NVFP4> trk, trv;
     __shared__ float s_o[kWaves][16][kD];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+    __shared__ uint32_t s_meta[kWaves][RES ? 4 : 2][kMetaWords];  // per wave: 2 slots (+2 residual)
     if constexpr (FMT == FMT_NVFP4) {
         fp4_table_fill(tk, *a.k.gscale);
         fp4_table_fill(tv, *a.v.gscale);
@@ -155,12 +392,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_attn_split(AttnArgs a) {
     if constexpr (RFMT == FMT_NVFP4) { ptrk = &trk; ptrv = &trv; }
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;  // query row of the group (and the K token / V channel-octet index)
     const int q = lane >> 4;
     const int h = blockIdx.y;
     const int64_t t_begin = (int64_t)blockIdx.x * a.tc;
     const int64_t t_end = min<int64_t>(a.T, t_begin + a.tc);
+    // each wave walks its own contiguous quarter of the block's tokens (a multiple of 16)
+    const int64_t w_len = a.tc / kWaves;
+    const int64_t w_begin = t_begin + (int64_t)wave * w_len;
+    const int64_t w_end = min<int64_t>(t_end, w_begin + w_len);
 
     // Q^T operand: row r (query head h * rep + r), channels 32q + 4s + j for step s
     uint32_t qw[16];
@@ -176,66 +417,87 @@ __global__ __launch_bounds__(64 * kWaves) void k_attn_split(AttnArgs a) {
         for (int i = 0; i < 16; ++i) qw[i] = 0u;
     }
 
-    float m_run = -__builtin_inff(), l_run = 0.0f;
-    f4_t o[8];
+    WaveState st;
+    st.m = -__builtin_inff();
+    st.l = 0.0f;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) o[n] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int n = 0; n < 8; ++n) st.o[n] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int64_t t0 = t_begin + (int64_t)wave * kSub; t0 < t_end; t0 += kWaves * kSub) {
-        // ---- scores S^T = K Q^T for tokens t0 .. t0 + 15 ----
-        const int64_t tk_ = min<int64_t>(t0 + r, t_end - 1);
-        float kv[32], kr[32];
-        k_values<FMT>(a.k, ptk, tk_, a.H, h, q, kv);
-        if constexpr (RES) k_values<RFMT>(a.rk, ptrk, tk_, a.H, h, q, kr);
-        f4_t sacc = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int c = 4 * s;
-            const uint32_t k01 = rebuild2(kv[c], kv[c + 1], RES ? kr[c] : 0.0f, RES ? kr[c + 1] : 0.0f, RES);
-            const uint32_t k23 = rebuild2(kv[c + 2], kv[c + 3], RES ? kr[c + 2] : 0.0f, RES ? kr[c + 3] : 0.0f, RES);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s4(k01, k23), as_s4(qw[2 * s], qw[2 * s + 1]), sacc, 0,
-                                                             0, 0);
+    const int ks = kgroup_shift<FMT>(a.k);
+    int rks = 0;
+    if constexpr (RES) rks = kgroup_shift<RFMT>(a.rk);
+    uint32_t* slots = &s_meta[wave][0][0];
+    auto kslot = [&](int64_t t) { return slots + ((t >> ks) & 1) * kMetaWords; };
+    auto rkslot = [&](int64_t t) { return slots + (2 + ((t >> rks) & 1)) * kMetaWords; };
+
+    // Full sub-tiles (all 16 tokens in range) run in the main loop with loop-invariant offsets;
+    // the block's last sub-tile may be partial and runs after it, its rows clamped to the last.
+    CallOffsets<RFMT> full;
+    call_offsets<FMT, RFMT>(a, h, r, q, 0, kSub, full);
+    const int64_t w_full = w_begin + ((w_end - w_begin) & ~(int64_t)(kSub - 1));
+
+    // One full sub-tile at t from `cur`: the next full sub-tile's codes (into `nxt`, with
+    // prefetching) and, where the next sub-tile opens a new K group, that group's metadata are
+    // fetched first; the metadata goes to its LDS slot (the one the current group does not use)
+    // afterwards.
+    auto step = [&](int64_t t, SubRaw<RES>& cur, SubRaw<RES>& nxt) {
+        const int64_t tn = t + kSub;
+        const bool more = tn < w_end;
+        const bool nk = more && (tn >> ks) != (t >> ks);
+        const bool nr = RES && more && (tn >> rks) != (t >> rks);
+        MetaStage mk, mr;
+        if (KVQ_ATTN_PREFETCH && tn < w_full) sub_load<FMT, RFMT>(a, tn, full, nxt);
+        if (!KVQ_ATTN_PREFETCH) sub_load<FMT, RFMT>(a, t, full, cur);
+        if (nk) meta_fetch<FMT>(a.k, tn, a.H, h, lane, mk);
+        if constexpr (RES) {
+            if (nr) meta_fetch<RFMT>(a.rk, tn, a.H, h, lane, mr);
         }
-        // ---- online softmax over this sub-tile: lane holds S[row r][token t0 + 4q + j] ----
-        float sc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sc[j] = (t0 + 4 * q + j < t_end) ? sacc[j] * a.qscale : -__builtin_inff();
-        const float m_tile = lane_max(__builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3])));
-        const float m_new = __builtin_fmaxf(m_run, m_tile);  // finite: token t0 is in range
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - m_new);
-        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m_run = m_new;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) o[n] *= alpha;
-        const s4_t pb = as_s4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-        // ---- O^T += V^T P^T: lane loads tokens t0 + 4q + j, channels 8r .. 8r + 7 ----
-        float vv[4][8], vr[4][8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t tv_ = min<int64_t>(t0 + 4 * q + j, t_end - 1);
-            v_values<FMT>(a.v, ptv, tv_, a.H, h, r, vv[j]);
-            if constexpr (RES) v_values<RFMT>(a.rv, ptrv, tv_, a.H, h, r, vr[j]);
+        __builtin_amdgcn_wave_barrier();
+        sub_compute<FMT, RFMT, false>(a, kSub, q, qw, cur, kslot(t), RES ? rkslot(t) : nullptr, ptv, ptrv, st);
+        if (nk) meta_store<FMT>(kslot(tn), mk, lane, ptk);
+        if constexpr (RES) {
+            if (nr) meta_store<RFMT>(rkslot(tn), mr, lane, ptrk);
         }
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            const uint32_t v01 = rebuild2(vv[0][n], vv[1][n], RES ? vr[0][n] : 0.0f, RES ? vr[1][n] : 0.0f, RES);
-            const uint32_t v23 = rebuild2(vv[2][n], vv[3][n], RES ? vr[2][n] : 0.0f, RES ? vr[3][n] : 0.0f, RES);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s4(v01, v23), pb, o[n], 0, 0, 0);
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    int64_t t0 = w_begin;
+    SubRaw<RES> A, B;
+    if (t0 < w_end) {
+        MetaStage m;
+        meta_fetch<FMT>(a.k, t0, a.H, h, lane, m);
+        meta_store<FMT>(kslot(t0), m, lane, ptk);
+        if constexpr (RES) {
+            meta_fetch<RFMT>(a.rk, t0, a.H, h, lane, m);
+            meta_store<RFMT>(rkslot(t0), m, lane, ptrk);
         }
+    }
+    if (KVQ_ATTN_PREFETCH && t0 < w_full) sub_load<FMT, RFMT>(a, t0, full, A);
+    while (t0 < w_full) {  // unrolled twice so that the two raw buffers swap roles for free
+        step(t0, A, B);
+        t0 += kSub;
+        if (t0 >= w_full) break;
+        step(t0, B, A);
+        t0 += kSub;
+    }
+    if (t0 < w_end) {  // the partial sub-tile (its group's metadata is already in place)
+        CallOffsets<RFMT> tail;
+        call_offsets<FMT, RFMT>(a, h, r, q, t0, w_end, tail);
+        sub_load<FMT, RFMT>(a, t0, tail, A);
+        __builtin_amdgcn_wave_barrier();
+        sub_compute<FMT, RFMT, true>(a, (int)(w_end - t0), q, qw, A, kslot(t0), RES ? rkslot(t0) : nullptr, ptv,
+                                     ptrv, st);
     }
 
     // ---- fold the block's 4 waves: lane holds O[row r][channel 32q + 8j + n] ----
-    float l_row = l_run + __shfl_xor(l_run, 16);  // the row's 4 lanes share m_run
+    float l_row = st.l + __shfl_xor(st.l, 16);  // the row's 4 lanes share m
     l_row += __shfl_xor(l_row, 32);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s_o[wave][r][32 * q + 8 * j + n] = o[n][j];
+        for (int j = 0; j < 4; ++j) s_o[wave][r][32 * q + 8 * j + n] = st.o[n][j];
     if (q == 0) {
-        s_m[wave][r] = m_run;  // -inf for a wave without tokens (then l = 0 and O = 0)
+        s_m[wave][r] = st.m;  // -inf for a wave without tokens (then l = 0 and O = 0)
         s_l[wave][r] = l_row;
     }
     __syncthreads();
@@ -260,33 +522,112 @@ __global__ __launch_bounds__(64 * kWaves) void k_attn_split(AttnArgs a) {
     }
 }
 
-// out[hq][c] = sum_s O_s e^(m_s - M) / sum_s l_s e^(m_s - M) over the blocks' partials.
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int Hq = a.H * a.rep;
-    if (idx >= (int64_t)Hq * kD) return;
-    const int hq = (int)(idx / kD), c = (int)(idx - (int64_t)hq * kD);
-    const int h = hq / a.rep, row = hq - h * a.rep;
-    float M = -__builtin_inff();
-    for (int s = 0; s < a.n_split; ++s)
-        M = __builtin_fmaxf(M, a.part_ml[(((size_t)h * a.n_split + s) * a.rep + row) * 2]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < a.n_split; ++s) {
-        const size_t pi = ((size_t)h * a.n_split + s) * a.rep + row;
-        const float f = __builtin_amdgcn_exp2f(a.part_ml[pi * 2] - M);
-        L += a.part_ml[pi * 2 + 1] * f;
-        O += a.part_o[pi * kD + c] * f;
+// out[hq][c] = sum_s O_s e^(m_s - M) / sum_s l_s e^(m_s - M) over the blocks' partials. One
+// block per query head: the weights are spread over the 256 threads, then 8 groups of 32
+// threads (4 channels each, 512-byte rows) sum every 8th partial.
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* s_w) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_xor(v, d);
+        v = is_max ? __builtin_fmaxf(v, o) : v + o;
     }
-    a.out[idx] = O / L;
+    __syncthreads();  // s_w may still be read by a previous reduction
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = s_w[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v = is_max ? __builtin_fmaxf(v, s_w[w]) : v + s_w[w];
+    return v;
 }
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+    constexpr int kPer = KVQ_ATTN_MAX_SPLIT / 256;  // partials per thread in the weight pass
+    __shared__ float s_f[KVQ_ATTN_MAX_SPLIT];
+    __shared__ float s_w[4];
+    __shared__ f4v s_o[8][32];
+    const int hq = blockIdx.x;
+    const int h = hq / a.rep, row = hq - h * a.rep;
+    const int tid = threadIdx.x;
+    const size_t base = (size_t)h * a.n_split * a.rep + row;  // partial index of split 0
+    const size_t step = (size_t)a.rep;                       // partial index step per split
+    const float* ml = a.part_ml + base * 2;
+
+    float mv[kPer], lv[kPer];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int s = tid + 256 * i;
+        mv[i] = -__builtin_inff();
+        lv[i] = 0.0f;
+        if (s < a.n_split) {
+            mv[i] = ml[s * step * 2];
+            lv[i] = ml[s * step * 2 + 1];
+        }
+        m = __builtin_fmaxf(m, mv[i]);
+    }
+    const float M = block_reduce(m, true, s_w);
+    float l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int s = tid + 256 * i;
+        const float f = (mv[i] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mv[i] - M);
+        if (s < a.n_split) s_f[s] = f;
+        l += lv[i] * f;
+    }
+    const float L = block_reduce(l, false, s_w);  // its barriers also publish s_f
+
+    const int c4 = tid & 31, sl = tid >> 5;  // channels 4 c4 .. 4 c4 + 3; splits sl, sl + 8, ...
+    const f4v* po = reinterpret_cast<const f4v*>(a.part_o + base * kD) + c4;
+    f4v o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int s = sl; s < a.n_split; s += 8) o += s_f[s] * po[s * step * (kD / 4)];
+    s_o[sl][c4] = o;
+    __syncthreads();
+    if (sl == 0) {
+        f4v t = s_o[0][c4];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) t += s_o[i][c4];
+        reinterpret_cast<f4v*>(a.out + (size_t)hq * kD)[c4] = t / L;
+    }
+}
+
+// Resident blocks of a kernel on the current device (compute units x blocks per unit), cached
+// per device for each kernel.
 template <int FMT, int RFMT>
-hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
+int resident_blocks() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_attn_split<FMT, RFMT>, 64 * kWaves, 0) != hipSuccess)
+        return 0;
+    n = cus * per;
+    if (n > 0) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// The split of one call: as many blocks per KV head as fill the device once (within the bound the
+// workspace was sized for), each a multiple of 64 tokens.
+template <int FMT, int RFMT>
+hipError_t attn_launch(AttnArgs a, hipStream_t s) {
+    const int32_t bound = a.n_split;
+    if (bound < 1 || bound > KVQ_ATTN_MAX_SPLIT) return hipErrorInvalidValue;  // combine's weight table
+    const int resident = resident_blocks<FMT, RFMT>();
+    const int64_t want = resident > 0 ? std::max<int64_t>(1, resident / a.H) : bound;
+    const int64_t splits = std::min<int64_t>(want, bound);
+    const int64_t per = (a.T + 64 * splits - 1) / (64 * splits);
+    a.tc = 64 * per;
+    a.n_split = (int32_t)((a.T + a.tc - 1) / a.tc);  // <= splits
+    a.part_ml = a.part_o + (size_t)a.H * a.n_split * a.rep * kD;
     hipLaunchKernelGGL((k_attn_split<FMT, RFMT>), dim3(a.n_split, a.H), dim3(64 * kWaves), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const uint64_t n = (uint64_t)a.H * a.rep * kD;
-    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(a.H * a.rep)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -302,10 +302,12 @@ __device__ __forceinline__ uint32_t int4_code(float x, const Int4Group& g) {
     return (uint32_t)c;
 }
 
-// INT4 decode before the final rounding to bf16: fl(fl(c * scale16) + min16).
-__device__ __forceinline__ float int4_value_f(float c, float s16, float m16) {
-    return __fadd_rn(__fmul_rn(c, s16), m16);
-}
+// INT4 decode before the final rounding to bf16: fl(fl(c * scale16) + min16). For a code
+// c in 0..15 and a scale widened from f16 (at most 11 significant bits, never below 2^-24 unless
+// zero) the product c * scale16 has at most 15 significant bits and is exact in FP32, so one
+// FMA gives the same result as the multiply and the add (the device probe checks the product
+// for every code and every finite f16).
+__device__ __forceinline__ float int4_value_f(float c, float s16, float m16) { return __builtin_fmaf(c, s16, m16); }
 __device__ __forceinline__ float int4_value(uint32_t c, float s16, float m16) { return int4_value_f((float)c, s16, m16); }
 
 // ---- NVFP4 block constants ------------------------------------------------------------------

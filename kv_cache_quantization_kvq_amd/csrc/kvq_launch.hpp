@@ -104,20 +104,25 @@ struct CopyArgs {
 // Decode attention over packed K/V (head_dim 128; KVQ_ATTN_NO_RESIDUAL: no residual).
 #define KVQ_ATTN_D 128
 #define KVQ_ATTN_NO_RESIDUAL (-1)
+#define KVQ_ATTN_MAX_SPLIT 2048  // token blocks per KV head at most
 struct AttnPlanes {
     const uint8_t* codes;
     const void* meta0;
     const void* meta1;
     const float* gscale;
-    int32_t G;
+    int32_t gshift;  // log2 of the group size (INT4; NVFP4 blocks are 16)
 };
+// Load the next 16-token sub-tile's raw data before decoding the current one (1), or not (0).
+#ifndef KVQ_ATTN_PREFETCH
+#define KVQ_ATTN_PREFETCH 0
+#endif
 struct AttnArgs {
     const uint16_t* q;  // [H * rep, 128] bf16
     AttnPlanes k, v, rk, rv;
     int64_t T;
     int32_t H, rep;
-    int32_t n_split;
-    int64_t tc;         // tokens per block (a multiple of 64)
+    int32_t n_split;    // token blocks per KV head (on entry to the launcher: the bound)
+    int64_t tc;         // tokens per block (a multiple of 64), set by the launcher
     float qscale;       // softmax scale * log2(e)
     float* part_o;      // [H, n_split, rep, 128]
     float* part_ml;     // [H, n_split, rep, 2]

@@ -20,6 +20,9 @@
 //   [11] v_cvt_pk_fp8_f32 with kvq::e4m3_encode(|x|) plus the sign bit of x, every |x| <= 448
 //        (signed zeros included), in both halves of the packed word
 //   [12] v_cvt_pk_f32_fp8 with the signed kvq::e4m3_decode, every finite E4M3 code, both halves
+//   [14] for every INT4 code c (0..15) and every finite f16 scale s: c * f32(s) is exact in FP32
+//        (fma(c, s, -fl(c * s)) == 0), which makes kvq::int4_value_f's single FMA equal to the
+//        multiply-then-add; also kvq::int4_value_f(c, s, m) == fl(fl(c * s) + m) for 4 minimums
 // and, in a second kernel, the INT4 quotient kvq::int4_quot_raw(d, group(scale)) against the
 // IEEE d / scale for every scale significand (2^23) at eight exponents from 2^-100 to 2^99:
 //   [10] d = RN(m * scale) and its two neighbours for the 512 points m = h + k * ulp(h) / 2
@@ -41,7 +44,7 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kChecks = 14;
+constexpr int kChecks = 15;
 
 __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint32_t* first) {
     unsigned long long c[kChecks] = {};
@@ -113,6 +116,18 @@ __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint3
             for (uint32_t k = 0; k < 16u; ++k) {
                 const uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32((float)k, 2, 0xAABBCCDDu);
                 if (b != ((0xAABBCCDDu & 0xFF00FFFFu) | (k << 16))) { ++c[5]; f[5] = min(f[5], 0x100u + k); }
+            }
+        }
+        if (bits < (1u << 20)) {  // bits = c << 16 | f16 scale
+            const uint32_t cc = bits >> 16, hs = bits & 0xFFFFu;
+            if (((hs >> 10) & 31u) != 31u) {
+                const float sf = f16_to_f32(hs), cf = (float)cc;
+                const float prod = __fmul_rn(cf, sf);
+                bool bad = __builtin_fmaf(cf, sf, -prod) != 0.0f;
+                const float ms[4] = {0.0f, -0.0f, 1.5f, -3.0517578125e-05f};
+                for (int i = 0; i < 4; ++i)
+                    bad |= __float_as_uint(int4_value_f(cf, sf, ms[i])) != __float_as_uint(__fadd_rn(prod, ms[i]));
+                if (bad) { ++c[14]; f[14] = min(f[14], bits); }
             }
         }
         if (bits < 256u && (bits & 0x7Fu) != 0x7Fu) {

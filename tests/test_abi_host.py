@@ -226,6 +226,10 @@ def test_attention_argument_errors():
     assert lib.kvq_attention_workspace_bytes(0, 8, 64) == 0
     assert lib.kvq_attention_workspace_bytes(100, 8, 60) == 0
     assert lib.kvq_attention_workspace_bytes(131072, 8, 64) > 0
+    # one partial (128 outputs, max, sum) per query head and token block; at most 2048 blocks per KV head
+    for T, H, Hq in ((1, 1, 1), (64, 1, 16), (65, 2, 2), (1 << 20, 1, 1), (1 << 30, 1, 4), (1 << 22, 4096, 4096)):
+        n_split = lib.kvq_attention_workspace_bytes(T, H, Hq) // (Hq * 130 * 4)
+        assert 1 <= n_split <= max(1, 2048 // H) and n_split * 64 * (-(-T // (64 * n_split))) >= T
     k = _packed(format=0, kind=0, group_size=64, dtype=0, rows=256, H=2, D=128, full_T=256)
     v = _packed(format=0, kind=1, group_size=64, dtype=0, rows=256, H=2, D=128, full_T=256)
     for obj in (k, v):
@@ -243,7 +247,13 @@ def test_attention_argument_errors():
     assert call(k, v, wsb=16) == 9           # workspace too small
     k64 = _packed(format=0, kind=0, group_size=8, dtype=0, rows=256, H=2, D=128, full_T=256)
     k64.codes, k64.meta0, k64.meta1 = k.codes, k.meta0, k.meta1
-    assert call(k64, v) == 5                 # INT4 K groups must be a multiple of 16 tokens
+    assert call(k64, v) == 5                 # INT4 K groups: a power of two of at least 16 tokens
+    k48 = _packed(format=0, kind=0, group_size=48, dtype=0, rows=256, H=2, D=128, full_T=256)
+    k48.codes, k48.meta0, k48.meta1 = k.codes, k.meta0, k.meta1
+    assert call(k48, v) == 5                 # not a power of two
+    v4 = _packed(format=0, kind=1, group_size=4, dtype=0, rows=256, H=2, D=128, full_T=256)
+    v4.codes, v4.meta0, v4.meta1 = v.codes, v.meta0, v.meta1
+    assert call(k, v4) == 5                  # INT4 V groups: 8 to 128 channels
     k96 = _packed(format=0, kind=0, group_size=64, dtype=0, rows=256, H=2, D=96, full_T=256)
     k96.codes, k96.meta0, k96.meta1 = k.codes, k.meta0, k.meta1
     assert call(k96, v) == 2                 # head_dim 128 only

@@ -30,7 +30,7 @@ NAMES = ["bf16", "f16", "fp4 encode (all finite)", "fp4 encode (|x| <= 8)", "fp4
          "v_rcp_f32 within 1 ulp", "reciprocal + Newton step == RN(1/x)",
          "INT4 quotient (Markstein) == IEEE d / scale",
          "v_cvt_pk_fp8_f32 == E4M3 encode (|x| <= 448)", "v_cvt_pk_f32_fp8 == E4M3 decode",
-         "FP8-row quotient (Markstein) == IEEE x / scale"]
+         "FP8-row quotient (Markstein) == IEEE x / scale", "INT4 decode product exact (one FMA)"]
 
 
 def test_conversion_instructions_match_software_rounding():
