@@ -169,11 +169,13 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
     return out
 
 
+TRAFFIC_SOURCES = ("csrc/kvq_device.hpp", "csrc/kvq_encode.hip", "csrc/kvq_launch.hpp", "_build.py")
+
+
 def measured_traffic(kernel_name: str):
     """HBM bytes per launch of `kernel_name` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     runs (profiles/traffic.json, copy-kernel scaled), or None if those counters were taken on
     other kernel sources or for another kernel."""
-    import glob
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -182,9 +184,8 @@ def measured_traffic(kernel_name: str):
     with open(path) as f:
         rec = json.load(f)
     h = hashlib.sha256()
-    srcs = sorted(glob.glob(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc", "*")))
-    for p in srcs + [os.path.join(ROOT, "include", "kvq.h")]:
-        with open(p, "rb") as f:
+    for rel in TRAFFIC_SOURCES:  # the dominant kernel's translation unit and its build flags
+        with open(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", rel), "rb") as f:
             h.update(f.read())
     if rec.get("source_sha256") != h.hexdigest() or rec.get("kernel") != kernel_name:
         return None
