@@ -120,6 +120,14 @@ __device__ __forceinline__ void lane_offsets(const AttnPlanes& pk, const AttnPla
     }
 }
 
+// A value the optimizer must treat as unknown: it keeps nibble masks from merging into the byte
+// extraction (so the four bytes convert with v_cvt_f32_ubyte0..3) and offsets from being widened
+// outside a loop.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // A wave-uniform global address kept in SGPRs and opaque to the optimizer, so that a lane's
 // 32-bit byte offset is added by the load itself (the scalar-base form of global loads).
 typedef const __attribute__((address_space(1))) uint8_t* gptr;
@@ -135,14 +143,17 @@ __device__ __forceinline__ gptr sbase(const void* p, size_t off) {
     return b;
 }
 
+// (The offset passes through opaque() at the load so that its widening is not hoisted out of
+// the loop as a 64-bit register pair, which would cost the scalar-base form.)
 template <class T>
 __device__ __forceinline__ T ld_at(gptr base, uint32_t off) {
-    return *reinterpret_cast<const __attribute__((address_space(1))) T*>(base + off);
+    return *reinterpret_cast<const __attribute__((address_space(1))) T*>(base + opaque(off));
 }
 
 template <class T>
 __device__ __forceinline__ T ld_nt_at(gptr base, uint32_t off) {
-    return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) T*>(base + off));
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const __attribute__((address_space(1))) T*>(base + opaque(off)));
 }
 
 template <int FMT>
@@ -170,12 +181,6 @@ __device__ __forceinline__ void tile_load(const AttnPlanes& pk, const AttnPlanes
     }
 }
 
-// Keep the optimizer from merging the nibble masks into the byte extraction, so that the four
-// bytes convert with v_cvt_f32_ubyte0..3.
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-    asm("" : "+v"(v));
-    return v;
-}
 
 // The lane's 8 decoded K values of word i (channels 32q + 8i .. 32q + 8i + 7) from the LDS slot.
 template <int FMT>
@@ -369,7 +374,7 @@ __device__ __forceinline__ int kgroup_shift(const AttnPlanes& p) {
 }
 
 template <int FMT, int RFMT>
-__global__ __launch_bounds__(64 * kWaves) void k_attn_split(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) void k_attn_split(AttnArgs a) {
     constexpr bool RES = RFMT != kNone;
     __shared__ TableT<FMT == FMT_NVFP4> tk, tv;
     __shared__ TableT<RFMT == FMT_NVFP4> trk, trv;
