@@ -122,7 +122,7 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
     Hq = 64
     qv = torch.randn((Hq, D), generator=torch.Generator(device="cpu").manual_seed(3)).to(torch.bfloat16).to(dev)
     aout = torch.empty((Hq, D), dtype=torch.float32, device=dev)
-    for fmt, G in (("int4", 64), ("nvfp4", 16)):
+    for fmt, G in (("int4", 64), ("nvfp4", 16), ("nvfp4_row", 16), ("fp8_row", 0)):
         pk = kvq.pack(x0, "key", fmt, G)
         pv = kvq.pack(X["value"][0], "value", fmt, G)
         pbytes = pk.nbytes() + pv.nbytes()

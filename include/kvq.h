@@ -268,8 +268,9 @@ size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq);
  * output matches float64 attention over the decoded cache to within about 2^-9 of max |V|.
  *   q        device bf16 [Hq, 128], contiguous, 16-byte aligned
  *   k, v     packed KEY / VALUE tensors of one layer: rows = T >= 1, the same H, head_dim 128,
- *            dense, the same format (INT4 or NVFP4); INT4 groups a power of two, at least 16
- *            tokens for K and 8 to 128 channels for V; planes 16-byte aligned
+ *            dense, the same format (any of the four); INT4 groups a power of two, at least 16
+ *            tokens for K and 8 to 128 channels for V; code planes 16-byte aligned, metadata
+ *            planes aligned to their element size (INT4 and NVFP4: 16 bytes)
  *   k_res, v_res  optional dense residuals of the same shape (formats may differ from k, v)
  *   Hq       a multiple of H with Hq / H <= 16
  *   out      device float [Hq, 128]

@@ -392,25 +392,39 @@ size_t attn_workspace(int64_t T, int64_t H, int64_t rep) {
     return (size_t)H * attn_split_bound(T, H) * rep * (KVQ_ATTN_D + 2) * sizeof(float);
 }
 
-// One packed tensor of an attention call: dense, the expected kind, head_dim 128, and a group
-// size the kernel's tiling takes (INT4: a power of two, K at least 16, V from 8 to 128).
+// One packed tensor of an attention call: dense, the expected kind, head_dim 128, any of the
+// four formats, and for INT4 a group size the kernel's tiling takes (a power of two, K at least
+// 16, V from 8 to 128).
 kvq_status attn_operand(const kvq_packed* p, int kind, int64_t T, int64_t H, AttnPlanes* out) {
     kvq_status st = check_packed(p);
     if (st) return st;
     if (p->kind != kind || p->positions) return KVQ_ERR_MISMATCH;
-    if (p->format != KVQ_INT4 && p->format != KVQ_NVFP4) return KVQ_ERR_FORMAT;
     if (p->D != KVQ_ATTN_D) return KVQ_ERR_SHAPE;
     if (p->rows != T || p->H != H) return KVQ_ERR_MISMATCH;
     const int32_t G = p->group_size;
-    if (p->format == KVQ_INT4) {
-        // powers of two: a K group holds whole 16-token sub-tiles, a V group whole 8-channel lanes
-        if (!is_pow2(G) || (kind == KVQ_KEY ? G < 16 : (G < 8 || G > KVQ_ATTN_D))) return KVQ_ERR_GROUP;
-        if (!aligned(p->meta0, 16) || !aligned(p->meta1, 16)) return KVQ_ERR_LAYOUT;
-    } else if (!aligned(p->meta0, 16)) {
-        return KVQ_ERR_LAYOUT;
+    int32_t gshift = 0;
+    switch (p->format) {
+        case KVQ_INT4:
+            // powers of two: a K group holds whole 16-token sub-tiles, a V group whole 8-channel lanes
+            if (!is_pow2(G) || (kind == KVQ_KEY ? G < 16 : (G < 8 || G > KVQ_ATTN_D))) return KVQ_ERR_GROUP;
+            if (!aligned(p->meta0, 16) || !aligned(p->meta1, 16)) return KVQ_ERR_LAYOUT;
+            gshift = log2i(G);
+            break;
+        case KVQ_NVFP4:
+            if (!aligned(p->meta0, 16)) return KVQ_ERR_LAYOUT;
+            gshift = 4;
+            break;
+        case KVQ_NVFP4_ROW:  // block-scale bytes read in pairs, FP32 row multipliers
+            if (!aligned(p->meta0, 2) || !aligned(p->meta1, 4)) return KVQ_ERR_LAYOUT;
+            break;
+        case KVQ_FP8_ROW:  // FP32 row scales
+            if (!aligned(p->meta0, 4)) return KVQ_ERR_LAYOUT;
+            break;
+        default:
+            return KVQ_ERR_FORMAT;
     }
     if (!aligned(p->codes, 16)) return KVQ_ERR_LAYOUT;
-    *out = AttnPlanes{p->codes, p->meta0, p->meta1, p->global_scale, log2i(G)};
+    *out = AttnPlanes{p->codes, p->meta0, p->meta1, p->global_scale, gshift};
     return KVQ_OK;
 }
 

@@ -86,37 +86,60 @@ __device__ __forceinline__ void meta_store(uint32_t* slot, const MetaStage& m, i
     }
 }
 
-// --- raw loads (issued one sub-tile ahead) and in-register decoding ---
+// --- raw loads and in-register decoding ---
 
-// Codes of one sub-tile for this lane: K of token l % 16, channels 32q .. 32q + 31 (16 bytes);
-// V of tokens 4q + j, channels 8r .. 8r + 7 (4 bytes each) with their group's metadata
-// (INT4: f16 scale << 16 | f16 minimum; NVFP4: the E4M3 block-scale byte).
+// Formats whose K metadata belongs to a group of tokens (it goes through the LDS slots); the
+// row formats carry their metadata per (token, KV head) row and load it with the codes.
+template <int FMT>
+constexpr bool kGroupMeta = FMT == FMT_INT4 || FMT == FMT_NVFP4;
+// Code bytes of one (token, KV head) row of 128 channels.
+template <int FMT>
+constexpr int kRowBytes = FMT == FMT_FP8_ROW ? kD : kD / 2;
+
+// Raw data of one sub-tile for this lane.
+//   K of token l % 16, channels 32q .. 32q + 31: codes (16 bytes; FP8-row 32), and for the row
+//   formats that row's metadata: NVFP4-row the two E4M3 block-scale bytes of these channels and
+//   the FP32 row multiplier g, FP8-row the FP32 row scale.
+//   V of tokens 4q + j, channels 8r .. 8r + 7: codes (4 bytes; FP8-row 8) and metadata (INT4:
+//   f16 scale << 16 | f16 minimum; NVFP4, NVFP4-row: the block-scale byte; FP8-row: the row
+//   scale's bits), and for NVFP4-row the row multiplier.
+template <int FMT>
 struct TileRaw {
-    u32x4 kc;
-    uint32_t vc[4];
+    u32x4 kc[FMT == FMT_FP8_ROW ? 2 : 1];
+    uint32_t km;
+    float kg;
+    uint32_t vc[4][FMT == FMT_FP8_ROW ? 2 : 1];
     uint32_t vm[4];
+    float vg[4];
 };
 
-// Loop-invariant lane byte offsets of one packed tensor (K codes of token l % 16, channel
-// group q; V codes and metadata of tokens 4q + j, channels 8r .. 8r + 7), relative to the
-// sub-tile's first row, whose addresses are wave-uniform.
+// Loop-invariant lane byte offsets of one packed tensor, relative to the sub-tile's first row,
+// whose addresses are wave-uniform: K codes, K row metadata (block bytes, row FP32), V codes, V
+// metadata, V row FP32.
 struct LaneOffsets {
-    uint32_t kc;
-    uint32_t vc[4], vm[4];
+    uint32_t kc, km, kg;
+    uint32_t vc[4], vm[4], vg[4];
 };
 
 template <int FMT>
 __device__ __forceinline__ void lane_offsets(const AttnPlanes& pk, const AttnPlanes& pv, int H, int h, int r, int q,
                                              int64_t dt_k, const int64_t (&dt_v)[4], LaneOffsets& o) {
-    o.kc = (uint32_t)(((uint64_t)dt_k * H + h) * (kD / 2) + 16 * q);
+    constexpr int RB = kRowBytes<FMT>;
+    const uint64_t krow = (uint64_t)dt_k * H + h;
+    o.kc = (uint32_t)(krow * RB + (RB / 4) * q);
+    o.km = (uint32_t)(krow * (kD / 16) + 2 * q);  // NVFP4-row: blocks 2q, 2q + 1
+    o.kg = (uint32_t)(krow * 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint64_t row = (uint64_t)dt_v[j] * H + h;
-        o.vc[j] = (uint32_t)(row * (kD / 2) + 4 * r);
+        o.vc[j] = (uint32_t)(row * RB + (RB / 16) * r);
         if constexpr (FMT == FMT_INT4)  // f16 entries [row][channel group]
             o.vm[j] = (uint32_t)(2 * ((row << (7 - pv.gshift)) + ((8u * r) >> pv.gshift)));
+        else if constexpr (FMT == FMT_FP8_ROW)  // FP32 [row]
+            o.vm[j] = (uint32_t)(row * 4);
         else  // E4M3 bytes [row][16-channel block]
             o.vm[j] = (uint32_t)(row * (kD / 16) + (r >> 1));
+        o.vg[j] = (uint32_t)(row * 4);
     }
 }
 
@@ -158,34 +181,81 @@ __device__ __forceinline__ T ld_nt_at(gptr base, uint32_t off) {
 
 template <int FMT>
 __device__ __forceinline__ void tile_load(const AttnPlanes& pk, const AttnPlanes& pv, int64_t t0, int H,
-                                          const LaneOffsets& o, TileRaw& x) {
-    const size_t crow = (size_t)t0 * H * (kD / 2);
-    x.kc = ld_nt_at<u32x4>(sbase(pk.codes, crow), o.kc);
-    gptr vcb = sbase(pv.codes, crow);
-    if constexpr (FMT == FMT_INT4) {
-        const size_t g = 2 * ((size_t)t0 * H << (7 - pv.gshift));
-        gptr mb = sbase(pv.meta0, g);
-        gptr sb = sbase(pv.meta1, g);
+                                          const LaneOffsets& o, TileRaw<FMT>& x) {
+    const size_t rows = (size_t)t0 * H;  // (token, head) rows before the sub-tile
+    gptr kcb = sbase(pk.codes, rows * kRowBytes<FMT>);
+    gptr vcb = sbase(pv.codes, rows * kRowBytes<FMT>);
+    if constexpr (FMT == FMT_FP8_ROW) {
+        x.kc[0] = ld_nt_at<u32x4>(kcb, o.kc);
+        x.kc[1] = ld_nt_at<u32x4>(kcb, o.kc + 16);
+        x.kg = __uint_as_float(ld_at<uint32_t>(sbase(pk.meta0, rows * 4), o.kg));
+        gptr vsb = sbase(pv.meta0, rows * 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x.vc[j] = ld_nt_at<uint32_t>(vcb, o.vc[j]);
-            x.vm[j] = (uint32_t)ld_at<uint16_t>(mb, o.vm[j]) | ((uint32_t)ld_at<uint16_t>(sb, o.vm[j]) << 16);
+            const u2_t w = ld_nt_at<u2_t>(vcb, o.vc[j]);
+            x.vc[j][0] = w.x;
+            x.vc[j][1] = w.y;
+            x.vm[j] = ld_at<uint32_t>(vsb, o.vm[j]);
         }
     } else {
-        gptr mb = sbase(pv.meta0, (size_t)t0 * H * (kD / 16));
+        x.kc[0] = ld_nt_at<u32x4>(kcb, o.kc);
+        if constexpr (FMT == FMT_NVFP4_ROW) {
+            x.km = ld_at<uint16_t>(sbase(pk.meta0, rows * (kD / 16)), o.km);
+            x.kg = __uint_as_float(ld_at<uint32_t>(sbase(pk.meta1, rows * 4), o.kg));
+        }
+        if constexpr (FMT == FMT_INT4) {
+            const size_t g = 2 * (rows << (7 - pv.gshift));
+            gptr mb = sbase(pv.meta0, g);
+            gptr sb = sbase(pv.meta1, g);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x.vc[j] = ld_nt_at<uint32_t>(vcb, o.vc[j]);
-            x.vm[j] = ld_at<uint8_t>(mb, o.vm[j]);
+            for (int j = 0; j < 4; ++j) {
+                x.vc[j][0] = ld_nt_at<uint32_t>(vcb, o.vc[j]);
+                x.vm[j] = (uint32_t)ld_at<uint16_t>(mb, o.vm[j]) | ((uint32_t)ld_at<uint16_t>(sb, o.vm[j]) << 16);
+            }
+        } else {
+            gptr mb = sbase(pv.meta0, rows * (kD / 16));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x.vc[j][0] = ld_nt_at<uint32_t>(vcb, o.vc[j]);
+                x.vm[j] = ld_at<uint8_t>(mb, o.vm[j]);
+            }
+            if constexpr (FMT == FMT_NVFP4_ROW) {
+                gptr gb = sbase(pv.meta1, rows * 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x.vg[j] = __uint_as_float(ld_at<uint32_t>(gb, o.vg[j]));
+            }
         }
     }
 }
 
+// NVFP4-row decode scale of one block: fl(e4m3(code) / g), the codec's own division.
+__device__ __forceinline__ float nvfp4_row_sdec(uint32_t code, float g) { return e4m3_decode(code & 0x7Fu) / g; }
 
-// The lane's 8 decoded K values of word i (channels 32q + 8i .. 32q + 8i + 7) from the LDS slot.
+// Per-sub-tile K constants of a row format: NVFP4-row the two block decode scales of the lane's
+// channels, FP8-row the row scale.
+struct KPrep {
+    float s[2];
+};
+
 template <int FMT>
-__device__ __forceinline__ void k_decode8(uint32_t w, const uint32_t* slot, int q, int i, float (&y)[8]) {
+__device__ __forceinline__ void k_prep(const TileRaw<FMT>& x, KPrep& k) {
+    if constexpr (FMT == FMT_NVFP4_ROW) {
+        k.s[0] = nvfp4_row_sdec(x.km & 0xFFu, x.kg);
+        k.s[1] = nvfp4_row_sdec(x.km >> 8, x.kg);
+    } else if constexpr (FMT == FMT_FP8_ROW) {
+        k.s[0] = k.s[1] = x.kg;
+    } else {
+        k.s[0] = k.s[1] = 0.0f;
+    }
+}
+
+// The lane's 8 decoded K values of chunk i (channels 32q + 8i .. 32q + 8i + 7): group formats
+// read their metadata from the LDS slot, row formats from the sub-tile's own row metadata.
+template <int FMT>
+__device__ __forceinline__ void k_decode8(const TileRaw<FMT>& x, const KPrep& kp, const uint32_t* slot, int q, int i,
+                                          float (&y)[8]) {
     if constexpr (FMT == FMT_INT4) {
+        const uint32_t w = x.kc[0][i];
         const u32x4 m4 = reinterpret_cast<const u32x4*>(slot)[4 * q + i];
         const u32x4 s4 = reinterpret_cast<const u32x4*>(slot + kMetaWords / 2)[4 * q + i];
         const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
@@ -196,12 +266,27 @@ __device__ __forceinline__ void k_decode8(uint32_t w, const uint32_t* slot, int 
             y[2 * b] = int4_value_f(c0, f16_to_f32(ss[b] & 0xFFFFu), f16_to_f32(mm[b] & 0xFFFFu));
             y[2 * b + 1] = int4_value_f(c1, f16_to_f32(ss[b] >> 16), f16_to_f32(mm[b] >> 16));
         }
+    } else if constexpr (FMT == FMT_FP8_ROW) {
+        const uint32_t w0 = x.kc[i >> 1][2 * (i & 1)], w1 = x.kc[i >> 1][2 * (i & 1) + 1];
+        const f32x2 e0 = fp8_values<false>(w0), e1 = fp8_values<true>(w0);
+        const f32x2 e2 = fp8_values<false>(w1), e3 = fp8_values<true>(w1);
+        const float e[8] = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+#pragma unroll
+        for (int n = 0; n < 8; ++n) y[n] = __fmul_rn(e[n], kp.s[0]);
     } else {
-        const u32x4 f0 = reinterpret_cast<const u32x4*>(slot)[8 * q + 2 * i];
-        const u32x4 f1 = reinterpret_cast<const u32x4*>(slot)[8 * q + 2 * i + 1];
-        const float sd[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
-                             __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
-                             __uint_as_float(f1.z), __uint_as_float(f1.w)};
+        const uint32_t w = x.kc[0][i];
+        float sd[8];
+        if constexpr (FMT == FMT_NVFP4) {
+            const u32x4 f0 = reinterpret_cast<const u32x4*>(slot)[8 * q + 2 * i];
+            const u32x4 f1 = reinterpret_cast<const u32x4*>(slot)[8 * q + 2 * i + 1];
+            sd[0] = __uint_as_float(f0.x); sd[1] = __uint_as_float(f0.y);
+            sd[2] = __uint_as_float(f0.z); sd[3] = __uint_as_float(f0.w);
+            sd[4] = __uint_as_float(f1.x); sd[5] = __uint_as_float(f1.y);
+            sd[6] = __uint_as_float(f1.z); sd[7] = __uint_as_float(f1.w);
+        } else {  // NVFP4-row: chunk i lies in block 2q + i / 2
+#pragma unroll
+            for (int n = 0; n < 8; ++n) sd[n] = kp.s[i >> 1];
+        }
         const f32x2 e0 = e2m1_values<0>(w), e1 = e2m1_values<1>(w), e2 = e2m1_values<2>(w), e3 = e2m1_values<3>(w);
         const float e[8] = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
 #pragma unroll
@@ -210,24 +295,29 @@ __device__ __forceinline__ void k_decode8(uint32_t w, const uint32_t* slot, int 
 }
 
 // V of one sub-tile prepared for decoding: the masked nibble words (INT4: low nibbles of the
-// four tokens' words, then high) or the raw words (NVFP4), with each token's scale and minimum.
+// four tokens' words, then high), the raw words (NVFP4, NVFP4-row: one per token; FP8-row: two
+// per token), with each token's scale (and INT4 minimum).
 struct VPrep {
     uint32_t w[8];
     float s[4], m[4];
 };
 
 template <int FMT>
-__device__ __forceinline__ void v_prep(const TileRaw& x, const Fp4Table* tab, VPrep& v) {
+__device__ __forceinline__ void v_prep(const TileRaw<FMT>& x, const Fp4Table* tab, VPrep& v) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if constexpr (FMT == FMT_INT4) {
-            v.w[j] = opaque(x.vc[j] & 0x0F0F0F0Fu);
-            v.w[4 + j] = opaque((x.vc[j] >> 4) & 0x0F0F0F0Fu);
+            v.w[j] = opaque(x.vc[j][0] & 0x0F0F0F0Fu);
+            v.w[4 + j] = opaque((x.vc[j][0] >> 4) & 0x0F0F0F0Fu);
             v.m[j] = f16_to_f32(x.vm[j] & 0xFFFFu);
             v.s[j] = f16_to_f32(x.vm[j] >> 16);
+        } else if constexpr (FMT == FMT_FP8_ROW) {
+            v.w[2 * j] = x.vc[j][0];
+            v.w[2 * j + 1] = x.vc[j][1];
+            v.s[j] = __uint_as_float(x.vm[j]);
         } else {
-            v.w[j] = x.vc[j];
-            v.s[j] = tab->e[x.vm[j] & 0x7Fu][0];
+            v.w[j] = x.vc[j][0];
+            v.s[j] = (FMT == FMT_NVFP4) ? tab->e[x.vm[j] & 0x7Fu][0] : nvfp4_row_sdec(x.vm[j], x.vg[j]);
         }
     }
 }
@@ -240,6 +330,10 @@ __device__ __forceinline__ void v_decode_n(const VPrep& v, int n, float (&y)[4])
         if constexpr (FMT == FMT_INT4) {
             const uint32_t w = v.w[(n & 1) ? 4 + j : j];  // nibble n: byte n / 2, low or high half
             y[j] = int4_value_f((float)((w >> (8 * (n >> 1))) & 0xFFu), v.s[j], v.m[j]);
+        } else if constexpr (FMT == FMT_FP8_ROW) {
+            const uint32_t w = v.w[2 * j + (n >> 2)];  // byte n of the token's 8
+            const f32x2 e = (n & 2) ? fp8_values<true>(w) : fp8_values<false>(w);
+            y[j] = __fmul_rn(e[n & 1], v.s[j]);
         } else {
             const f32x2 e = (n >> 1) == 0   ? e2m1_values<0>(v.w[j])
                             : (n >> 1) == 1 ? e2m1_values<1>(v.w[j])
@@ -265,10 +359,10 @@ __device__ __forceinline__ s4_t as_s4(uint32_t lo, uint32_t hi) {
 }
 
 // Raw data of one 16-token sub-tile (base and, for a residual, the residual planes).
-template <bool RES>
+template <int FMT, int RFMT>
 struct SubRaw {
-    TileRaw b;
-    std::conditional_t<RES, TileRaw, char> r;
+    TileRaw<FMT> b;
+    std::conditional_t<RFMT != kNone, TileRaw<RFMT == kNone ? FMT_INT4 : RFMT>, char> r;
 };
 
 // Per-wave running state of the online softmax. m is the offset subtracted from the scores
@@ -301,29 +395,27 @@ __device__ __forceinline__ void call_offsets(const AttnArgs& a, int h, int r, in
 
 template <int FMT, int RFMT>
 __device__ __forceinline__ void sub_load(const AttnArgs& a, int64_t t0, const CallOffsets<RFMT>& o,
-                                         SubRaw<RFMT != kNone>& s) {
+                                         SubRaw<FMT, RFMT>& s) {
     tile_load<FMT>(a.k, a.v, t0, a.H, o.b, s.b);
     if constexpr (RFMT != kNone) tile_load<RFMT>(a.rk, a.rv, t0, a.H, o.r, s.r);
 }
 
 template <int FMT, int RFMT, bool TAIL>
 __device__ __forceinline__ void sub_compute(const AttnArgs& a, int n_valid, int q, const uint32_t (&qw)[16],
-                                            const SubRaw<RFMT != kNone>& s, const uint32_t* kslot,
+                                            const SubRaw<FMT, RFMT>& s, const uint32_t* kslot,
                                             const uint32_t* rkslot, const Fp4Table* ptv, const Fp4Table* ptrv,
                                             WaveState& st) {
     constexpr bool RES = RFMT != kNone;
     // ---- scores S^T = K Q^T, 8 channels (two MFMA steps) at a time ----
     f4_t sacc = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t kw[4] = {s.b.kc.x, s.b.kc.y, s.b.kc.z, s.b.kc.w};
-    uint32_t rw[4] = {0u, 0u, 0u, 0u};
-    if constexpr (RES) {
-        rw[0] = s.r.kc.x; rw[1] = s.r.kc.y; rw[2] = s.r.kc.z; rw[3] = s.r.kc.w;
-    }
+    KPrep kpb, kpr;
+    k_prep<FMT>(s.b, kpb);
+    if constexpr (RES) k_prep<RFMT>(s.r, kpr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float kv[8], kr[8];
-        k_decode8<FMT>(kw[i], kslot, q, i, kv);
-        if constexpr (RES) k_decode8<RFMT>(rw[i], rkslot, q, i, kr);
+        k_decode8<FMT>(s.b, kpb, kslot, q, i, kv);
+        if constexpr (RES) k_decode8<RFMT>(s.r, kpr, rkslot, q, i, kr);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int c = 4 * h2, st4 = 2 * i + h2;
@@ -367,11 +459,16 @@ __device__ __forceinline__ void sub_compute(const AttnArgs& a, int n_valid, int 
     }
 }
 
-// log2 of the tokens per K metadata group (NVFP4 K blocks are 16 tokens)
+// log2 of the tokens per K metadata group (NVFP4 K blocks are 16 tokens; row formats have no
+// K groups)
 template <int FMT>
 __device__ __forceinline__ int kgroup_shift(const AttnPlanes& p) {
     return FMT == FMT_INT4 ? p.gshift : 4;
 }
+
+// LDS metadata slots per wave: two for a group-format base, two more for a group-format residual.
+template <int FMT, int RFMT>
+constexpr int kSlots = (kGroupMeta<FMT> ? 2 : 0) + (RFMT != kNone && kGroupMeta<RFMT == kNone ? FMT_INT4 : RFMT> ? 2 : 0);
 
 template <int FMT, int RFMT>
 __global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) void k_attn_split(AttnArgs a) {
@@ -380,7 +477,9 @@ __global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) 
     __shared__ TableT<RFMT == FMT_NVFP4> trk, trv;
     __shared__ float s_o[kWaves][16][kD];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-    __shared__ uint32_t s_meta[kWaves][RES ? 4 : 2][kMetaWords];  // per wave: 2 slots (+2 residual)
+    constexpr bool GK = kGroupMeta<FMT>;                                        // base K metadata via LDS
+    constexpr bool GR = RES && kGroupMeta<RFMT == kNone ? FMT_INT4 : RFMT>;    // residual K metadata via LDS
+    __shared__ uint32_t s_meta[kWaves][kSlots<FMT, RFMT> > 0 ? kSlots<FMT, RFMT> : 1][kMetaWords];
     if constexpr (FMT == FMT_NVFP4) {
         fp4_table_fill(tk, *a.k.gscale);
         fp4_table_fill(tv, *a.v.gscale);
@@ -428,12 +527,12 @@ __global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) 
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.o[n] = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int ks = kgroup_shift<FMT>(a.k);
-    int rks = 0;
-    if constexpr (RES) rks = kgroup_shift<RFMT>(a.rk);
+    int ks = 0, rks = 0;
+    if constexpr (GK) ks = kgroup_shift<FMT>(a.k);
+    if constexpr (GR) rks = kgroup_shift<RFMT>(a.rk);
     uint32_t* slots = &s_meta[wave][0][0];
-    auto kslot = [&](int64_t t) { return slots + ((t >> ks) & 1) * kMetaWords; };
-    auto rkslot = [&](int64_t t) { return slots + (2 + ((t >> rks) & 1)) * kMetaWords; };
+    auto kslot = [&](int64_t t) { return GK ? slots + ((t >> ks) & 1) * kMetaWords : nullptr; };
+    auto rkslot = [&](int64_t t) { return GR ? slots + ((GK ? 2 : 0) + ((t >> rks) & 1)) * kMetaWords : nullptr; };
 
     // Full sub-tiles (all 16 tokens in range) run in the main loop with loop-invariant offsets;
     // the block's last sub-tile may be partial and runs after it, its rows clamped to the last.
@@ -445,34 +544,40 @@ __global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) 
     // prefetching) and, where the next sub-tile opens a new K group, that group's metadata are
     // fetched first; the metadata goes to its LDS slot (the one the current group does not use)
     // afterwards.
-    auto step = [&](int64_t t, SubRaw<RES>& cur, SubRaw<RES>& nxt) {
+    auto step = [&](int64_t t, SubRaw<FMT, RFMT>& cur, SubRaw<FMT, RFMT>& nxt) {
         const int64_t tn = t + kSub;
         const bool more = tn < w_end;
-        const bool nk = more && (tn >> ks) != (t >> ks);
-        const bool nr = RES && more && (tn >> rks) != (t >> rks);
+        const bool nk = GK && more && (tn >> ks) != (t >> ks);
+        const bool nr = GR && more && (tn >> rks) != (t >> rks);
         MetaStage mk, mr;
         if (KVQ_ATTN_PREFETCH && tn < w_full) sub_load<FMT, RFMT>(a, tn, full, nxt);
         if (!KVQ_ATTN_PREFETCH) sub_load<FMT, RFMT>(a, t, full, cur);
-        if (nk) meta_fetch<FMT>(a.k, tn, a.H, h, lane, mk);
-        if constexpr (RES) {
+        if constexpr (GK) {
+            if (nk) meta_fetch<FMT>(a.k, tn, a.H, h, lane, mk);
+        }
+        if constexpr (GR) {
             if (nr) meta_fetch<RFMT>(a.rk, tn, a.H, h, lane, mr);
         }
         __builtin_amdgcn_wave_barrier();
-        sub_compute<FMT, RFMT, false>(a, kSub, q, qw, cur, kslot(t), RES ? rkslot(t) : nullptr, ptv, ptrv, st);
-        if (nk) meta_store<FMT>(kslot(tn), mk, lane, ptk);
-        if constexpr (RES) {
+        sub_compute<FMT, RFMT, false>(a, kSub, q, qw, cur, kslot(t), rkslot(t), ptv, ptrv, st);
+        if constexpr (GK) {
+            if (nk) meta_store<FMT>(kslot(tn), mk, lane, ptk);
+        }
+        if constexpr (GR) {
             if (nr) meta_store<RFMT>(rkslot(tn), mr, lane, ptrk);
         }
         __builtin_amdgcn_wave_barrier();
     };
 
     int64_t t0 = w_begin;
-    SubRaw<RES> A, B;
+    SubRaw<FMT, RFMT> A, B;
     if (t0 < w_end) {
         MetaStage m;
-        meta_fetch<FMT>(a.k, t0, a.H, h, lane, m);
-        meta_store<FMT>(kslot(t0), m, lane, ptk);
-        if constexpr (RES) {
+        if constexpr (GK) {
+            meta_fetch<FMT>(a.k, t0, a.H, h, lane, m);
+            meta_store<FMT>(kslot(t0), m, lane, ptk);
+        }
+        if constexpr (GR) {
             meta_fetch<RFMT>(a.rk, t0, a.H, h, lane, m);
             meta_store<RFMT>(rkslot(t0), m, lane, ptrk);
         }
@@ -490,8 +595,7 @@ __global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) 
         call_offsets<FMT, RFMT>(a, h, r, q, t0, w_end, tail);
         sub_load<FMT, RFMT>(a, t0, tail, A);
         __builtin_amdgcn_wave_barrier();
-        sub_compute<FMT, RFMT, true>(a, (int)(w_end - t0), q, qw, A, kslot(t0), RES ? rkslot(t0) : nullptr, ptv,
-                                     ptrv, st);
+        sub_compute<FMT, RFMT, true>(a, (int)(w_end - t0), q, qw, A, kslot(t0), rkslot(t0), ptv, ptrv, st);
     }
 
     // ---- fold the block's 4 waves: lane holds O[row r][channel 32q + 8j + n] ----
@@ -641,6 +745,8 @@ hipError_t attn_fmt(int rfmt, const AttnArgs& a, hipStream_t s) {
     if (rfmt == kNone) return attn_launch<FMT, kNone>(a, s);
     if (rfmt == FMT_INT4) return attn_launch<FMT, FMT_INT4>(a, s);
     if (rfmt == FMT_NVFP4) return attn_launch<FMT, FMT_NVFP4>(a, s);
+    if (rfmt == FMT_NVFP4_ROW) return attn_launch<FMT, FMT_NVFP4_ROW>(a, s);
+    if (rfmt == FMT_FP8_ROW) return attn_launch<FMT, FMT_FP8_ROW>(a, s);
     return hipErrorInvalidValue;
 }
 
@@ -649,6 +755,8 @@ hipError_t attn_fmt(int rfmt, const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attention(int fmt, int rfmt, const AttnArgs& a, hipStream_t s) {
     if (fmt == FMT_INT4) return attn_fmt<FMT_INT4>(rfmt, a, s);
     if (fmt == FMT_NVFP4) return attn_fmt<FMT_NVFP4>(rfmt, a, s);
+    if (fmt == FMT_NVFP4_ROW) return attn_fmt<FMT_NVFP4_ROW>(rfmt, a, s);
+    if (fmt == FMT_FP8_ROW) return attn_fmt<FMT_FP8_ROW>(rfmt, a, s);
     return hipErrorInvalidValue;
 }
 

@@ -23,7 +23,7 @@ from workloads import bf16_bits, c4_tensors, normal_kv
 pytestmark = pytest.mark.gpu
 
 D = 128
-FORMS = [("int4", 64, 64), ("int4", 16, 32), ("int4", 128, 8), ("nvfp4", 16, 16)]
+FORMS = [("int4", 64, 64), ("int4", 16, 32), ("int4", 128, 8), ("nvfp4", 16, 16), ("nvfp4_row", 16, 16), ("fp8_row", 0, 0)]
 
 
 def packed_pair(k_bits, v_bits, fmt, gk, gv):
@@ -90,11 +90,13 @@ def test_one_dominant_key_selects_its_value(fmt, gk, gv):
         np.testing.assert_allclose(out[hq], vr[t, h], rtol=0, atol=1e-5 * np.abs(vr).max())
 
 
-@pytest.mark.parametrize("bfmt,rfmt", [("int4", "int4"), ("nvfp4", "int4"), ("int4", "nvfp4")])
+@pytest.mark.parametrize("bfmt,rfmt", [("int4", "int4"), ("nvfp4", "int4"), ("int4", "nvfp4"), ("fp8_row", "int4"),
+                                       ("int4", "fp8_row"), ("nvfp4_row", "nvfp4_row"), ("fp8_row", "nvfp4"),
+                                       ("nvfp4", "nvfp4_row")])
 def test_fused_residual_reconstruction(bfmt, rfmt):
     rng = np.random.default_rng(9)
     T, H, Hq = 900, 2, 16
-    g = {"int4": (64, 64), "nvfp4": (16, 16)}
+    g = {"int4": (64, 64), "nvfp4": (16, 16), "nvfp4_row": (16, 16), "fp8_row": (0, 0)}
     k0, v0 = normal_kv(rng, T, H, D), normal_kv(rng, T, H, D)
     k1 = bf16_bits(oracle.bf16_to_f32(k0).astype(np.float64) + 0.1 * rng.standard_normal(k0.shape))
     v1 = bf16_bits(oracle.bf16_to_f32(v0).astype(np.float64) + 0.1 * rng.standard_normal(v0.shape))
@@ -111,7 +113,7 @@ def test_fused_residual_reconstruction(bfmt, rfmt):
     check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"{bfmt}+{rfmt}")
 
 
-@pytest.mark.parametrize("fmt,gk,gv", [("int4", 64, 64), ("nvfp4", 16, 16)])
+@pytest.mark.parametrize("fmt,gk,gv", [("int4", 64, 64), ("nvfp4", 16, 16), ("fp8_row", 0, 0)])
 def test_bulk_shape(fmt, gk, gv):
     """The bench's shape: T = 131072 tokens, 8 KV heads, 64 query heads (heavy-tailed data)."""
     T, H, Hq = 131072, 8, 64
