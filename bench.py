@@ -22,8 +22,12 @@ unpack_paged of K with page-local groups (16-token pages of a pool that interlea
 page, so the page stride is padded), and store_rows / load_rows of 16384 rows into and out of
 a 131072-slot cache, and the BF16 window (first 4 / latest 16 rows raw) around INT4 G64 K
 pack and residual encode/decode, and decode attention of 64 query heads over the packed K/V
-(INT4 G64 with and without one fused residual, NVFP4 G16), whose algorithmic bytes are the
-packed planes it reads. Algorithmic bytes per element for a row format with c code bytes and
+(all four formats; INT4 G64 also with one fused residual), whose algorithmic bytes are the
+packed planes it reads. Context lines: INT4 and NVFP4 K ops on one KV head's shard
+([T, 1, 128], the per-GPU shape of head sharding over 8 GPUs); the 268 MB tensor copied by this
+library's row-copy kernel and by the runtime's device-to-device copy (read + write bytes); and
+the dominant bulk op timed after a 1 GiB write that evicts the 256 MB Infinity Cache (inside the
+step it follows the op that wrote one of its inputs). Algorithmic bytes per element for a row format with c code bytes and
 m = block-scale bytes + 4/D row-scale bytes per element: pack and unpack 2 + c + m, residual
 encode and decode 4 + c + m; page-local INT4 G16 K 2.75; a slot write or read of N rows moves
 N*H*D*(2 + c + m) bytes plus 4 B per slot id; a windowed op moves the codec bytes of its
@@ -74,8 +78,8 @@ def row_format_bytes(fmt: str) -> tuple:
 
 
 def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
-    """Row formats, paged views and slot writes/reads on the bulk tensors (see the module
-    docstring); returns {name: {us, GBps, pct_peak}}."""
+    """Row formats, paged views, slot writes/reads, windows, decode attention and the context
+    lines on the bulk tensors (see the module docstring); returns {name: {us, GBps, pct_peak}}."""
     n = T * H * D
     x0, x1 = X["key"]
     calls = []
@@ -147,14 +151,48 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
             (f"{fmt}-store_rows-16384", nb, lambda cache=cache: kvq.store_rows(cache, rows, slots)),
             (f"{fmt}-load_rows-16384", nb, lambda cache=cache, outr=outr: kvq.load_rows(cache, slots, out=outr)),
         ]
+    # one KV head's shard of the same tensors ([T, 1, 128], contiguous): the per-GPU shape of head
+    # (tensor-parallel) sharding over 8 GPUs
+    xs0, xs1 = x0[:, :1].contiguous(), x1[:, :1].contiguous()
+    ns = xs0.numel()
+    ps = kvq.alloc_packed("int4", "key", 64, T, 1, D, T, dev)
+    pn = kvq.alloc_packed("nvfp4", "key", 16, T, 1, D, T, dev)
+    rs = kvq.alloc_packed("int4", "key", 64, T, 1, D, T, dev)
+    Rs = kvq.unpack(kvq.pack(xs0, "key", "int4", 64))
+    calls += [
+        ("int4-key-pack-shard_H1", ns * 2.5625, lambda: kvq.pack(xs0, "key", "int4", 64, out=ps)),
+        ("int4-key-encode_residual-shard_H1", ns * 4.5625,
+         lambda: kvq.encode_residual(xs1, Rs, "key", "int4", 64, out=rs)),
+        ("nvfp4-key-pack-shard_H1", ns * 4.5625 + 4, lambda: kvq.pack(xs0, "key", "nvfp4", 16, out=pn)),
+    ]
+    # context: the same 268 MB copied by a plain row-copy kernel of this library (a sparse residual
+    # with no rows decodes out of place as one copy) and by the runtime's device-to-device copy;
+    # and the dominant bulk op timed right after a 1 GiB write that evicts the 256 MB Infinity
+    # Cache (in the step it follows the op that wrote its input)
+    cdst = torch.empty_like(x0)
+    empty = kvq.encode_residual(x0, x0, "key", "int4", 64, positions=torch.zeros(0, dtype=torch.int32, device=dev))
+    flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    R0 = kvq.unpack(kvq.pack(x0, "key", "int4", 64))
+    rr = kvq.alloc_packed("int4", "key", 64, T, H, D, T, dev)
+    calls += [
+        ("context-copy_kernel-268MB", 4 * n, lambda: kvq.decode_residual(empty, x0, out=cdst)),
+        ("context-d2d_copy-268MB", 4 * n, lambda: cdst.copy_(x0)),
+        ("int4-key-encode_residual-after_cache_flush", n * 4.5625,
+         (lambda: kvq.encode_residual(x1, R0, "key", "int4", 64, out=rr), lambda: flush.fill_(1))),
+    ]
     stream = torch.cuda.current_stream(dev)
     for _, _, fn in calls:  # warmup
-        fn()
+        (fn[0] if isinstance(fn, tuple) else fn)()
     torch.cuda.synchronize()
     out = {}
     for name, nbytes, fn in calls:
+        pre = None
+        if isinstance(fn, tuple):  # (op, untimed preparation run before each timed call)
+            fn, pre = fn
         ev = []
         for _ in range(reps):
+            if pre is not None:
+                pre()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()
@@ -212,9 +250,16 @@ def cpu_baseline(T_sample: int):
             oracle.decode_residual(r, R0)
             total_bytes += sum(algo_bytes(op, fmt, n) for op in OPS)
     dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"leading {T_sample} of {T_FULL} tokens (H=8, D=128), all 16 ops of one step, "
-                      f"single-threaded C oracle, {dt:.1f} s"}
+                      f"single-threaded C oracle, {dt:.1f} s",
+            "cpu": cpu_model}
 
 
 def main() -> int:

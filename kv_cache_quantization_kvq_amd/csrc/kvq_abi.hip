@@ -151,9 +151,12 @@ kvq_status view_of_paged(const kvq_paged* x, View* v) {
 // spans D/8 lanes of one wave).
 bool row_vec_dims(int64_t D) { return D % 8 == 0 && is_pow2(D / 8) && D / 8 <= 64; }
 
-// Geometry of the 8-channel vector path.
+// Geometry of the 8-channel vector path. Rows shorter than 64 chunks whose chunk count divides
+// 64 use lane groups (several row tiles per task, task_lane); with VALUE groups (lane_groups
+// of lpg lanes) the groups must also tile a row's lanes.
 template <typename Args>
-void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, int rows_per_task) {
+void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, int rows_per_task,
+                       bool lane_groups_in_rows = true) {
     a.D8 = (int32_t)(D / 8);
     a.C8 = (int32_t)(H * (D / 8));
     a.n_slabs = (int32_t)cdiv(a.C8, 64);
@@ -163,6 +166,12 @@ void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, i
     a.div_D8 = fastdiv_make((uint32_t)a.D8);
     a.div_slabs = fastdiv_make((uint32_t)a.n_slabs);
     a.n_tasks = (uint32_t)(cdiv(rows, rows_per_task) * a.n_slabs);
+    a.ri_shift = a.c8_shift = 0;
+    if (a.C8 < 64 && is_pow2(a.C8) && (!lane_groups_in_rows || a.C8 % a.lpg == 0)) {
+        a.c8_shift = log2i(a.C8);
+        a.ri_shift = 6 - a.c8_shift;
+        a.n_tasks = (uint32_t)cdiv(cdiv(rows, rows_per_task), (int64_t)1 << a.ri_shift);
+    }
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
@@ -218,7 +227,7 @@ kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* po
         if (row_format(format) || kind == KVQ_VALUE) {
             fill_vec_geometry(a, rows, H, D, row_format(format) ? 8 : G, KVQ_ENCODE_ROWS_V);
         } else {
-            fill_vec_geometry(a, rows, H, D, G, G);
+            fill_vec_geometry(a, rows, H, D, G, G, false);  // KEY groups run over tokens
         }
         a.div_C8 = fastdiv_make((uint32_t)a.C8);
     }
@@ -335,7 +344,7 @@ kvq_status decode_run(const kvq_packed* p, int64_t rows, const kvq_tensor* prev,
         vec = vec && !src && (G % 8 == 0) && (G % KVQ_DECODE_ROWS == 0) &&
               (p->format == KVQ_INT4 ? (aligned(p->meta0, 16) && aligned(p->meta1, 16)) : aligned(p->meta0, 8));
     }
-    if (vec) fill_vec_geometry(a, rows, H, D, G, KVQ_DECODE_ROWS);
+    if (vec) fill_vec_geometry(a, rows, H, D, G, KVQ_DECODE_ROWS, p->kind == KVQ_VALUE);
     return hip_status(launch_decode(p->format, p->kind, a, prev != nullptr, positions != nullptr, vec, stream));
 }
 

@@ -31,7 +31,7 @@ __device__ __forceinline__ uint32_t finish_pair(float y0, float y1, uint32_t pre
     return pack_bf16x2(__fadd_rn(bf16lo(prev_word), bf16lo(yb)), __fadd_rn(bf16hi(prev_word), bf16hi(yb)));
 }
 
-template <int FMT, int KIND, bool ADD, bool SCATTER>
+template <int FMT, int KIND, bool ADD, bool SCATTER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     constexpr int RW = KVQ_DECODE_ROWS;
     __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
@@ -40,9 +40,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     const uint32_t task =
         __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, gridDim.x) * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
-    const uint32_t rtile = fdiv(task, a.div_slabs);
-    const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
-    const uint32_t c8raw = slab * 64u + lane;
+    uint32_t rtile, c8raw;
+    task_lane<LG>(a, task, lane, rtile, c8raw);  // with LG a lane group past the last row tile stores nothing
     const bool valid = c8raw < (uint32_t)a.C8;
     const uint32_t c8 = valid ? c8raw : (uint32_t)a.C8 - 1u;  // idle lanes read a valid chunk
     const uint32_t h = fdiv(c8, a.div_D8);
@@ -88,7 +87,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     // KEY: per-channel metadata of this task's token group (G % RW == 0), loaded once
     float ks[8], km[8];
     if constexpr (KIND == KIND_KEY) {
-        const size_t mbase = ((size_t)(r0 / a.G) * (uint32_t)a.C8 + c8) * 8u;
+        // (a lane group past the last row tile, which stores nothing, reads the last group's)
+        const size_t mbase = ((size_t)(min<int64_t>(r0, a.rows - 1) / a.G) * (uint32_t)a.C8 + c8) * 8u;
         if constexpr (FMT == FMT_INT4) {
             const u32x4 mins = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.meta0) + mbase);
             const u32x4 scs = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.meta1) + mbase);
@@ -241,9 +241,12 @@ inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 
 
 template <int FMT, int KIND, bool ADD, bool SCATTER>
 hipError_t decode_launch(const DecArgs& a, bool vec, hipStream_t s) {
-    if (vec) {
-        hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, SCATTER>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads), 0,
-                           s, a);
+    if (vec && a.ri_shift > 0) {
+        hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, SCATTER, true>), dim3(ceil_div_u(a.n_tasks, 4)),
+                           dim3(kThreads), 0, s, a);
+    } else if (vec) {
+        hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, SCATTER, false>), dim3(ceil_div_u(a.n_tasks, 4)),
+                           dim3(kThreads), 0, s, a);
     } else {
         const uint64_t n = (uint64_t)a.rows * a.H * ((a.D + 1) / 2);
         hipLaunchKernelGGL((k_decode_gen<FMT, KIND, ADD, SCATTER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0,

@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
 // ---- VALUE, vector path ------------------------------------------------------------------------
 
 // A wave task is RW consecutive rows of one 64-chunk column slab.
-template <int FMT, bool DIFF, bool GATHER>
+template <int FMT, bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
     constexpr int RW = kEncodeRowsV;
     __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
@@ -121,9 +121,8 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
     const int lane = threadIdx.x & 63;
     const uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
-    const uint32_t rtile = fdiv(task, a.div_slabs);
-    const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
-    const uint32_t c8raw = slab * 64u + lane;
+    uint32_t rtile, c8raw;
+    task_lane<LG>(a, task, lane, rtile, c8raw);  // with LG a lane group past the last row tile stores nothing
     const bool valid = c8raw < (uint32_t)a.C8;
     const uint32_t c8 = valid ? c8raw : (uint32_t)a.C8 - 1u;  // idle lanes read a valid chunk
     const uint32_t h = fdiv(c8, a.div_D8);
@@ -179,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 
 // An item is one token group (G rows) of one 64-chunk column slab. WPG waves share an item,
 // RPW rows each; a block of WPB waves holds WPB/WPG items.
-template <int FMT, int G, bool DIFF, bool GATHER>
+template <int FMT, int G, bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(EncArgs a) {
     constexpr int WPG = key_waves_per_group(G);
     constexpr int RPW = key_rows_per_wave(G);
@@ -201,10 +200,10 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
     const uint32_t item_raw = blockIdx.x * (uint32_t)IPB + (uint32_t)(wave / WPG);
     const bool item_ok = item_raw < a.n_tasks;
     const uint32_t item = item_ok ? item_raw : a.n_tasks - 1u;  // surplus waves mirror the last item
-    const uint32_t b = fdiv(item, a.div_slabs);
-    const uint32_t slab = item - b * (uint32_t)a.n_slabs;
-    const uint32_t c8raw = slab * 64u + lane;
-    const bool valid = item_ok && c8raw < (uint32_t)a.C8;
+    uint32_t b, c8raw;  // token group and chunk of this lane
+    task_lane<LG>(a, item, lane, b, c8raw);
+    // with LG a lane group past the last token group loads rows of the last one and stores nothing
+    const bool valid = item_ok && c8raw < (uint32_t)a.C8 && (int64_t)b * G < a.rows;
     const uint32_t c8 = (c8raw < (uint32_t)a.C8) ? c8raw : (uint32_t)a.C8 - 1u;
     const uint32_t h = fdiv(c8, a.div_D8);
     const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
@@ -322,7 +321,7 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
         }
     }
     if constexpr (GATHER) {
-        if (slab == 0 && lane == 0)
+        if (c8raw == 0)  // one lane per token group (per lane group with LG)
             for (int i = 0; i < nr; ++i) a.pos_out[r0 + i] = a.pos[r0 + i];
     }
 }
@@ -467,7 +466,7 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m) {
     return max(max(sm[0], sm[1]), max(sm[2], sm[3]));
 }
 
-template <bool DIFF, bool GATHER>
+template <bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_amax_vec(EncArgs a) {
     constexpr int RW = DIFF ? 4 : 8;
     const int lane = threadIdx.x & 63;
@@ -475,9 +474,8 @@ __global__ __launch_bounds__(kThreads) void k_amax_vec(EncArgs a) {
     const uint32_t nwaves = gridDim.x * 4u;
     for (uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6)); task < a.n_tasks;
          task += nwaves) {
-        const uint32_t rtile = fdiv(task, a.div_slabs);
-        const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
-        const uint32_t c8raw = slab * 64u + lane;
+        uint32_t rtile, c8raw;  // with LG a lane group past the last row tile re-reads the last row
+        task_lane<LG>(a, task, lane, rtile, c8raw);
         const uint32_t c8 = (c8raw < (uint32_t)a.C8) ? c8raw : (uint32_t)a.C8 - 1u;
         const uint32_t h = fdiv(c8, a.div_D8);
         const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
@@ -543,16 +541,24 @@ inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 
 template <int FMT, int G, bool DIFF, bool GATHER>
 void launch_key_vec(const EncArgs& a, hipStream_t s) {
     constexpr uint32_t ipb = (uint32_t)(key_waves_per_block(G) / key_waves_per_group(G));
-    hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER>), dim3(ceil_div_u(a.n_tasks, ipb)),
-                       dim3(64 * key_waves_per_block(G)), 0, s, a);
+    if (a.ri_shift > 0)
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true>), dim3(ceil_div_u(a.n_tasks, ipb)),
+                           dim3(64 * key_waves_per_block(G)), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false>), dim3(ceil_div_u(a.n_tasks, ipb)),
+                           dim3(64 * key_waves_per_block(G)), 0, s, a);
 }
 
 template <int FMT, bool DIFF, bool GATHER>
 hipError_t encode_dispatch(int kind, const EncArgs& a, bool vec, hipStream_t s) {
     if (vec) {
         if (kind == KIND_VALUE) {
-            hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads), 0,
-                               s, a);
+            if (a.ri_shift > 0)
+                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, true>), dim3(ceil_div_u(a.n_tasks, 4)),
+                                   dim3(kThreads), 0, s, a);
+            else
+                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, false>), dim3(ceil_div_u(a.n_tasks, 4)),
+                                   dim3(kThreads), 0, s, a);
         } else {
             switch (a.G) {
                 case 16:
@@ -603,10 +609,15 @@ hipError_t amax_dispatch(const EncArgs& a, bool vec, hipStream_t s) {
         // amax tiles: 8 rows per wave task (4 for a residual, which loads two tensors)
         const uint32_t rw = DIFF ? 4u : 8u;
         EncArgs b = a;
-        b.n_tasks = (uint32_t)((a.rows + rw - 1) / rw) * (uint32_t)a.n_slabs;
+        const uint64_t tiles = (uint64_t)((a.rows + rw - 1) / rw);
+        b.n_tasks = a.ri_shift > 0 ? (uint32_t)((tiles + (1u << a.ri_shift) - 1) >> a.ri_shift)
+                                   : (uint32_t)tiles * (uint32_t)a.n_slabs;
         blocks = ceil_div_u(b.n_tasks, 4);
         if (blocks > kAmaxMaxBlocks) blocks = kAmaxMaxBlocks;
-        hipLaunchKernelGGL((k_amax_vec<DIFF, GATHER>), dim3(blocks), dim3(kThreads), 0, s, b);
+        if (a.ri_shift > 0)
+            hipLaunchKernelGGL((k_amax_vec<DIFF, GATHER, true>), dim3(blocks), dim3(kThreads), 0, s, b);
+        else
+            hipLaunchKernelGGL((k_amax_vec<DIFF, GATHER, false>), dim3(blocks), dim3(kThreads), 0, s, b);
     } else {
         const uint64_t total = (uint64_t)a.rows * a.H * a.D;
         const uint64_t want = (total + kThreads * 4 - 1) / (kThreads * 4);

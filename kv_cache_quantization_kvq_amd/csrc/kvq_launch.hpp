@@ -60,6 +60,7 @@ struct EncArgs {
     // vector-path geometry: C8 = H*D/8 chunks of 8 channels per row; a VALUE group spans
     // lpg = G/8 = 1 << lpg_shift lanes, ngr = C8 / lpg groups per row
     int32_t C8, D8, n_slabs, lpg, lpg_shift, ngr;
+    int32_t ri_shift, c8_shift;  // lane groups of short rows (see task_lane); 0 when unused
     uint32_t n_tasks;
     FastDiv div_D8, div_slabs, div_C8;
     uint8_t* codes;
@@ -87,9 +88,26 @@ struct DecArgs {
     int64_t rows;
     int32_t H, D, G;
     int32_t C8, D8, n_slabs, lpg, lpg_shift, ngr;
+    int32_t ri_shift, c8_shift;  // lane groups of short rows (see task_lane); 0 when unused
     uint32_t n_tasks;
     FastDiv div_D8, div_slabs;
 };
+
+// Lanes of a vector-path task. Rows of 64 or more 8-channel chunks (or a count that does not
+// divide 64): the wave's 64 lanes take 64 consecutive chunks (a slab) of one row tile, and a
+// task is (row tile, slab). Shorter rows (LG): C8 = 1 << c8_shift chunks per row, and the lanes
+// form 1 << ri_shift groups of C8, group k taking row tile (task << ri_shift) + k, so every lane
+// has work (a head-sharded [T, 1, 128] tensor has 16 chunks per row).
+template <bool LG, class Args>
+__device__ __forceinline__ void task_lane(const Args& a, uint32_t task, int lane, uint32_t& rtile, uint32_t& c8raw) {
+    if constexpr (LG) {
+        rtile = (task << a.ri_shift) + ((uint32_t)lane >> a.c8_shift);
+        c8raw = (uint32_t)lane & ((1u << a.c8_shift) - 1u);
+    } else {
+        rtile = fdiv(task, a.div_slabs);
+        c8raw = (task - rtile * (uint32_t)a.n_slabs) * 64u + (uint32_t)lane;
+    }
+}
 
 struct CopyArgs {
     const uint16_t* src;

@@ -101,15 +101,14 @@ __device__ __forceinline__ uint2 fp8_chunk(const u32x4& v, const Fp8Row& rs) {
 }
 
 // One wave task: RW rows of a 64-chunk slab (the VALUE encoder's tiling).
-template <int FMT, bool DIFF, bool GATHER>
+template <int FMT, bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
     constexpr int RW = KVQ_ENCODE_ROWS_V;
     const int lane = threadIdx.x & 63;
     const uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
-    const uint32_t rtile = fdiv(task, a.div_slabs);
-    const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
-    const uint32_t c8raw = slab * 64u + lane;
+    uint32_t rtile, c8raw;
+    task_lane<LG>(a, task, lane, rtile, c8raw);
     const bool valid = c8raw < (uint32_t)a.C8;
     const uint32_t c8 = valid ? c8raw : (uint32_t)a.C8 - 1u;
     const uint32_t h = fdiv(c8, a.div_D8);
@@ -211,16 +210,15 @@ __device__ __forceinline__ uint32_t row_finish(float y0, float y1, uint32_t prev
     return pack_bf16x2(__fadd_rn(bf16lo(prev_word), bf16lo(yb)), __fadd_rn(bf16hi(prev_word), bf16hi(yb)));
 }
 
-template <int FMT, bool ADD, bool SCATTER>
+template <int FMT, bool ADD, bool SCATTER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_row_decode_vec(DecArgs a) {
     constexpr int RW = KVQ_DECODE_ROWS;
     const int lane = threadIdx.x & 63;
     const uint32_t task =
         __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, gridDim.x) * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
-    const uint32_t rtile = fdiv(task, a.div_slabs);
-    const uint32_t slab = task - rtile * (uint32_t)a.n_slabs;
-    const uint32_t c8raw = slab * 64u + lane;
+    uint32_t rtile, c8raw;
+    task_lane<LG>(a, task, lane, rtile, c8raw);
     const bool valid = c8raw < (uint32_t)a.C8;
     const uint32_t c8 = valid ? c8raw : (uint32_t)a.C8 - 1u;
     const uint32_t h = fdiv(c8, a.div_D8);
@@ -330,9 +328,12 @@ inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 
 
 template <int FMT, bool DIFF, bool GATHER>
 void row_encode_launch(const EncArgs& a, bool vec, hipStream_t s) {
-    if (vec)
-        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads), 0, s,
-                           a);
+    if (vec && a.ri_shift > 0)
+        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, true>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
+                           0, s, a);
+    else if (vec)
+        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, false>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
+                           0, s, a);
     else
         hipLaunchKernelGGL((k_row_encode_gen<FMT, DIFF, GATHER>), dim3(ceil_div_u((uint64_t)a.rows * a.H, kThreads)),
                            dim3(kThreads), 0, s, a);
@@ -340,9 +341,12 @@ void row_encode_launch(const EncArgs& a, bool vec, hipStream_t s) {
 
 template <int FMT, bool ADD, bool SCATTER>
 void row_decode_launch(const DecArgs& a, bool vec, hipStream_t s) {
-    if (vec) {
-        hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads), 0, s,
-                           a);
+    if (vec && a.ri_shift > 0) {
+        hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, true>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
+                           0, s, a);
+    } else if (vec) {
+        hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, false>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
+                           0, s, a);
     } else {
         const uint64_t n = (uint64_t)a.rows * a.H * ((a.D + 1) / 2);
         hipLaunchKernelGGL((k_row_decode_gen<FMT, ADD, SCATTER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0, s,
