@@ -26,9 +26,10 @@ pack and residual encode/decode, and decode attention of 64 query heads over the
 packed planes it reads. Context lines: INT4 and NVFP4 K ops on one KV head's shard
 ([T, 1, 128], the per-GPU shape of head sharding over 8 GPUs); the 268 MB tensor copied by this
 library's row-copy kernel and by the runtime's device-to-device copy (read + write bytes); and
-the dominant bulk op timed after a 1 GiB write that evicts the 256 MB Infinity Cache (inside the
-step it follows the op that wrote one of its inputs). Algorithmic bytes per element for a row format with c code bytes and
-m = block-scale bytes + 4/D row-scale bytes per element: pack and unpack 2 + c + m, residual
+the dominant bulk op on a clean cache (a 1 GiB write, then a 1 GiB read, before each call; inside
+the step it follows the op that wrote one of its inputs). Algorithmic bytes per element for a
+row format with c code bytes and m = block-scale bytes + 4/D row-scale bytes per element: pack
+and unpack 2 + c + m, residual
 encode and decode 4 + c + m; page-local INT4 G16 K 2.75; a slot write or read of N rows moves
 N*H*D*(2 + c + m) bytes plus 4 B per slot id; a windowed op moves the codec bytes of its
 T - 20 middle rows plus the 20 protected rows read and written in bf16.
@@ -167,8 +168,9 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
     ]
     # context: the same 268 MB copied by a plain row-copy kernel of this library (a sparse residual
     # with no rows decodes out of place as one copy) and by the runtime's device-to-device copy;
-    # and the dominant bulk op timed right after a 1 GiB write that evicts the 256 MB Infinity
-    # Cache (in the step it follows the op that wrote its input)
+    # and the dominant bulk op on a clean cache: a 1 GiB write then a 1 GiB read evict the 256 MB
+    # Infinity Cache without leaving dirty lines (in the step the op follows the unpack that
+    # wrote one of its inputs, part of which it then reads from that cache)
     cdst = torch.empty_like(x0)
     empty = kvq.encode_residual(x0, x0, "key", "int4", 64, positions=torch.zeros(0, dtype=torch.int32, device=dev))
     flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)
@@ -177,8 +179,8 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
     calls += [
         ("context-copy_kernel-268MB", 4 * n, lambda: kvq.decode_residual(empty, x0, out=cdst)),
         ("context-d2d_copy-268MB", 4 * n, lambda: cdst.copy_(x0)),
-        ("int4-key-encode_residual-after_cache_flush", n * 4.5625,
-         (lambda: kvq.encode_residual(x1, R0, "key", "int4", 64, out=rr), lambda: flush.fill_(1))),
+        ("int4-key-encode_residual-after_cache_eviction", n * 4.5625,
+         (lambda: kvq.encode_residual(x1, R0, "key", "int4", 64, out=rr), lambda: (flush.fill_(1), torch.amax(flush)))),
     ]
     stream = torch.cuda.current_stream(dev)
     for _, _, fn in calls:  # warmup
