@@ -317,7 +317,10 @@ __device__ __forceinline__ void v_prep(const TileRaw<FMT>& x, const Fp4Table* ta
             v.s[j] = __uint_as_float(x.vm[j]);
         } else {
             v.w[j] = x.vc[j][0];
-            v.s[j] = (FMT == FMT_NVFP4) ? tab->e[x.vm[j] & 0x7Fu][0] : nvfp4_row_sdec(x.vm[j], x.vg[j]);
+            if constexpr (FMT == FMT_NVFP4)
+                v.s[j] = tab->e[x.vm[j] & 0x7Fu][0];
+            else
+                v.s[j] = nvfp4_row_sdec(x.vm[j], x.vg[j]);
         }
     }
 }

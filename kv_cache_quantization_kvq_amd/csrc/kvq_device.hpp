@@ -404,16 +404,66 @@ __device__ __forceinline__ float fp4_global(uint32_t amax_bits) {
     return __builtin_isinf(g) ? 3.4028234663852886e38f : g;
 }
 
+// ---- NVFP4-row: per-row divisions without the IEEE division sequence -------------------------
+//
+// The encoder's per-row constants: a row's multiplier g = fl(2688 / amax), a block's decode scale
+// s_dec = fl(sf / g) and its reciprocal fl(1 / s_dec), by the Markstein correction of the INT4
+// quotient (decoders keep the plain division, which measured faster there): y = RN(1/b)
+// (rcp_rn), ylo = RN((1 - b y) y), q0 = fma(a, y, RN(a ylo)), q = fma(fma(-b, q0, a), y, q0), for
+// divisors b in [2^-100, 2^100]; other divisors divide. The inputs are finite positive bf16 amax
+// values (2^15 of them) and the 126 positive E4M3 scales, so the device probe compares all three
+// with the IEEE quotients exhaustively (every amax, every amax x code pair).
+struct RcpPair {
+    float b, y, ylo;
+    bool fast;
+};
+
+__device__ __forceinline__ RcpPair rcp_pair(float b) {
+    RcpPair p;
+    p.b = b;
+    p.fast = b >= 7.888609052210118e-31f && b <= 1.2676506002282294e30f;  // 2^-100, 2^100
+    p.y = rcp_rn(b);
+    p.ylo = __fmul_rn(__builtin_fmaf(-b, p.y, 1.0f), p.y);
+    return p;
+}
+
+// fl(a / b) for a >= 0
+__device__ __forceinline__ float quot_rn(float a, const RcpPair& p) {
+    if (__builtin_expect(!p.fast, 0)) return a / p.b;
+    const float q0 = __builtin_fmaf(a, p.y, __fmul_rn(a, p.ylo));
+    return __builtin_fmaf(__builtin_fmaf(-p.b, q0, a), p.y, q0);
+}
+
+// fp4_global without the IEEE division (same results; probe check [15])
+__device__ __forceinline__ float fp4_global_rn(uint32_t amax_bits) {
+    const float amax = bf16_to_f32(amax_bits);
+    if (amax == 0.0f) return 1.0f;
+    const float g = quot_rn(2688.0f, rcp_pair(amax));
+    return __builtin_isinf(g) ? 3.4028234663852886e38f : g;
+}
+
+// fp4_code_scales(c, g) without IEEE divisions, gp = rcp_pair(g) (probe checks [16], [17])
+__device__ __forceinline__ f32x2 fp4_code_scales_rn(uint32_t c, const RcpPair& gp) {
+    const float sf = e4m3_decode(c);
+    const float s_dec = quot_rn(sf, gp);
+    float r = 0.0f;
+    if (sf != 0.0f) {
+        const bool fast = s_dec >= 7.888609052210118e-31f && s_dec <= 1.2676506002282294e30f;
+        r = __builtin_expect(fast, 1) ? rcp_rn(s_dec) : 1.0f / s_dec;
+    }
+    return (f32x2){s_dec, r};
+}
+
 // Block constants for a multiplier that changes from row to row (NVFP4-row): the same values
-// as fp4_block, with the decode scale and its reciprocal divided out directly instead of
-// looked up in a per-launch table.
-__device__ __forceinline__ Fp4Block fp4_block_direct(uint32_t bamax_bits, float g) {
+// as fp4_block, with the decode scale and its reciprocal computed per row (gp = rcp_pair(g))
+// instead of looked up in a per-launch table.
+__device__ __forceinline__ Fp4Block fp4_block_direct(uint32_t bamax_bits, float g, const RcpPair& gp) {
     Fp4Block b;
     const float t6 = div_const<6>(bf16_to_f32(bamax_bits));
     float s = __fmul_rn(g, t6);
     s = (s <= 448.0f) ? s : 448.0f;
     b.code = e4m3_encode(s);
-    const f32x2 e = fp4_code_scales(b.code, g);
+    const f32x2 e = fp4_code_scales_rn(b.code, gp);
     b.s_dec = e[0];
     b.rcp = e[1];
     b.div = __builtin_isinf(e[1]);

@@ -137,10 +137,10 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
                 if (row_leader) reinterpret_cast<float*>(a.meta0)[hr] = rs.s;
             }
         } else {
-            const float g = fp4_global(amax);
+            const float g = fp4_global_rn(amax);
             // a 16-channel block is this lane and its neighbour (one lane when D = 8)
             const uint32_t bam = (lpr >= 2) ? max(am, dpp<0xB1>(am)) : am;
-            const Fp4Block fb = fp4_block_direct(bam, g);
+            const Fp4Block fb = fp4_block_direct(bam, g, rcp_pair(g));
             const uint32_t word = fp4_word(v[i], &fb, 0);
             if (i < nr && valid) {
                 reinterpret_cast<uint32_t*>(a.codes)[(size_t)wr * (uint32_t)a.C8 + c8] = word;
@@ -179,7 +179,8 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_gen(EncArgs a) {
             crow[dd] = (uint8_t)(e4m3_encode(m) | ((__float_as_uint(x) >> 24) & 0x80u));
         }
     } else {
-        const float g = fp4_global(amax);
+        const float g = fp4_global_rn(amax);
+        const RcpPair gp = rcp_pair(g);
         reinterpret_cast<float*>(a.meta1)[hr] = g;
         const int nb = (D + 15) / 16, Dp = (D + 1) / 2;
         uint8_t* crow = a.codes + hr * (size_t)Dp;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_gen(EncArgs a) {
             const int d0 = b * 16, d1 = min(D, d0 + 16);
             uint32_t bam = 0;
             for (int dd = d0; dd < d1; ++dd) bam = max(bam, row_load<DIFF>(a, t, h, dd) & 0x7FFFu);
-            const Fp4Block fb = fp4_block_direct(bam, g);
+            const Fp4Block fb = fp4_block_direct(bam, g, gp);
             srow[b] = (uint8_t)fb.code;
             for (int dd = d0; dd < d1; dd += 2) {
                 const uint32_t lo = fp4_code(bf16_to_f32(row_load<DIFF>(a, t, h, dd)), fb);

@@ -28,12 +28,17 @@
 //   [10] d = RN(m * scale) and its two neighbours for the 512 points m = h + k * ulp(h) / 2
 //        (h = 0.5 ... 15.5, k = -16 ... 15), i.e. quotients at and next to every half-integer
 //        and float midpoint near it, plus one pseudo-random d in [scale / 2, 16 scale): the
-//        quotient bits must match; for d = RN(scale * 2^-j), j = 3 ... 40, the code (rint) must
+//        quotient bits must match; for d = RN(scale * 2^-j), j = 3 ... 40, the code (rint) must match;
 // and, in a third kernel, the FP8-row quotient kvq::fp8_quot(x, fp8_row_scale(scale)) against
 // the IEEE x / scale for every scale significand at eight exponents from 2^-90 to 2^99:
 //   [13] signed x = RN(m * scale) and its two neighbours, m a float midpoint in a pseudo-random
 //        binade from 2^-12 to 2^9 with a pseudo-random significand: the quotient bits must
-//        match; for tiny quotients (scale * 2^-11 ... 2^-48) the E4M3 code must
+//        match; for tiny quotients (scale * 2^-11 ... 2^-48) the E4M3 codes must match;
+// and, in a fourth kernel, the NVFP4-row per-row constants without the IEEE division, for
+// every finite positive bf16 row amax (0x0001 ... 0x7F7F) and every E4M3 scale code 0 ... 126:
+//   [15] kvq::fp4_global_rn(amax) == kvq::fp4_global(amax) (the IEEE 2688 / amax)
+//   [16] kvq::fp4_code_scales_rn(c, rcp_pair(g))[0] == fl(e4m3(c) / g), g the row multiplier
+//   [17] its reciprocal [1] == fl(1 / s_dec) (+inf where that overflows, 0 for code 0)
 // counting mismatches and recording the smallest mismatching input of each check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,7 +49,7 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kChecks = 15;
+constexpr int kChecks = 18;
 
 __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint32_t* first) {
     unsigned long long c[kChecks] = {};
@@ -231,6 +236,29 @@ __global__ __launch_bounds__(256) void k_probe_fp8div(unsigned long long* counts
     }
 }
 
+// NVFP4-row constants: one row amax per thread, all scale codes.
+__global__ __launch_bounds__(256) void k_probe_nvfp4row(unsigned long long* counts, uint32_t* first) {
+    const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x + 1u;  // bf16 magnitude bits
+    if (b > 0x7F7Fu) return;
+    unsigned long long c[3] = {0, 0, 0};
+    const float g = fp4_global(b);
+    const float gr = fp4_global_rn(b);
+    if (__float_as_uint(g) != __float_as_uint(gr)) ++c[0];
+    const RcpPair gp = rcp_pair(gr);
+    for (uint32_t code = 0; code <= 126u; ++code) {
+        const f32x2 e = fp4_code_scales(code, g);
+        const f32x2 f = fp4_code_scales_rn(code, gp);
+        if (__float_as_uint(e[0]) != __float_as_uint(f[0])) ++c[1];
+        if (__float_as_uint(e[1]) != __float_as_uint(f[1])) ++c[2];
+    }
+    for (int k = 0; k < 3; ++k) {
+        if (c[k]) {
+            atomicAdd(&counts[15 + k], c[k]);
+            atomicMin(&first[15 + k], b);
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_host) {
@@ -245,6 +273,8 @@ extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_ho
     hipLaunchKernelGGL(k_probe_div, dim3(4096), dim3(256), 0, 0, counts, first);
     if (hipGetLastError() != hipSuccess) return 3;
     hipLaunchKernelGGL(k_probe_fp8div, dim3(4096), dim3(256), 0, 0, counts, first);
+    if (hipGetLastError() != hipSuccess) return 3;
+    hipLaunchKernelGGL(k_probe_nvfp4row, dim3((0x7F7Fu + 255u) / 256u), dim3(256), 0, 0, counts, first);
     if (hipGetLastError() != hipSuccess) return 3;
     if (hipDeviceSynchronize() != hipSuccess) return 4;
     hipMemcpy(counts_host, counts, kChecks * sizeof(unsigned long long), hipMemcpyDeviceToHost);

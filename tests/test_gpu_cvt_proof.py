@@ -13,7 +13,10 @@ quotients at and next to every half-integer and float midpoint, for every scale 
 eight exponents (about 1.5e11 cases); the E4M3 conversion instructions against the integer E4M3
 rounding (every binary32 of magnitude up to 448) and decode (every finite code); and the
 branch-free FP8-row quotient against the IEEE division on signed quotients at and next to float
-midpoints from 2^-12 to 2^9 for every scale significand at eight exponents. The software formulations are written from the format definitions and are pinned
+midpoints from 2^-12 to 2^9 for every scale significand at eight exponents; and the NVFP4-row
+row multiplier, block decode scale and its reciprocal computed without the IEEE division sequence
+against the IEEE quotients for every finite positive bf16 row amax and every E4M3 scale code.
+The software formulations are written from the format definitions and are pinned
 against the oracle end to end by the parity tests.
 """
 
@@ -30,7 +33,10 @@ NAMES = ["bf16", "f16", "fp4 encode (all finite)", "fp4 encode (|x| <= 8)", "fp4
          "v_rcp_f32 within 1 ulp", "reciprocal + Newton step == RN(1/x)",
          "INT4 quotient (Markstein) == IEEE d / scale",
          "v_cvt_pk_fp8_f32 == E4M3 encode (|x| <= 448)", "v_cvt_pk_f32_fp8 == E4M3 decode",
-         "FP8-row quotient (Markstein) == IEEE x / scale", "INT4 decode product exact (one FMA)"]
+         "FP8-row quotient (Markstein) == IEEE x / scale", "INT4 decode product exact (one FMA)",
+         "NVFP4-row g = 2688 / amax without division (every bf16 amax)",
+         "NVFP4-row s_dec = e4m3 / g without division (every amax x code)",
+         "NVFP4-row 1 / s_dec without division (every amax x code)"]
 
 
 def test_conversion_instructions_match_software_rounding():
