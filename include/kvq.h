@@ -272,7 +272,8 @@ size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq);
  *            tokens for K and 8 to 128 channels for V; code planes 16-byte aligned, metadata
  *            planes aligned to their element size (INT4 and NVFP4: 16 bytes)
  *   k_res, v_res  optional dense residuals of the same shape (formats may differ from k, v)
- *   Hq       a multiple of H with Hq / H <= 16
+ *   Hq       a multiple of H (query heads per KV head beyond 16 run as several 16-row tiles, each
+ *            reading the KV head's cache)
  *   out      device float [Hq, 128]
  *   workspace  device memory of at least kvq_attention_workspace_bytes(T, H, Hq) bytes
  * Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, MISMATCH, WORKSPACE, HIP. */

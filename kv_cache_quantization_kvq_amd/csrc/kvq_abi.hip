@@ -675,7 +675,7 @@ kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, 
     if (!q || !out || !k || !v || !workspace) return KVQ_ERR_NULL;
     if ((k_res == nullptr) != (v_res == nullptr)) return KVQ_ERR_NULL;
     const int64_t T = k->rows, H = k->H;
-    if (T < 1 || H < 1 || Hq < 1 || Hq % H != 0 || Hq / H > 16) return KVQ_ERR_SHAPE;
+    if (T < 1 || H < 1 || Hq < 1 || Hq % H != 0 || Hq >= kMaxDim || Hq / H > 16 * 65535) return KVQ_ERR_SHAPE;
     AttnArgs a;
     memset(&a, 0, sizeof a);
     kvq_status st = attn_operand(k, KVQ_KEY, T, H, &a.k);

@@ -9,8 +9,10 @@
 // would produce, bf16 value for bf16 value; scores and the softmax run in FP32, P is rounded to
 // bf16 for the PV product, accumulation is FP32.
 //
-// Work split (flash decoding): a block owns one KV head and a range of tokens; each of its 4
-// waves walks 16-token sub-tiles with its own online softmax; the waves meet in LDS, the block
+// Work split (flash decoding): a block owns one KV head, a range of tokens and a tile of up to 16
+// of the head's query rows (grid z; more than 16 query heads per KV head take several tiles,
+// each reading the same K/V); each of its 4 waves walks 16-token sub-tiles with its own online
+// softmax; the waves meet in LDS, the block
 // writes one partial (max, sum, unnormalized output) per query row, and a second kernel folds the
 // partials of all blocks.
 //
@@ -510,10 +512,13 @@ __global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) 
     const int64_t w_begin = t_begin + (int64_t)wave * w_len;
     const int64_t w_end = min<int64_t>(t_end, w_begin + w_len);
 
-    // Q^T operand: row r (query head h * rep + r), channels 32q + 4s + j for step s
+    // Q^T operand: row r of this block's query tile (query head h * rep + row0 + r), channels
+    // 32q + 4s + j for step s; rows past the tile are zero
+    const int row0 = 16 * (int)blockIdx.z;
+    const int nrows = min(16, a.rep - row0);
     uint32_t qw[16];
-    if (r < a.rep) {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((size_t)h * a.rep + r) * kD + 32 * q);
+    if (r < nrows) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((size_t)h * a.rep + row0 + r) * kD + 32 * q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const u32x4 v = qp[i];
@@ -613,8 +618,8 @@ __global__ __launch_bounds__(64 * kWaves, RFMT == KVQ_ATTN_NO_RESIDUAL ? 4 : 3) 
         s_l[wave][r] = l_row;
     }
     __syncthreads();
-    const size_t pbase = ((size_t)h * a.n_split + blockIdx.x) * a.rep;
-    for (int idx = threadIdx.x; idx < a.rep * kD; idx += 64 * kWaves) {
+    const size_t pbase = ((size_t)h * a.n_split + blockIdx.x) * a.rep + row0;
+    for (int idx = threadIdx.x; idx < nrows * kD; idx += 64 * kWaves) {
         const int row = idx / kD, c = idx - row * kD;
         float M = s_m[0][row];
 #pragma unroll
@@ -729,14 +734,15 @@ template <int FMT, int RFMT>
 hipError_t attn_launch(AttnArgs a, hipStream_t s) {
     const int32_t bound = a.n_split;
     if (bound < 1 || bound > KVQ_ATTN_MAX_SPLIT) return hipErrorInvalidValue;  // combine's weight table
+    const int n_qt = (a.rep + 15) / 16;  // 16-row query tiles per KV head (grid z)
     const int resident = resident_blocks<FMT, RFMT>();
-    const int64_t want = resident > 0 ? std::max<int64_t>(1, resident / a.H) : bound;
+    const int64_t want = resident > 0 ? std::max<int64_t>(1, resident / ((int64_t)a.H * n_qt)) : bound;
     const int64_t splits = std::min<int64_t>(want, bound);
     const int64_t per = (a.T + 64 * splits - 1) / (64 * splits);
     a.tc = 64 * per;
     a.n_split = (int32_t)((a.T + a.tc - 1) / a.tc);  // <= splits
     a.part_ml = a.part_o + (size_t)a.H * a.n_split * a.rep * kD;
-    hipLaunchKernelGGL((k_attn_split<FMT, RFMT>), dim3(a.n_split, a.H), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL((k_attn_split<FMT, RFMT>), dim3(a.n_split, a.H, n_qt), dim3(64 * kWaves), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(a.H * a.rep)), dim3(256), 0, s, a);

@@ -53,6 +53,20 @@ def test_random_vs_oracle(fmt, gk, gv, T, H, Hq):
     check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"{fmt} T={T}")
 
 
+@pytest.mark.parametrize("fmt,gk,gv", [("int4", 64, 64), ("nvfp4", 16, 16), ("fp8_row", 0, 0)])
+@pytest.mark.parametrize("T,H,Hq", [(500, 1, 40), (300, 2, 64), (77, 1, 128), (1000, 4, 68)])
+def test_many_query_heads_per_kv_head(fmt, gk, gv, T, H, Hq):
+    """More than 16 query heads per KV head (multi-query models): 16-row query tiles."""
+    rng = np.random.default_rng(T + Hq)
+    k, v = normal_kv(rng, T, H, D), normal_kv(rng, T, H, D)
+    q = bf16_bits(rng.standard_normal((Hq, D)))
+    gk_, gv_, ok, ov = packed_pair(k, v, fmt, gk, gv)
+    out = kvq.decode_attention(to_dev(q), gk_, gv_).cpu().numpy()
+    kr, vr = reconstruct(ok), reconstruct(ov)
+    want = decode_attention(q, kr, vr, 1.0 / np.sqrt(D))
+    check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"{fmt} T={T} H={H} Hq={Hq}")
+
+
 @pytest.mark.parametrize("fmt,gk,gv", FORMS)
 @pytest.mark.parametrize("T", [16, 333, 5000])
 def test_zero_query_is_mean_of_v(fmt, gk, gv, T):
