@@ -252,10 +252,11 @@ kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int6
 kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
                              const kvq_tensor* prev, const kvq_tensor* out, hipStream_t stream);
 
-/* Bytes of device workspace kvq_decode_attention needs for T cached tokens, H KV heads and Hq
- * query heads (per-block partial maxima, sums and unnormalized outputs); 0 for invalid sizes.
- * No initialization is needed. Calls that may run concurrently need distinct workspaces. */
-size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq);
+/* Bytes of device workspace kvq_decode_attention needs for T cached tokens, H KV heads, Hq
+ * query heads and head_dim D (per-block partial maxima, sums and unnormalized outputs); 0 for
+ * invalid sizes. No initialization is needed. Calls that may run concurrently need distinct
+ * workspaces. */
+size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq, int64_t D);
 
 /* Decode attention that reads the packed cache directly ([PR166] reviews of the codec: the
  * hot-path option of dequantizing to BF16 in registers and keeping a BF16 matrix multiply, and
@@ -266,16 +267,17 @@ size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq);
  * of those dense residuals on top (both or neither). Scores and softmax run in FP32, the
  * probabilities are rounded to bf16 for the PV product (bf16 MFMA, FP32 accumulation), so the
  * output matches float64 attention over the decoded cache to within about 2^-9 of max |V|.
- *   q        device bf16 [Hq, 128], contiguous, 16-byte aligned
- *   k, v     packed KEY / VALUE tensors of one layer: rows = T >= 1, the same H, head_dim 128,
- *            dense, the same format (any of the four); INT4 groups a power of two, at least 16
- *            tokens for K and 8 to 128 channels for V; code planes 16-byte aligned, metadata
- *            planes aligned to their element size (INT4 and NVFP4: 16 bytes)
+ *   q        device bf16 [Hq, D], contiguous, 16-byte aligned
+ *   k, v     packed KEY / VALUE tensors of one layer: rows = T >= 1, the same H, the same
+ *            head_dim D of 64, 128 or 256, dense, the same format (any of the four); INT4 groups
+ *            a power of two, at least 16 tokens for K and from max(8, D/16) to D channels for V;
+ *            code planes 16-byte aligned, metadata planes aligned to their element size (INT4
+ *            and NVFP4: 16 bytes)
  *   k_res, v_res  optional dense residuals of the same shape (formats may differ from k, v)
  *   Hq       a multiple of H (query heads per KV head beyond 16 run as several 16-row tiles, each
  *            reading the KV head's cache)
- *   out      device float [Hq, 128]
- *   workspace  device memory of at least kvq_attention_workspace_bytes(T, H, Hq) bytes
+ *   out      device float [Hq, D]
+ *   workspace  device memory of at least kvq_attention_workspace_bytes(T, H, Hq, D) bytes
  * Errors: NULL, SHAPE, LAYOUT, FORMAT, GROUP, MISMATCH, WORKSPACE, HIP. */
 kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, const kvq_packed* v,
                                 const kvq_packed* k_res, const kvq_packed* v_res, float softmax_scale, float* out,

@@ -117,7 +117,7 @@ def library() -> ctypes.CDLL:
         lib.kvq_encode_window.restype = ctypes.c_int
         lib.kvq_decode_window.argtypes = [PP, P, I64, I64, TP, TP, P]
         lib.kvq_decode_window.restype = ctypes.c_int
-        lib.kvq_attention_workspace_bytes.argtypes = [I64, I64, I64]
+        lib.kvq_attention_workspace_bytes.argtypes = [I64, I64, I64, I64]
         lib.kvq_attention_workspace_bytes.restype = ctypes.c_size_t
         lib.kvq_decode_attention.argtypes = [P, I64, PP, PP, PP, PP, ctypes.c_float, P, P, ctypes.c_size_t, P]
         lib.kvq_decode_attention.restype = ctypes.c_int
@@ -477,7 +477,8 @@ def decode_attention(q: torch.Tensor, k: Packed, v: Packed, k_res: Optional[Pack
                      v_res: Optional[Packed] = None, scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step of attention over the packed cache (K, V, optionally one residual each):
-    q bf16 [Hq, 128] -> float32 [Hq, 128]; query head hq reads KV head hq // (Hq // H)."""
+    q bf16 [Hq, D] -> float32 [Hq, D] (D = 64, 128 or 256); query head hq reads KV head
+    hq // (Hq // H)."""
     dev = _device_of(q)
     if q.dtype != torch.bfloat16 or q.dim() != 2:
         raise ValueError("kvq: q must be a bf16 [Hq, head_dim] tensor")
@@ -485,7 +486,7 @@ def decode_attention(q: torch.Tensor, k: Packed, v: Packed, k_res: Optional[Pack
     Hq, Dq = q.shape
     if out is None:
         out = torch.empty((Hq, Dq), dtype=torch.float32, device=dev)
-    need = int(library().kvq_attention_workspace_bytes(k.rows, k.H, Hq))
+    need = int(library().kvq_attention_workspace_bytes(k.rows, k.H, Hq, k.D))
     key = (dev.index if dev.index is not None else torch.cuda.current_device(), torch.cuda.current_stream(dev).cuda_stream)
     ws = _attn_ws.get(key)
     if ws is None or ws.numel() < max(need, 4):

@@ -397,25 +397,28 @@ int32_t attn_split_bound(int64_t T, int64_t H) {
     return (int32_t)n;
 }
 
-size_t attn_workspace(int64_t T, int64_t H, int64_t rep) {
-    return (size_t)H * attn_split_bound(T, H) * rep * (KVQ_ATTN_D + 2) * sizeof(float);
+size_t attn_workspace(int64_t T, int64_t H, int64_t rep, int64_t D) {
+    return (size_t)H * attn_split_bound(T, H) * rep * (D + 2) * sizeof(float);
 }
 
-// One packed tensor of an attention call: dense, the expected kind, head_dim 128, any of the
-// four formats, and for INT4 a group size the kernel's tiling takes (a power of two, K at least
-// 16, V from 8 to 128).
+bool attn_head_dim(int64_t D) { return D == 64 || D == 128 || D == 256; }
+
+// One packed tensor of an attention call: dense, the expected kind, head_dim 64, 128 or 256, any
+// of the four formats, and for INT4 a group size the kernel's tiling takes (a power of two, K at
+// least 16 tokens, V from D/16 (at least 8) to D channels).
 kvq_status attn_operand(const kvq_packed* p, int kind, int64_t T, int64_t H, AttnPlanes* out) {
     kvq_status st = check_packed(p);
     if (st) return st;
     if (p->kind != kind || p->positions) return KVQ_ERR_MISMATCH;
-    if (p->D != KVQ_ATTN_D) return KVQ_ERR_SHAPE;
+    if (!attn_head_dim(p->D)) return KVQ_ERR_SHAPE;
     if (p->rows != T || p->H != H) return KVQ_ERR_MISMATCH;
     const int32_t G = p->group_size;
     int32_t gshift = 0;
     switch (p->format) {
         case KVQ_INT4:
             // powers of two: a K group holds whole 16-token sub-tiles, a V group whole 8-channel lanes
-            if (!is_pow2(G) || (kind == KVQ_KEY ? G < 16 : (G < 8 || G > KVQ_ATTN_D))) return KVQ_ERR_GROUP;
+            if (!is_pow2(G) || (kind == KVQ_KEY ? G < 16 : (G < 8 || G < p->D / 16 || G > p->D)))
+                return KVQ_ERR_GROUP;
             if (!aligned(p->meta0, 16) || !aligned(p->meta1, 16)) return KVQ_ERR_LAYOUT;
             gshift = log2i(G);
             break;
@@ -664,9 +667,11 @@ kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t si
                           nr, H, D, stream);
 }
 
-size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq) {
-    if (T < 1 || H < 1 || Hq < H || Hq % H != 0 || T >= kMaxDim || H >= kMaxDim) return 0;
-    return attn_workspace(T, H, Hq / H);
+size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq, int64_t D) {
+    if (T < 1 || H < 1 || Hq < H || Hq % H != 0 || T >= kMaxDim || H >= kMaxDim || Hq >= kMaxDim ||
+        !attn_head_dim(D))
+        return 0;
+    return attn_workspace(T, H, Hq / H, D);
 }
 
 kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, const kvq_packed* v,
@@ -682,20 +687,23 @@ kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, 
     if (!st) st = attn_operand(v, KVQ_VALUE, T, H, &a.v);
     if (st) return st;
     if (k->format != v->format) return KVQ_ERR_FORMAT;
+    if (v->D != k->D) return KVQ_ERR_MISMATCH;
     int rfmt = KVQ_ATTN_NO_RESIDUAL;
     if (k_res) {
         if ((st = attn_operand(k_res, KVQ_KEY, T, H, &a.rk))) return st;
         if ((st = attn_operand(v_res, KVQ_VALUE, T, H, &a.rv))) return st;
         if (k_res->format != v_res->format) return KVQ_ERR_FORMAT;
+        if (k_res->D != k->D || v_res->D != k->D) return KVQ_ERR_MISMATCH;
         rfmt = k_res->format;
     }
     if (!aligned(q, 16) || !aligned(out, 4) || !aligned(workspace, 4)) return KVQ_ERR_LAYOUT;
     const int64_t rep = Hq / H;
-    if (workspace_bytes < attn_workspace(T, H, rep)) return KVQ_ERR_WORKSPACE;
+    if (workspace_bytes < attn_workspace(T, H, rep, k->D)) return KVQ_ERR_WORKSPACE;
     a.q = static_cast<const uint16_t*>(q);
     a.T = T;
     a.H = (int32_t)H;
     a.rep = (int32_t)rep;
+    a.D = (int32_t)k->D;
     a.n_split = attn_split_bound(T, H);  // the launcher chooses the split within this bound
     a.qscale = softmax_scale * 1.4426950408889634f;  // scores in log2 units: exp(x) = exp2(x log2 e)
     a.part_o = static_cast<float*>(workspace);      // the launcher places part_ml after its split

@@ -119,8 +119,7 @@ struct CopyArgs {
     FastDiv div_C8, div_D8;
 };
 
-// Decode attention over packed K/V (head_dim 128; KVQ_ATTN_NO_RESIDUAL: no residual).
-#define KVQ_ATTN_D 128
+// Decode attention over packed K/V (head_dim 64, 128 or 256; KVQ_ATTN_NO_RESIDUAL: no residual).
 #define KVQ_ATTN_NO_RESIDUAL (-1)
 #define KVQ_ATTN_MAX_SPLIT 2048  // token blocks per KV head at most
 struct AttnPlanes {
@@ -135,16 +134,16 @@ struct AttnPlanes {
 #define KVQ_ATTN_PREFETCH 0
 #endif
 struct AttnArgs {
-    const uint16_t* q;  // [H * rep, 128] bf16
+    const uint16_t* q;  // [H * rep, D] bf16
     AttnPlanes k, v, rk, rv;
     int64_t T;
-    int32_t H, rep;
+    int32_t H, rep, D;
     int32_t n_split;    // token blocks per KV head (on entry to the launcher: the bound)
     int64_t tc;         // tokens per block (a multiple of 64), set by the launcher
     float qscale;       // softmax scale * log2(e)
-    float* part_o;      // [H, n_split, rep, 128]
+    float* part_o;      // [H, n_split, rep, D]
     float* part_ml;     // [H, n_split, rep, 2]
-    float* out;         // [H * rep, 128] fp32
+    float* out;         // [H * rep, D] fp32
 };
 
 // ---- launchers (return hipGetLastError() of the launch) ----

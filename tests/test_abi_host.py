@@ -223,12 +223,15 @@ def test_window_argument_errors():
 
 def test_attention_argument_errors():
     lib = kvq.library()
-    assert lib.kvq_attention_workspace_bytes(0, 8, 64) == 0
-    assert lib.kvq_attention_workspace_bytes(100, 8, 60) == 0
-    assert lib.kvq_attention_workspace_bytes(131072, 8, 64) > 0
+    assert lib.kvq_attention_workspace_bytes(0, 8, 64, 128) == 0
+    assert lib.kvq_attention_workspace_bytes(100, 8, 60, 128) == 0
+    assert lib.kvq_attention_workspace_bytes(100, 8, 64, 96) == 0      # head_dim 64, 128 or 256
+    assert lib.kvq_attention_workspace_bytes(131072, 8, 64, 128) > 0
+    assert (lib.kvq_attention_workspace_bytes(131072, 8, 64, 256) * 130
+            == lib.kvq_attention_workspace_bytes(131072, 8, 64, 128) * 258)
     # one partial (128 outputs, max, sum) per query head and token block; at most 2048 blocks per KV head
     for T, H, Hq in ((1, 1, 1), (64, 1, 16), (65, 2, 2), (1 << 20, 1, 1), (1 << 30, 1, 4), (1 << 22, 4096, 4096)):
-        n_split = lib.kvq_attention_workspace_bytes(T, H, Hq) // (Hq * 130 * 4)
+        n_split = lib.kvq_attention_workspace_bytes(T, H, Hq, 128) // (Hq * 130 * 4)
         assert 1 <= n_split <= max(1, 2048 // H) and n_split * 64 * (-(-T // (64 * n_split))) >= T
     k = _packed(format=0, kind=0, group_size=64, dtype=0, rows=256, H=2, D=128, full_T=256)
     v = _packed(format=0, kind=1, group_size=64, dtype=0, rows=256, H=2, D=128, full_T=256)
@@ -256,7 +259,7 @@ def test_attention_argument_errors():
     assert call(k, v4) == 5                  # INT4 V groups: 8 to 128 channels
     k96 = _packed(format=0, kind=0, group_size=64, dtype=0, rows=256, H=2, D=96, full_T=256)
     k96.codes, k96.meta0, k96.meta1 = k.codes, k.meta0, k.meta1
-    assert call(k96, v) == 2                 # head_dim 128 only
+    assert call(k96, v) == 2                 # head_dim 64, 128 or 256
     vt = _packed(format=0, kind=1, group_size=64, dtype=0, rows=255, H=2, D=128, full_T=255)
     vt.codes, vt.meta0, vt.meta1 = v.codes, v.meta0, v.meta1
     assert call(k, vt) == 7                  # token counts differ

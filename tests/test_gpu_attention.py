@@ -2,7 +2,7 @@
 float64 oracle (oracle/attention.py) over the codec's own decode of the same packed planes.
 
 Tolerance, from the arithmetic: K and V are reconstructed exactly (bf16 for bf16); the scores'
-products are exact in FP32 and their 128-term FP32 sums err by well under 2^-16 relative; the
+products are exact in FP32 and their D-term FP32 sums (D = 64 .. 256) err by well under 2^-16 relative; the
 probabilities are rounded to bf16 (relative error <= 2^-9) before the PV product, which bounds
 the output error by 2^-9 * sum_t p_t |v_t| <= 2^-9 * max |V|, plus FP32 accumulation. The tests
 use 2^-8 * max |V| per element, and a mean error well below that. Two structural cases are tight:
@@ -141,3 +141,65 @@ def test_bulk_shape(fmt, gk, gv):
     kr, vr = reconstruct(ok), reconstruct(ov)
     want = decode_attention(q, kr, vr, 1.0 / np.sqrt(D))
     check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"bulk {fmt}")
+
+
+def forms_for(d):
+    """Formats at head dim d: an INT4 VALUE group spans d/16 to d channels."""
+    if d == 64:
+        return [("int4", 64, 64), ("int4", 16, 8), ("int4", 128, 32), ("nvfp4", 16, 16), ("nvfp4_row", 16, 16),
+                ("fp8_row", 0, 0)]
+    return [("int4", 64, 64), ("int4", 16, 16), ("int4", 128, 256), ("nvfp4", 16, 16), ("nvfp4_row", 16, 16),
+            ("fp8_row", 0, 0)]
+
+
+HEAD_DIM_CASES = [(d, *f) for d in (64, 256) for f in forms_for(d)]
+
+
+@pytest.mark.parametrize("d,fmt,gk,gv", HEAD_DIM_CASES)
+@pytest.mark.parametrize("T,H,Hq", [(1, 1, 1), (17, 1, 16), (333, 2, 8), (4099, 4, 8), (600, 1, 40)])
+def test_head_dims_vs_oracle(d, fmt, gk, gv, T, H, Hq):
+    """Head dims 64 and 256: the same kernels at their own per-lane geometry (the K lane group
+    covers d/4 channels, each V lane d/16)."""
+    rng = np.random.default_rng(T * 3 + Hq + d)
+    k, v = normal_kv(rng, T, H, d), normal_kv(rng, T, H, d)
+    q = bf16_bits(rng.standard_normal((Hq, d)))
+    gk_, gv_, ok, ov = packed_pair(k, v, fmt, gk, gv)
+    out = kvq.decode_attention(to_dev(q), gk_, gv_).cpu().numpy()
+    assert out.shape == (Hq, d)
+    kr, vr = reconstruct(ok), reconstruct(ov)
+    want = decode_attention(q, kr, vr, 1.0 / np.sqrt(d))
+    check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"D={d} {fmt} T={T} Hq={Hq}")
+
+
+@pytest.mark.parametrize("d,fmt,gk,gv", HEAD_DIM_CASES)
+def test_head_dims_zero_query_is_mean_of_v(d, fmt, gk, gv):
+    rng = np.random.default_rng(d)
+    T, H, Hq = 1000, 2, 8
+    k, v = normal_kv(rng, T, H, d), normal_kv(rng, T, H, d)
+    gk_, gv_, ok, ov = packed_pair(k, v, fmt, gk, gv)
+    out = kvq.decode_attention(torch.zeros((Hq, d), dtype=torch.bfloat16, device=dev()), gk_, gv_).cpu().numpy()
+    vr = oracle.bf16_to_f32(reconstruct(ov)).astype(np.float64)
+    want = np.repeat(vr.mean(axis=0), Hq // H, axis=0)
+    np.testing.assert_allclose(out, want, rtol=0, atol=2e-6 * np.abs(vr).max())
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bfmt,rfmt", [("int4", "int4"), ("nvfp4", "nvfp4_row"), ("fp8_row", "int4"),
+                                       ("nvfp4_row", "fp8_row")])
+def test_head_dims_fused_residual(d, bfmt, rfmt):
+    rng = np.random.default_rng(d + 1)
+    T, H, Hq = 700, 2, 16
+    g = {"int4": (64, 64), "nvfp4": (16, 16), "nvfp4_row": (16, 16), "fp8_row": (0, 0)}
+    k0, v0 = normal_kv(rng, T, H, d), normal_kv(rng, T, H, d)
+    k1 = bf16_bits(oracle.bf16_to_f32(k0).astype(np.float64) + 0.1 * rng.standard_normal(k0.shape))
+    v1 = bf16_bits(oracle.bf16_to_f32(v0).astype(np.float64) + 0.1 * rng.standard_normal(v0.shape))
+    gk0, gv0, ok0, ov0 = packed_pair(k0, v0, bfmt, *g[bfmt])
+    grk = kvq.encode_residual(to_dev(k1), kvq.unpack(gk0), "key", rfmt, g[rfmt][0])
+    grv = kvq.encode_residual(to_dev(v1), kvq.unpack(gv0), "value", rfmt, g[rfmt][1])
+    ork = oracle.encode_residual(k1, oracle.unpack(ok0), "key", rfmt, g[rfmt][0])
+    orv = oracle.encode_residual(v1, oracle.unpack(ov0), "value", rfmt, g[rfmt][1])
+    q = bf16_bits(rng.standard_normal((Hq, d)))
+    out = kvq.decode_attention(to_dev(q), gk0, gv0, grk, grv).cpu().numpy()
+    kr, vr = reconstruct(ok0, ork), reconstruct(ov0, orv)
+    want = decode_attention(q, kr, vr, 1.0 / np.sqrt(d))
+    check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"D={d} {bfmt}+{rfmt}")
