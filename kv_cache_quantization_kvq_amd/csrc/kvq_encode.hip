@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
             if (i < nr && leader) reinterpret_cast<uint8_t*>(a.meta0)[midx] = (uint8_t)fb.code;
         }
         if (i < nr) {
-            if (valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)wr * (uint32_t)a.C8 + c8] = word;
+            if (valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
             if constexpr (GATHER) {
                 if (c8raw == 0) a.pos_out[r] = a.pos[r];
             }
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const uint32_t word = int4_word(v[i], gp, 1, slow);
-            if (i < nr && valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8] = word;
+            if (i < nr && valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)(r0 + i) * (uint32_t)a.C8 + c8, word);
         }
         if (wsub == 0 && valid) {
             u32x4 mins, scales;
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const uint32_t word = fp4_word(v[i], fb, 1);
-            if (i < nr && valid) reinterpret_cast<uint32_t*>(a.codes)[(size_t)(r0 + i) * (uint32_t)a.C8 + c8] = word;
+            if (i < nr && valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)(r0 + i) * (uint32_t)a.C8 + c8, word);
         }
         if (wsub == 0 && valid) {
             uint2 sc;

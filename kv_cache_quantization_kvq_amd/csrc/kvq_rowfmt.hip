@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
             const Fp8Row rs = fp8_row(bf16_to_f32(amax));
             const uint2 o = fp8_chunk(v[i], rs);
             if (i < nr) {
-                if (valid) *reinterpret_cast<uint2*>(a.codes + hr * (uint32_t)a.D + d) = o;
+                if (valid) st_code<!DIFF>(reinterpret_cast<u32x2*>(a.codes + hr * (uint32_t)a.D + d), (u32x2){o.x, o.y});
                 if (row_leader) reinterpret_cast<float*>(a.meta0)[hr] = rs.s;
             }
         } else {
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
             const Fp4Block fb = fp4_block_direct(bam, g, rcp_pair(g));
             const uint32_t word = fp4_word(v[i], &fb, 0);
             if (i < nr && valid) {
-                reinterpret_cast<uint32_t*>(a.codes)[(size_t)wr * (uint32_t)a.C8 + c8] = word;
+                st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
                 const uint32_t nb = ((uint32_t)a.D + 15u) / 16u;
                 if ((dc & 1u) == 0u) reinterpret_cast<uint8_t*>(a.meta0)[hr * nb + (dc >> 1)] = (uint8_t)fb.code;
                 if (row_leader) reinterpret_cast<float*>(a.meta1)[hr] = g;
