@@ -1,0 +1,168 @@
+// kvq_launch.hpp -- argument blocks and launchers shared by the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.hpp"
+
+namespace kvq {
+
+enum : int { FMT_INT4 = 0, FMT_NVFP4 = 1, FMT_NVFP4_ROW = 2, FMT_FP8_ROW = 3 };
+
+// Row offset of row t in a (possibly paged) view: rows come in pages of 2^pshift rows,
+// consecutive rows of a page `st` apart and pages `pst` apart. An unpaged view uses pshift 62
+// (every row in page 0), so the offset is t * st.
+__host__ __device__ __forceinline__ int64_t row_offset(int64_t t, int32_t pshift, int64_t pst, int64_t st) {
+    return (t >> pshift) * pst + (t & (((int64_t)1 << pshift) - 1)) * st;
+}
+constexpr int32_t kNoPaging = 62;
+
+// The NVFP4 amax pass writes one partial maximum per block into the workspace.
+#define KVQ_AMAX_MAX_BLOCKS 4096u
+
+// Rows per wave task of the vector VALUE encoder and of the vector decoder (a KEY decode needs
+// G % KVQ_DECODE_ROWS == 0 so that a task's rows share one token group). Shared by the host
+// code that sizes the grids and the kernels. Four decode rows per wave measured 6-7% faster
+// than eight on residual decodes of the bulk shape (more, shorter waves), and the same on
+// plain unpacks; two rows slowed the unpacks.
+#ifndef KVQ_ENCODE_ROWS_V
+#define KVQ_ENCODE_ROWS_V 8
+#endif
+#ifndef KVQ_DECODE_ROWS
+#define KVQ_DECODE_ROWS 4
+#endif
+// Rows per wave of the vector KEY encoder (a power of two): min(G, KVQ_KEY_ROWS), but at least
+// G / 16 so that the G / rows waves sharing a token group fit one block of at most 1024 threads.
+#ifndef KVQ_KEY_ROWS
+#define KVQ_KEY_ROWS 8
+#endif
+constexpr int key_rows_per_wave(int G) {
+    const int r = G < KVQ_KEY_ROWS ? G : KVQ_KEY_ROWS;
+    return r < G / 16 ? G / 16 : r;
+}
+constexpr int key_waves_per_group(int G) { return G / key_rows_per_wave(G); }
+constexpr int key_waves_per_block(int G) { return key_waves_per_group(G) > 4 ? key_waves_per_group(G) : 4; }
+enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
+
+// Rows being encoded: row r is source row t = pos ? pos[r] : r; the element value is
+// cur[t, h, d], or bf16(cur[t, h, d] - prev[t, h, d]) for a residual.
+struct EncArgs {
+    const uint16_t* cur;
+    int64_t cst, csh;
+    int32_t cpshift;       // paging of `cur` (kNoPaging when unpaged)
+    int64_t cpst;
+    const uint16_t* prev;  // residual only
+    int64_t pst, psh;
+    const int32_t* pos;    // sparse residual only
+    int32_t* pos_out;      // owned copy of pos
+    const int32_t* dst;    // slot writes: encoded row r lands in packed row dst[r] (NULL: row r)
+    int64_t rows;
+    int32_t H, D, G;
+    // vector-path geometry: C8 = H*D/8 chunks of 8 channels per row; a VALUE group spans
+    // lpg = G/8 = 1 << lpg_shift lanes, ngr = C8 / lpg groups per row
+    int32_t C8, D8, n_slabs, lpg, lpg_shift, ngr;
+    int32_t ri_shift, c8_shift;  // lane groups of short rows (see task_lane); 0 when unused
+    uint32_t n_tasks;
+    FastDiv div_D8, div_slabs, div_C8;
+    uint8_t* codes;
+    void* meta0;
+    void* meta1;
+    float* gscale;
+    uint32_t* ws;  // NVFP4: per-block partial maxima of the amax pass
+};
+
+// Rows being decoded: output row r reads packed row src ? src[r] : r and goes to output row
+// t = pos ? pos[r] : r; with `prev` the output is bf16(prev[t] + bf16(decoded)).
+struct DecArgs {
+    const uint8_t* codes;
+    const void* meta0;
+    const void* meta1;
+    const float* gscale;
+    const int32_t* pos;
+    const int32_t* src;    // slot reads (NULL: identity)
+    const uint16_t* prev;
+    int64_t pst, psh;
+    uint16_t* out;
+    int64_t ost, osh;
+    int32_t opshift;       // paging of `out` (kNoPaging when unpaged)
+    int64_t opst;
+    int64_t rows;
+    int32_t H, D, G;
+    int32_t C8, D8, n_slabs, lpg, lpg_shift, ngr;
+    int32_t ri_shift, c8_shift;  // lane groups of short rows (see task_lane); 0 when unused
+    uint32_t n_tasks;
+    FastDiv div_D8, div_slabs;
+};
+
+// Lanes of a vector-path task. Rows of 64 or more 8-channel chunks (or a count that does not
+// divide 64): the wave's 64 lanes take 64 consecutive chunks (a slab) of one row tile, and a
+// task is (row tile, slab). Shorter rows (LG): C8 = 1 << c8_shift chunks per row, and the lanes
+// form 1 << ri_shift groups of C8, group k taking row tile (task << ri_shift) + k, so every lane
+// has work (a head-sharded [T, 1, 128] tensor has 16 chunks per row).
+template <bool LG, class Args>
+__device__ __forceinline__ void task_lane(const Args& a, uint32_t task, int lane, uint32_t& rtile, uint32_t& c8raw) {
+    if constexpr (LG) {
+        rtile = (task << a.ri_shift) + ((uint32_t)lane >> a.c8_shift);
+        c8raw = (uint32_t)lane & ((1u << a.c8_shift) - 1u);
+    } else {
+        rtile = fdiv(task, a.div_slabs);
+        c8raw = (task - rtile * (uint32_t)a.n_slabs) * 64u + (uint32_t)lane;
+    }
+}
+
+struct CopyArgs {
+    const uint16_t* src;
+    int64_t sst, ssh;
+    uint16_t* dst;
+    int64_t dst_t, dsh;
+    int64_t T;
+    int32_t H, D, C8;
+    FastDiv div_C8, div_D8;
+};
+
+// Decode attention over packed K/V (head_dim 64, 128 or 256; KVQ_ATTN_NO_RESIDUAL: no residual).
+#define KVQ_ATTN_NO_RESIDUAL (-1)
+#define KVQ_ATTN_MAX_SPLIT 2048  // token blocks per KV head at most
+struct AttnPlanes {
+    const uint8_t* codes;
+    const void* meta0;
+    const void* meta1;
+    const float* gscale;
+    int32_t gshift;  // log2 of the group size (INT4; NVFP4 blocks are 16)
+};
+// Load the next 16-token sub-tile's raw data before decoding the current one (1), or not (0).
+#ifndef KVQ_ATTN_PREFETCH
+#define KVQ_ATTN_PREFETCH 0
+#endif
+struct AttnArgs {
+    const uint16_t* q;  // [H * rep, D] bf16
+    AttnPlanes k, v, rk, rv;
+    int64_t T;
+    int32_t H, rep, D;
+    int32_t n_split;    // token blocks per KV head (on entry to the launcher: the bound)
+    int64_t tc;         // tokens per block (a multiple of 64), set by the launcher
+    float qscale;       // softmax scale * log2(e)
+    float* part_o;      // [H, n_split, rep, D]
+    float* part_ml;     // [H, n_split, rep, 2]
+    float* out;         // [H * rep, D] fp32
+};
+
+// ---- launchers (return hipGetLastError() of the launch) ----
+// vec: the 8-channel vector path is legal for these arguments (alignment, strides, G).
+
+hipError_t launch_amax(const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
+hipError_t launch_set_global(float* gscale, uint32_t value_bits, hipStream_t s);
+hipError_t launch_encode(int fmt, int kind, const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
+hipError_t launch_decode(int fmt, int kind, const DecArgs& a, bool add, bool scatter, bool vec, hipStream_t s);
+hipError_t launch_copy_rows(const CopyArgs& a, bool vec, hipStream_t s);
+// Row formats (NVFP4-row, FP8-row): encode / decode of rows that each carry their own scale.
+hipError_t launch_row_encode(int fmt, const EncArgs& a, bool diff, bool gather, bool vec, hipStream_t s);
+hipError_t launch_row_decode(int fmt, const DecArgs& a, bool add, bool scatter, bool vec, hipStream_t s);
+// Decode attention: base format of K and V, residual format (or KVQ_ATTN_NO_RESIDUAL).
+hipError_t launch_attention(int fmt, int rfmt, const AttnArgs& a, hipStream_t s);
+hipError_t launch_copy_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
+hipError_t launch_validate_positions(const int32_t* pos, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,
+                                     hipStream_t s);
+
+}  // namespace kvq
