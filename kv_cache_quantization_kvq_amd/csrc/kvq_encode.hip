@@ -108,6 +108,73 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
 
 // ---- VALUE, vector path ------------------------------------------------------------------------
 
+// INT4 VALUE groups of 64 channels (8 lanes) over 8 rows per task: instead of all-reducing every
+// row's minimum and maximum over the group's 8 lanes (and then computing the same group
+// constants on all 8), the statistics are reduce-scattered so that lane j of the group ends with
+// row j's, computes that row's constants alone, and the constants reach the other lanes by
+// ds_bpermute. Every lane then holds exactly the constants the all-reduce would give it, so the
+// codes and metadata are the same bits. Three butterfly steps pair lanes j <-> 7 - j (DPP
+// row_half_mirror), j <-> j ^ 2 and j <-> j ^ 1; at each step a lane keeps the half of its rows
+// whose index bit matches its own lane bit and sends the other half.
+template <bool DIFF, bool GATHER>
+__device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v)[8], int lane, int64_t r0, int nr,
+                                               bool valid, uint32_t c8, uint32_t c8raw) {
+    uint32_t mn8[8], mx8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        short2_t k = keys2(v[i].x), mn = k, mx = k;
+        k = keys2(v[i].y); mn = min2(mn, k); mx = max2(mx, k);
+        k = keys2(v[i].z); mn = min2(mn, k); mx = max2(mx, k);
+        k = keys2(v[i].w); mn = min2(mn, k); mx = max2(mx, k);
+        mn8[i] = (uint32_t)min((int)mn.x, (int)mn.y);
+        mx8[i] = (uint32_t)max((int)mx.x, (int)mx.y);
+    }
+    const uint32_t j = (uint32_t)lane & 7u;
+    const bool b2 = (j & 4u) != 0u, b1 = (j & 2u) != 0u, b0 = (j & 1u) != 0u;
+    uint32_t mn4[4], mx4[4];  // rows 4 b2 + k
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        mn4[k] = imin_op(b2 ? mn8[k + 4] : mn8[k], dpp<0x141>(b2 ? mn8[k] : mn8[k + 4]));
+        mx4[k] = imax_op(b2 ? mx8[k + 4] : mx8[k], dpp<0x141>(b2 ? mx8[k] : mx8[k + 4]));
+    }
+    uint32_t mn2[2], mx2[2];  // rows 4 b2 + 2 b1 + k
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        mn2[k] = imin_op(b1 ? mn4[k + 2] : mn4[k], dpp<0x4E>(b1 ? mn4[k] : mn4[k + 2]));
+        mx2[k] = imax_op(b1 ? mx4[k + 2] : mx4[k], dpp<0x4E>(b1 ? mx4[k] : mx4[k + 2]));
+    }
+    const uint32_t gmn = imin_op(b0 ? mn2[1] : mn2[0], dpp<0xB1>(b0 ? mn2[0] : mn2[1]));  // row j
+    const uint32_t gmx = imax_op(b0 ? mx2[1] : mx2[0], dpp<0xB1>(b0 ? mx2[0] : mx2[1]));
+    const Int4Group gj = int4_group(key_to_f32((int)gmn), key_to_f32((int)gmx));
+    if ((int)j < nr && valid) {  // row j's metadata (the group's 8 lanes are all valid or all idle)
+        const int64_t r = r0 + j;
+        const int64_t wr = a.dst ? (int64_t)a.dst[r] : r;
+        const size_t midx = (size_t)wr * (uint32_t)a.ngr + (c8 >> 3);
+        reinterpret_cast<uint16_t*>(a.meta0)[midx] = (uint16_t)f32_to_f16(gj.mn);
+        reinterpret_cast<uint16_t*>(a.meta1)[midx] = (uint16_t)f32_to_f16(gj.scale);
+    }
+    const uint32_t slow8 = (uint32_t)(__ballot(gj.slow) >> (lane & 56)) & 0xFFu;
+    const int gbase = lane & ~7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        Int4Group g;
+        g.mn = __shfl(gj.mn, gbase + i);
+        g.scale = __shfl(gj.scale, gbase + i);
+        g.y = __shfl(gj.y, gbase + i);
+        g.ylo = __shfl(gj.ylo, gbase + i);
+        g.slow = ((slow8 >> i) & 1u) != 0u;
+        const uint32_t word = int4_word(v[i], &g, 0, g.slow);
+        if (i < nr) {
+            const int64_t r = r0 + i;
+            const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
+            if (valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
+            if constexpr (GATHER) {
+                if (c8raw == 0) a.pos_out[r] = a.pos[r];
+            }
+        }
+    }
+}
+
 // A wave task is RW consecutive rows of one 64-chunk column slab.
 template <int FMT, bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
@@ -133,6 +200,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 
     u32x4 v[RW];
     load_rows8<RW, DIFF, GATHER>(a, r0, h, d, v);
+    if constexpr (FMT == FMT_INT4 && RW == 8) {
+        if (lpg == 8) {  // G = 64 (wave-uniform)
+            int4_value_g64<DIFF, GATHER>(a, v, lane, r0, nr, valid, c8, c8raw);
+            return;
+        }
+    }
     const bool leader = valid && ((lane & (lpg - 1)) == 0);
 
 #pragma unroll
