@@ -26,6 +26,7 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float f4_t __attribute__((ext_vector_type(4)));
 constexpr int kEncodeRowsV = KVQ_ENCODE_ROWS_V;           // rows per VALUE-encode wave task
 constexpr uint32_t kAmaxMaxBlocks = KVQ_AMAX_MAX_BLOCKS;  // partial maxima held in the workspace
 
@@ -260,6 +261,9 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
     constexpr int NW = (FMT == FMT_INT4) ? 8 : 4;  // exchanged words per lane
     static_assert(WPB <= 16 && WPB % WPG == 0, "KEY encoder block shape");
     __shared__ uint32_t lds[WPG > 1 ? WPB * NW * 64 : 1];
+    // INT4 with a group split over waves: each item's 8 channels' constants per lane
+    constexpr bool SPLIT = FMT == FMT_INT4 && WPG > 1;
+    __shared__ f4_t cst[SPLIT ? IPB * 8 * 64 : 1];
     __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
     float g = 0.0f;
     if constexpr (FMT == FMT_NVFP4) {
@@ -323,7 +327,30 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
         for (int j = 0; j < 4; ++j) st[j] = us2_as_u(am[j]);
     }
 
-    if constexpr (WPG > 1) {
+    if constexpr (SPLIT) {
+        // The group's waves share the constants' work: wave wsub reduces channels wsub,
+        // wsub + WPG, ... of every lane over the group's waves, computes their constants and
+        // leaves them in LDS (the slow flag as a negative reciprocal, which only the fast path
+        // reads); after a second barrier every wave reads all 8.
+#pragma unroll
+        for (int k = 0; k < NW; ++k) lds[(wave * NW + k) * 64 + lane] = st[k];
+        __syncthreads();
+        const int base = (wave / WPG) * WPG;
+        const int il = wave / WPG;
+        for (int c = wsub; c < 8; c += WPG) {  // wave-uniform
+            const int j = c >> 1;
+            uint32_t m = lds[(base * NW + j) * 64 + lane], x = lds[(base * NW + 4 + j) * 64 + lane];
+#pragma unroll
+            for (int o = 1; o < WPG; ++o) {
+                m = s2_as_u(min2(as_s2(m), as_s2(lds[((base + o) * NW + j) * 64 + lane])));
+                x = s2_as_u(max2(as_s2(x), as_s2(lds[((base + o) * NW + 4 + j) * 64 + lane])));
+            }
+            const short2_t ms = as_s2(m), xs = as_s2(x);
+            const Int4Group gc = int4_group(key_to_f32((c & 1) ? ms.y : ms.x), key_to_f32((c & 1) ? xs.y : xs.x));
+            cst[(il * 8 + c) * 64 + lane] = (f4_t){gc.mn, gc.scale, gc.slow ? -1.0f : gc.y, gc.ylo};
+        }
+        __syncthreads();
+    } else if constexpr (WPG > 1) {
 #pragma unroll
         for (int k = 0; k < NW; ++k) lds[(wave * NW + k) * 64 + lane] = st[k];
         __syncthreads();
@@ -349,11 +376,24 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
     const size_t mbase = ((size_t)b * (uint32_t)a.C8 + c8) * 8u;
     if constexpr (FMT == FMT_INT4) {
         Int4Group gp[8];
+        if constexpr (SPLIT) {
+            const int il = wave / WPG;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const short2_t mn = as_s2(st[j]), mx = as_s2(st[4 + j]);
-            gp[2 * j] = int4_group(key_to_f32(mn.x), key_to_f32(mx.x));
-            gp[2 * j + 1] = int4_group(key_to_f32(mn.y), key_to_f32(mx.y));
+            for (int c = 0; c < 8; ++c) {
+                const f4_t t = cst[(il * 8 + c) * 64 + lane];
+                gp[c].mn = t[0];
+                gp[c].scale = t[1];
+                gp[c].slow = t[2] < 0.0f;
+                gp[c].y = t[2];
+                gp[c].ylo = t[3];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const short2_t mn = as_s2(st[j]), mx = as_s2(st[4 + j]);
+                gp[2 * j] = int4_group(key_to_f32(mn.x), key_to_f32(mx.x));
+                gp[2 * j + 1] = int4_group(key_to_f32(mn.y), key_to_f32(mx.y));
+            }
         }
         bool slow = false;
 #pragma unroll
