@@ -127,7 +127,7 @@ def test_fused_residual_reconstruction(bfmt, rfmt):
     check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"{bfmt}+{rfmt}")
 
 
-@pytest.mark.parametrize("fmt,gk,gv", [("int4", 64, 64), ("nvfp4", 16, 16), ("fp8_row", 0, 0)])
+@pytest.mark.parametrize("fmt,gk,gv", [("int4", 64, 64), ("nvfp4", 16, 16), ("nvfp4_row", 16, 16), ("fp8_row", 0, 0)])
 def test_bulk_shape(fmt, gk, gv):
     """The bench's shape: T = 131072 tokens, 8 KV heads, 64 query heads (heavy-tailed data)."""
     T, H, Hq = 131072, 8, 64
@@ -203,3 +203,18 @@ def test_head_dims_fused_residual(d, bfmt, rfmt):
     kr, vr = reconstruct(ok0, ork), reconstruct(ov0, orv)
     want = decode_attention(q, kr, vr, 1.0 / np.sqrt(d))
     check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"D={d} {bfmt}+{rfmt}")
+
+
+@pytest.mark.parametrize("fmt,gk,gv", [("int4", 64, 64), ("nvfp4", 16, 16)])
+def test_head_dim_256_large(fmt, gk, gv):
+    """Head dim 256 at a long context: T = 32768 tokens, 4 KV heads, 32 query heads (many token
+    blocks per KV head, 8 query heads per KV head)."""
+    T, H, Hq, d = 32768, 4, 32, 256
+    rng = np.random.default_rng(256)
+    k, v = normal_kv(rng, T, H, d), normal_kv(rng, T, H, d)
+    q = bf16_bits(rng.standard_normal((Hq, d)))
+    gk_, gv_, ok, ov = packed_pair(k, v, fmt, gk, gv)
+    out = kvq.decode_attention(to_dev(q), gk_, gv_).cpu().numpy()
+    kr, vr = reconstruct(ok), reconstruct(ov)
+    want = decode_attention(q, kr, vr, 1.0 / np.sqrt(d))
+    check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"D=256 large {fmt}")
