@@ -209,13 +209,14 @@ def run_extras(kvq, torch, X, T: int, dev, reps: int = 20) -> dict:
     return out
 
 
-TRAFFIC_SOURCES = ("csrc/kvq_device.hpp", "csrc/kvq_encode.hip", "csrc/kvq_launch.hpp", "_build.py")
+TRAFFIC_SOURCES = ("csrc/kvq_device.hpp", "csrc/kvq_encode.hip", "csrc/kvq_decode.hip", "csrc/kvq_launch.hpp",
+                   "_build.py")
 
 
-def measured_traffic(kernel_name: str):
-    """HBM bytes per launch of `kernel_name` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    runs (profiles/traffic.json, copy-kernel scaled), or None if those counters were taken on
-    other kernel sources or for another kernel."""
+def measured_traffic(op_name: str):
+    """HBM bytes per launch of the single-launch op `op_name` from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs (profiles/traffic.json, copy-kernel scaled), or None if those
+    counters were taken on other kernel sources or do not cover the op."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -224,12 +225,13 @@ def measured_traffic(kernel_name: str):
     with open(path) as f:
         rec = json.load(f)
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:  # the dominant kernel's translation unit and its build flags
+    for rel in TRAFFIC_SOURCES:  # the bulk kernels' sources and their build flags
         with open(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", rel), "rb") as f:
             h.update(f.read())
-    if rec.get("source_sha256") != h.hexdigest() or rec.get("kernel") != kernel_name:
+    op = rec.get("ops", {}).get(op_name)
+    if rec.get("source_sha256") != h.hexdigest() or op is None:
         return None
-    return float(rec["traffic_bytes"])
+    return float(op["traffic_bytes"])
 
 
 def cpu_baseline(T_sample: int):
