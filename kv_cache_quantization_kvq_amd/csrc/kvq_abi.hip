@@ -212,6 +212,9 @@ kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* po
     bool vec = (D % 8 == 0) && view_vec_ok(cur) && aligned(planes->codes, 4) &&
                (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
     if (prev) vec = vec && view_vec_ok(prev->data, prev->stride_t, prev->stride_h);
+    // the vector encoders address a row's elements by a 32-bit byte offset from the row start
+    const auto span_ok = [&](int64_t sh) { return sh >= 0 && (H - 1) * sh + D <= ((int64_t)1 << 30); };
+    vec = vec && span_ok(cur.sh) && (!prev || span_ok(prev->stride_h));
     if (row_format(format)) {
         vec = vec && row_vec_dims(D) &&
               (format == KVQ_FP8_ROW ? aligned(planes->codes, 8) && aligned(planes->meta0, 4) : aligned(planes->meta1, 4));

@@ -56,12 +56,53 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Wave-uniform global addresses held in SGPRs (opaque to the optimizer), to which a lane adds a
+// 32-bit byte offset inside the memory instruction (the scalar-base form of global loads and
+// stores): a per-row address then costs scalar instructions only, instead of a 64-bit vector add
+// per lane. `p + off` must be the same on every lane of the wave.
+typedef const __attribute__((address_space(1))) uint8_t* wave_cptr;
+typedef __attribute__((address_space(1))) uint8_t* wave_ptr;
+
+__device__ __forceinline__ uint64_t wave_uniform_u64(uint64_t v) {
+    // readfirstlane returns a signed int: widen through uint32_t, never by sign extension
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+__device__ __forceinline__ wave_cptr wave_base(const void* p, int64_t off_bytes) {
+    wave_cptr b = (wave_cptr)wave_uniform_u64(reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(p) + off_bytes));
+    asm("" : "+s"(b));
+    return b;
+}
+
+__device__ __forceinline__ wave_ptr wave_base_w(void* p, int64_t off_bytes) {
+    wave_ptr b = (wave_ptr)wave_uniform_u64(reinterpret_cast<uint64_t>(static_cast<uint8_t*>(p) + off_bytes));
+    asm("" : "+s"(b));
+    return b;
+}
+
+// Streaming 16-byte load at a wave-uniform base plus a lane's byte offset.
+__device__ __forceinline__ u32x4 ld_stream_at(wave_cptr base, uint32_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(base + off));
+}
+
 // Store of packed codes: non-temporal when NT. The encoders pass NT for a plain pack, whose
 // codes are written once and not read back by the same pass; measured on the bulk shape this
 // frees the caches for the input stream (INT4 pack 71 -> 66 us). With a residual's second input
 // stream the hint slowed the encode, so residual encodes store normally.
 template <bool NT, class T>
 __device__ __forceinline__ void st_code(T* p, T w) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(w, p);
+    else
+        *p = w;
+}
+
+// The same at a wave-uniform base plus a lane's byte offset.
+template <bool NT, class T>
+__device__ __forceinline__ void st_code_at(wave_ptr base, uint32_t off, T w) {
+    auto* p = reinterpret_cast<__attribute__((address_space(1))) T*>(base + off);
     if constexpr (NT)
         __builtin_nontemporal_store(w, p);
     else

@@ -44,7 +44,9 @@ __device__ __forceinline__ uint32_t load_one(const EncArgs& a, int64_t t, int64_
 }
 
 // Loads the RW rows' 8-channel chunks of one lane (all issued before use), residual applied.
-template <int RW, bool DIFF, bool GATHER>
+// UNI: r0 is the same on every lane, so each row's address is a scalar base plus the lane's
+// 32-bit byte offset within the row (the host keeps a row's span below 2^31 bytes).
+template <int RW, bool DIFF, bool GATHER, bool UNI>
 __device__ __forceinline__ void load_rows8(const EncArgs& a, int64_t r0, uint32_t h, uint32_t d, u32x4 (&v)[RW]) {
     int64_t t[RW];
 #pragma unroll
@@ -52,12 +54,25 @@ __device__ __forceinline__ void load_rows8(const EncArgs& a, int64_t r0, uint32_
         const int64_t r = min<int64_t>(r0 + i, a.rows - 1);  // tail rows duplicate the last row
         t[i] = GATHER ? (int64_t)a.pos[r] : r;
     }
+    if constexpr (UNI) {
+        const uint32_t coff = (uint32_t)(((int64_t)h * a.csh + d) * 2);
 #pragma unroll
-    for (int i = 0; i < RW; ++i) v[i] = ld_stream(a.cur + row_offset(t[i], a.cpshift, a.cpst, a.cst) + (int64_t)h * a.csh + d);
+        for (int i = 0; i < RW; ++i)
+            v[i] = ld_stream_at(wave_base(a.cur, row_offset(t[i], a.cpshift, a.cpst, a.cst) * 2), coff);
+    } else {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) v[i] = ld_stream(a.cur + row_offset(t[i], a.cpshift, a.cpst, a.cst) + (int64_t)h * a.csh + d);
+    }
     if constexpr (DIFF) {
         u32x4 p[RW];
+        if constexpr (UNI) {
+            const uint32_t poff = (uint32_t)(((int64_t)h * a.psh + d) * 2);
 #pragma unroll
-        for (int i = 0; i < RW; ++i) p[i] = ld_stream(a.prev + t[i] * a.pst + (int64_t)h * a.psh + d);
+            for (int i = 0; i < RW; ++i) p[i] = ld_stream_at(wave_base(a.prev, t[i] * a.pst * 2), poff);
+        } else {
+#pragma unroll
+            for (int i = 0; i < RW; ++i) p[i] = ld_stream(a.prev + t[i] * a.pst + (int64_t)h * a.psh + d);
+        }
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             v[i].x = sub_bf16x2(v[i].x, p[i].x);
@@ -74,8 +89,10 @@ __device__ __forceinline__ uint32_t umax_op(uint32_t x, uint32_t y) { return max
 
 // 8 INT4 codes of one chunk (channel 2j in nibble 2j); group constants gp[k * stride].
 // `slow` (a lane's OR of its groups' slow flags) sends the whole chunk through the division.
-// Codes are integer-valued floats in [0, 15]; v_cvt_pk_u8_f32 places the even channels' codes
-// in the bytes of one word and the odd channels' in another, and one shift-or interleaves them.
+// The quotients lie in [0, 15.5); v_cvt_pk_u8_f32 rounds each to the nearest integer, ties to
+// even (the device probe checks it on every binary32 in that range), which is the code, and
+// places the even channels' codes in the bytes of one word and the odd channels' in another;
+// one shift-or interleaves them.
 __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* gp, int stride, bool slow) {
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
     float d[8], c[8];
@@ -88,11 +105,11 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const Int4Group& g = gp[k * stride];
-            c[k] = g.slow ? __builtin_rintf(d[k] / g.scale) : int4_quot(d[k], g);
+            c[k] = g.slow ? d[k] / g.scale : int4_quot_raw(d[k], g);
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) c[k] = int4_quot(d[k], gp[k * stride]);
+        for (int k = 0; k < 8; ++k) c[k] = int4_quot_raw(d[k], gp[k * stride]);
     }
     uint32_t even = 0, odd = 0;
     even = __builtin_amdgcn_cvt_pk_u8_f32(c[0], 0, even);
@@ -117,7 +134,7 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
 // codes and metadata are the same bits. Three butterfly steps pair lanes j <-> 7 - j (DPP
 // row_half_mirror), j <-> j ^ 2 and j <-> j ^ 1; at each step a lane keeps the half of its rows
 // whose index bit matches its own lane bit and sends the other half.
-template <bool DIFF, bool GATHER>
+template <bool DIFF, bool GATHER, bool LG>
 __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v)[8], int lane, int64_t r0, int nr,
                                                bool valid, uint32_t c8, uint32_t c8raw) {
     uint32_t mn8[8], mx8[8];
@@ -167,8 +184,12 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
         const uint32_t word = int4_word(v[i], &g, 0, g.slow);
         if (i < nr) {
             const int64_t r = r0 + i;
-            const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
-            if (valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
+            if (!LG && a.dst == nullptr) {
+                if (valid) st_code_at<!DIFF>(wave_base_w(a.codes, r * (int64_t)a.C8 * 4), c8 * 4u, word);
+            } else {
+                const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
+                if (valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
+            }
             if constexpr (GATHER) {
                 if (c8raw == 0) a.pos_out[r] = a.pos[r];
             }
@@ -200,10 +221,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
     const int lpg = a.lpg;
 
     u32x4 v[RW];
-    load_rows8<RW, DIFF, GATHER>(a, r0, h, d, v);
+    load_rows8<RW, DIFF, GATHER, !LG>(a, r0, h, d, v);
     if constexpr (FMT == FMT_INT4 && RW == 8) {
         if (lpg == 8) {  // G = 64 (wave-uniform)
-            int4_value_g64<DIFF, GATHER>(a, v, lane, r0, nr, valid, c8, c8raw);
+            int4_value_g64<DIFF, GATHER, LG>(a, v, lane, r0, nr, valid, c8, c8raw);
             return;
         }
     }
@@ -289,7 +310,7 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
     const int nr = item_ok ? (int)max<int64_t>(0, min<int64_t>(RPW, a.rows - r0)) : 0;
 
     u32x4 v[RPW];
-    load_rows8<RPW, DIFF, GATHER>(a, r0, h, d, v);
+    load_rows8<RPW, DIFF, GATHER, !LG>(a, r0, h, d, v);
 
     // per-channel statistics over this wave's rows: channel 2j in .x, 2j+1 in .y of word j
     uint32_t st[NW];
@@ -401,7 +422,12 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const uint32_t word = int4_word(v[i], gp, 1, slow);
-            if (i < nr && valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)(r0 + i) * (uint32_t)a.C8 + c8, word);
+            if (i < nr && valid) {
+                if constexpr (LG)
+                    st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)(r0 + i) * (uint32_t)a.C8 + c8, word);
+                else
+                    st_code_at<!DIFF>(wave_base_w(a.codes, (r0 + i) * (int64_t)a.C8 * 4), c8 * 4u, word);
+            }
         }
         if (wsub == 0 && valid) {
             u32x4 mins, scales;
@@ -424,7 +450,12 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const uint32_t word = fp4_word(v[i], fb, 1);
-            if (i < nr && valid) st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)(r0 + i) * (uint32_t)a.C8 + c8, word);
+            if (i < nr && valid) {
+                if constexpr (LG)
+                    st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)(r0 + i) * (uint32_t)a.C8 + c8, word);
+                else
+                    st_code_at<!DIFF>(wave_base_w(a.codes, (r0 + i) * (int64_t)a.C8 * 4), c8 * 4u, word);
+            }
         }
         if (wsub == 0 && valid) {
             uint2 sc;
@@ -593,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_vec(EncArgs a) {
         const uint32_t h = fdiv(c8, a.div_D8);
         const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
         u32x4 v[RW];
-        load_rows8<RW, DIFF, GATHER>(a, (int64_t)rtile * RW, h, d, v);
+        load_rows8<RW, DIFF, GATHER, !LG>(a, (int64_t)rtile * RW, h, d, v);
         ushort2_t mm = (ushort2_t){0, 0};
 #pragma unroll
         for (int i = 0; i < RW; ++i)

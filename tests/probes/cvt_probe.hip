@@ -39,6 +39,8 @@
 //   [15] kvq::fp4_global_rn(amax) == kvq::fp4_global(amax) (the IEEE 2688 / amax)
 //   [16] kvq::fp4_code_scales_rn(c, rcp_pair(g))[0] == fl(e4m3(c) / g), g the row multiplier
 //   [17] its reciprocal [1] == fl(1 / s_dec) (+inf where that overflows, 0 for code 0)
+//   [18] v_cvt_pk_u8_f32 of every binary32 in [+0, 15.5] (and -0) == its round-to-nearest-even
+//        integer in the selected byte, the other bytes kept
 // counting mismatches and recording the smallest mismatching input of each check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -49,7 +51,7 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kChecks = 18;
+constexpr int kChecks = 19;
 
 __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint32_t* first) {
     unsigned long long c[kChecks] = {};
@@ -142,6 +144,13 @@ __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint3
                 ++c[12];
                 f[12] = min(f[12], bits);
             }
+        }
+        if (bits <= 0x41780000u || bits == 0x80000000u) {  // every binary32 in [+0, 15.5], and -0
+            // v_cvt_pk_u8_f32 of an INT4 quotient rounds it to the nearest integer, ties to even
+            const uint32_t want = (uint32_t)__builtin_rintf(x);
+            const uint32_t b0 = __builtin_amdgcn_cvt_pk_u8_f32(x, 0, 0xAABBCCDDu);
+            const uint32_t b3 = __builtin_amdgcn_cvt_pk_u8_f32(x, 3, 0xAABBCCDDu);
+            if (b0 != (0xAABBCC00u | want) || b3 != (0x00BBCCDDu | (want << 24))) { ++c[18]; f[18] = min(f[18], bits); }
         }
         if (bits < 16u) {
             const float hv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(bits, 1.0f, 0)[0];

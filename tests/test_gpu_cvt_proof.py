@@ -15,7 +15,9 @@ rounding (every binary32 of magnitude up to 448) and decode (every finite code);
 branch-free FP8-row quotient against the IEEE division on signed quotients at and next to float
 midpoints from 2^-12 to 2^9 for every scale significand at eight exponents; and the NVFP4-row
 row multiplier, block decode scale and its reciprocal computed without the IEEE division sequence
-against the IEEE quotients for every finite positive bf16 row amax and every E4M3 scale code.
+against the IEEE quotients for every finite positive bf16 row amax and every E4M3 scale code;
+and v_cvt_pk_u8_f32 against round-to-nearest-even for every binary32 in [+0, 15.5] (the INT4
+quotients it turns into codes).
 The software formulations are written from the format definitions and are pinned
 against the oracle end to end by the parity tests.
 """
@@ -36,7 +38,8 @@ NAMES = ["bf16", "f16", "fp4 encode (all finite)", "fp4 encode (|x| <= 8)", "fp4
          "FP8-row quotient (Markstein) == IEEE x / scale", "INT4 decode product exact (one FMA)",
          "NVFP4-row g = 2688 / amax without division (every bf16 amax)",
          "NVFP4-row s_dec = e4m3 / g without division (every amax x code)",
-         "NVFP4-row 1 / s_dec without division (every amax x code)"]
+         "NVFP4-row 1 / s_dec without division (every amax x code)",
+         "v_cvt_pk_u8_f32 rounds [0, 15.5] to nearest even"]
 
 
 def test_conversion_instructions_match_software_rounding():
