@@ -395,26 +395,64 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
     if (!item_ok) return;
 
     const size_t mbase = ((size_t)b * (uint32_t)a.C8 + c8) * 8u;
-    if constexpr (FMT == FMT_INT4) {
-        Int4Group gp[8];
-        if constexpr (SPLIT) {
-            const int il = wave / WPG;
+    if constexpr (SPLIT) {
+        // Codes channel pair by channel pair: only two channels' constants are held at a time
+        // (instead of all eight), and each row's even and odd channels' codes gather in the bytes
+        // of two words, interleaved into nibbles at the end.
+        const int il = wave / WPG;
+        uint32_t ev[RPW], od[RPW];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const f4_t t = cst[(il * 8 + c) * 64 + lane];
-                gp[c].mn = t[0];
-                gp[c].scale = t[1];
-                gp[c].slow = t[2] < 0.0f;
-                gp[c].y = t[2];
-                gp[c].ylo = t[3];
+        for (int i = 0; i < RPW; ++i) ev[i] = od[i] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f4_t t0 = cst[(il * 8 + 2 * j) * 64 + lane], t1 = cst[(il * 8 + 2 * j + 1) * 64 + lane];
+            Int4Group g0, g1;
+            g0.mn = t0[0]; g0.scale = t0[1]; g0.y = t0[2]; g0.ylo = t0[3]; g0.slow = t0[2] < 0.0f;
+            g1.mn = t1[0]; g1.scale = t1[1]; g1.y = t1[2]; g1.ylo = t1[3]; g1.slow = t1[2] < 0.0f;
+            if (__builtin_expect(g0.slow || g1.slow, 0)) {
+#pragma unroll
+                for (int i = 0; i < RPW; ++i) {
+                    const float d0 = __fsub_rn(bf16lo(v[i][j]), g0.mn), d1 = __fsub_rn(bf16hi(v[i][j]), g1.mn);
+                    ev[i] = __builtin_amdgcn_cvt_pk_u8_f32(g0.slow ? d0 / g0.scale : int4_quot_raw(d0, g0), j, ev[i]);
+                    od[i] = __builtin_amdgcn_cvt_pk_u8_f32(g1.slow ? d1 / g1.scale : int4_quot_raw(d1, g1), j, od[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < RPW; ++i) {
+                    const float d0 = __fsub_rn(bf16lo(v[i][j]), g0.mn), d1 = __fsub_rn(bf16hi(v[i][j]), g1.mn);
+                    ev[i] = __builtin_amdgcn_cvt_pk_u8_f32(int4_quot_raw(d0, g0), j, ev[i]);
+                    od[i] = __builtin_amdgcn_cvt_pk_u8_f32(int4_quot_raw(d1, g1), j, od[i]);
+                }
             }
-        } else {
+        }
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const uint32_t word = ev[i] | (od[i] << 4);
+            if (i < nr && valid) {
+                if constexpr (LG)
+                    st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)(r0 + i) * (uint32_t)a.C8 + c8, word);
+                else
+                    st_code_at<!DIFF>(wave_base_w(a.codes, (r0 + i) * (int64_t)a.C8 * 4), c8 * 4u, word);
+            }
+        }
+        if (wsub == 0 && valid) {
+            u32x4 mins, scales;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const short2_t mn = as_s2(st[j]), mx = as_s2(st[4 + j]);
-                gp[2 * j] = int4_group(key_to_f32(mn.x), key_to_f32(mx.x));
-                gp[2 * j + 1] = int4_group(key_to_f32(mn.y), key_to_f32(mx.y));
+                const f4_t t0 = cst[(il * 8 + 2 * j) * 64 + lane], t1 = cst[(il * 8 + 2 * j + 1) * 64 + lane];
+                mins[j] = f32_to_f16(t0[0]) | (f32_to_f16(t1[0]) << 16);
+                scales[j] = f32_to_f16(t0[1]) | (f32_to_f16(t1[1]) << 16);
             }
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.meta0) + mbase) = mins;
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.meta1) + mbase) = scales;
+        }
+    } else if constexpr (FMT == FMT_INT4) {  // a group held by one wave
+        Int4Group gp[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const short2_t mn = as_s2(st[j]), mx = as_s2(st[4 + j]);
+            gp[2 * j] = int4_group(key_to_f32(mn.x), key_to_f32(mx.x));
+            gp[2 * j + 1] = int4_group(key_to_f32(mn.y), key_to_f32(mx.y));
         }
         bool slow = false;
 #pragma unroll
