@@ -239,6 +239,14 @@ __device__ __forceinline__ short2_t keys2(uint32_t w) {
     short2_t sgn = v >> (short2_t){15, 15};
     return v ^ (sgn & (short2_t){0x7FFF, 0x7FFF});
 }
+// The same order as unsigned 16-bit keys (the signed key with its top bit flipped), so that the
+// two halves of a word combine with one zero-extending half-word min or max.
+__device__ __forceinline__ uint32_t ukeys2(uint32_t w) {
+    const uint32_t sgn = s2_as_u(as_s2(w) >> (short2_t){15, 15});  // 0xFFFF in each negative half
+    return w ^ (sgn | 0x80008000u);
+}
+__device__ __forceinline__ float ukey_to_f32(uint32_t k) { return key_to_f32((int)(int16_t)(uint16_t)(k ^ 0x8000u)); }
+__device__ __forceinline__ ushort2_t umin2(ushort2_t a, ushort2_t b) { return __builtin_elementwise_min(a, b); }
 __device__ __forceinline__ short2_t min2(short2_t a, short2_t b) { return __builtin_elementwise_min(a, b); }
 __device__ __forceinline__ short2_t max2(short2_t a, short2_t b) { return __builtin_elementwise_max(a, b); }
 __device__ __forceinline__ ushort2_t umax2(ushort2_t a, ushort2_t b) { return __builtin_elementwise_max(a, b); }
@@ -247,12 +255,15 @@ __device__ __forceinline__ ushort2_t mag2(uint32_t w) { return as_us2(w & 0x7FFF
 
 // ---- cross-lane (DPP) -----------------------------------------------------------------------
 
-// Row-local data-parallel-primitive moves. All patterns read a valid lane, so no lane keeps a
-// stale value. quad_perm [1,0,3,2] = 0xB1 (xor 1), [2,3,0,1] = 0x4E (xor 2),
-// row_half_mirror = 0x141 (i -> 7-i within 8), row_mirror = 0x140 (i -> 15-i within 16).
+// Row-local data-parallel-primitive moves, every lane active: quad_perm [1,0,3,2] = 0xB1
+// (xor 1), [2,3,0,1] = 0x4E (xor 2), row_half_mirror = 0x141 (i -> 7-i within 8), row_mirror =
+// 0x140 (i -> 15-i within 16). All read a valid lane of the same row, so the bound value (0) is
+// never used; asking for it (old = 0, bound_ctrl) lets the compiler fold the move into the
+// instruction that consumes it (v_min_u32_dpp and the like).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+    static_assert((CTRL >= 0x00 && CTRL <= 0xFF) || CTRL == 0x140 || CTRL == 0x141, "in-row permutations only");
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
 // All-reduce over aligned groups of `lanes` lanes (1, 2, 4, 8 or 16; uniform across the wave).

@@ -137,33 +137,33 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
 template <bool DIFF, bool GATHER, bool LG>
 __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v)[8], int lane, int64_t r0, int nr,
                                                bool valid, uint32_t c8, uint32_t c8raw) {
-    uint32_t mn8[8], mx8[8];
+    uint32_t mn8[8], mx8[8];  // unsigned keys
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        short2_t k = keys2(v[i].x), mn = k, mx = k;
-        k = keys2(v[i].y); mn = min2(mn, k); mx = max2(mx, k);
-        k = keys2(v[i].z); mn = min2(mn, k); mx = max2(mx, k);
-        k = keys2(v[i].w); mn = min2(mn, k); mx = max2(mx, k);
-        mn8[i] = (uint32_t)min((int)mn.x, (int)mn.y);
-        mx8[i] = (uint32_t)max((int)mx.x, (int)mx.y);
+        ushort2_t k = as_us2(ukeys2(v[i].x)), mn = k, mx = k;
+        k = as_us2(ukeys2(v[i].y)); mn = umin2(mn, k); mx = umax2(mx, k);
+        k = as_us2(ukeys2(v[i].z)); mn = umin2(mn, k); mx = umax2(mx, k);
+        k = as_us2(ukeys2(v[i].w)); mn = umin2(mn, k); mx = umax2(mx, k);
+        mn8[i] = min((uint32_t)mn.x, (uint32_t)mn.y);
+        mx8[i] = max((uint32_t)mx.x, (uint32_t)mx.y);
     }
     const uint32_t j = (uint32_t)lane & 7u;
     const bool b2 = (j & 4u) != 0u, b1 = (j & 2u) != 0u, b0 = (j & 1u) != 0u;
     uint32_t mn4[4], mx4[4];  // rows 4 b2 + k
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        mn4[k] = imin_op(b2 ? mn8[k + 4] : mn8[k], dpp<0x141>(b2 ? mn8[k] : mn8[k + 4]));
-        mx4[k] = imax_op(b2 ? mx8[k + 4] : mx8[k], dpp<0x141>(b2 ? mx8[k] : mx8[k + 4]));
+        mn4[k] = min(b2 ? mn8[k + 4] : mn8[k], dpp<0x141>(b2 ? mn8[k] : mn8[k + 4]));
+        mx4[k] = max(b2 ? mx8[k + 4] : mx8[k], dpp<0x141>(b2 ? mx8[k] : mx8[k + 4]));
     }
     uint32_t mn2[2], mx2[2];  // rows 4 b2 + 2 b1 + k
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        mn2[k] = imin_op(b1 ? mn4[k + 2] : mn4[k], dpp<0x4E>(b1 ? mn4[k] : mn4[k + 2]));
-        mx2[k] = imax_op(b1 ? mx4[k + 2] : mx4[k], dpp<0x4E>(b1 ? mx4[k] : mx4[k + 2]));
+        mn2[k] = min(b1 ? mn4[k + 2] : mn4[k], dpp<0x4E>(b1 ? mn4[k] : mn4[k + 2]));
+        mx2[k] = max(b1 ? mx4[k + 2] : mx4[k], dpp<0x4E>(b1 ? mx4[k] : mx4[k + 2]));
     }
-    const uint32_t gmn = imin_op(b0 ? mn2[1] : mn2[0], dpp<0xB1>(b0 ? mn2[0] : mn2[1]));  // row j
-    const uint32_t gmx = imax_op(b0 ? mx2[1] : mx2[0], dpp<0xB1>(b0 ? mx2[0] : mx2[1]));
-    const Int4Group gj = int4_group(key_to_f32((int)gmn), key_to_f32((int)gmx));
+    const uint32_t gmn = min(b0 ? mn2[1] : mn2[0], dpp<0xB1>(b0 ? mn2[0] : mn2[1]));  // row j
+    const uint32_t gmx = max(b0 ? mx2[1] : mx2[0], dpp<0xB1>(b0 ? mx2[0] : mx2[1]));
+    const Int4Group gj = int4_group(ukey_to_f32(gmn), ukey_to_f32(gmx));
     if ((int)j < nr && valid) {  // row j's metadata (the group's 8 lanes are all valid or all idle)
         const int64_t r = r0 + j;
         const int64_t wr = a.dst ? (int64_t)a.dst[r] : r;
