@@ -99,9 +99,12 @@ __device__ __forceinline__ void st_code(T* p, T w) {
         *p = w;
 }
 
-// The same at a wave-uniform base plus a lane's byte offset.
+// The same at a wave-uniform base plus a lane's byte offset. (The offset passes through an
+// empty asm at each store so that the compiler does not widen it once into a 64-bit register
+// pair and add the base in vector registers, which would lose the scalar-base form.)
 template <bool NT, class T>
 __device__ __forceinline__ void st_code_at(wave_ptr base, uint32_t off, T w) {
+    asm("" : "+v"(off));
     auto* p = reinterpret_cast<__attribute__((address_space(1))) T*>(base + off);
     if constexpr (NT)
         __builtin_nontemporal_store(w, p);
