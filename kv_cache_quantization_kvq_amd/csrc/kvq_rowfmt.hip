@@ -50,8 +50,10 @@ __device__ __forceinline__ uint32_t row_load(const EncArgs& a, int64_t t, int64_
     return c;
 }
 
-// RW rows' chunks of one lane, residual applied (same loads as the other vector encoders)
-template <int RW, bool DIFF, bool GATHER>
+// RW rows' chunks of one lane, residual applied (same loads as the other vector encoders).
+// UNI: r0 is the same on every lane, so a row's address is a scalar base plus the lane's 32-bit
+// byte offset (the host keeps a row's span below 2^31 bytes).
+template <int RW, bool DIFF, bool GATHER, bool UNI>
 __device__ __forceinline__ void row_chunks(const EncArgs& a, int64_t r0, uint32_t h, uint32_t d, u32x4 (&v)[RW]) {
     int64_t t[RW];
 #pragma unroll
@@ -59,13 +61,26 @@ __device__ __forceinline__ void row_chunks(const EncArgs& a, int64_t r0, uint32_
         const int64_t r = min<int64_t>(r0 + i, a.rows - 1);
         t[i] = GATHER ? (int64_t)a.pos[r] : r;
     }
+    if constexpr (UNI) {
+        const uint32_t coff = (uint32_t)(((int64_t)h * a.csh + d) * 2);
 #pragma unroll
-    for (int i = 0; i < RW; ++i)
-        v[i] = ld_stream(a.cur + row_offset(t[i], a.cpshift, a.cpst, a.cst) + (int64_t)h * a.csh + d);
+        for (int i = 0; i < RW; ++i)
+            v[i] = ld_stream_at(wave_base(a.cur, row_offset(t[i], a.cpshift, a.cpst, a.cst) * 2), coff);
+    } else {
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            v[i] = ld_stream(a.cur + row_offset(t[i], a.cpshift, a.cpst, a.cst) + (int64_t)h * a.csh + d);
+    }
     if constexpr (DIFF) {
         u32x4 p[RW];
+        if constexpr (UNI) {
+            const uint32_t poff = (uint32_t)(((int64_t)h * a.psh + d) * 2);
 #pragma unroll
-        for (int i = 0; i < RW; ++i) p[i] = ld_stream(a.prev + t[i] * a.pst + (int64_t)h * a.psh + d);
+            for (int i = 0; i < RW; ++i) p[i] = ld_stream_at(wave_base(a.prev, t[i] * a.pst * 2), poff);
+        } else {
+#pragma unroll
+            for (int i = 0; i < RW; ++i) p[i] = ld_stream(a.prev + t[i] * a.pst + (int64_t)h * a.psh + d);
+        }
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             v[i].x = sub_bf16x2(v[i].x, p[i].x);
@@ -120,12 +135,16 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
     const bool row_leader = valid && dc == 0u;
 
     u32x4 v[RW];
-    row_chunks<RW, DIFF, GATHER>(a, r0, h, d, v);
+    // scalar-base row addresses measured faster for FP8-row (more code bytes per row) and slower
+    // for NVFP4-row (whose per-row scale work already keeps the scalar unit busy)
+    constexpr bool UNI = !LG && FMT == FMT_FP8_ROW;
+    row_chunks<RW, DIFF, GATHER, UNI>(a, r0, h, d, v);
 
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
         const int64_t r = r0 + i;
         const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
+        const bool sbase = UNI && a.dst == nullptr;  // packed row r0 + i, the same on every lane
         const uint32_t am = chunk_amax(v[i]);
         const uint32_t amax = lanes_umax(am, lpr);
         const size_t hr = (size_t)wr * (uint32_t)a.H + h;  // (packed row, head) index
@@ -133,7 +152,13 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
             const Fp8Row rs = fp8_row(bf16_to_f32(amax));
             const uint2 o = fp8_chunk(v[i], rs);
             if (i < nr) {
-                if (valid) st_code<!DIFF>(reinterpret_cast<u32x2*>(a.codes + hr * (uint32_t)a.D + d), (u32x2){o.x, o.y});
+                if (valid) {
+                    if (sbase)
+                        st_code_at<!DIFF>(wave_base_w(a.codes, r * (int64_t)a.H * a.D), (uint32_t)(h * (uint32_t)a.D + d),
+                                          (u32x2){o.x, o.y});
+                    else
+                        st_code<!DIFF>(reinterpret_cast<u32x2*>(a.codes + hr * (uint32_t)a.D + d), (u32x2){o.x, o.y});
+                }
                 if (row_leader) reinterpret_cast<float*>(a.meta0)[hr] = rs.s;
             }
         } else {
@@ -143,7 +168,10 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
             const Fp4Block fb = fp4_block_direct(bam, g, rcp_pair(g));
             const uint32_t word = fp4_word(v[i], &fb, 0);
             if (i < nr && valid) {
-                st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
+                if (sbase)
+                    st_code_at<!DIFF>(wave_base_w(a.codes, r * (int64_t)a.C8 * 4), c8 * 4u, word);
+                else
+                    st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
                 const uint32_t nb = ((uint32_t)a.D + 15u) / 16u;
                 if ((dc & 1u) == 0u) reinterpret_cast<uint8_t*>(a.meta0)[hr * nb + (dc >> 1)] = (uint8_t)fb.code;
                 if (row_leader) reinterpret_cast<float*>(a.meta1)[hr] = g;
