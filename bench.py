@@ -360,7 +360,7 @@ def main() -> int:
 
     # per-op table from an instrumented pass (events around every op; not the timed region)
     prof = []
-    for _ in range(min(10, max(1, args.steps))):
+    for _ in range(min(20, max(1, args.steps))):
         step(events=prof)
     torch.cuda.synchronize()
     per_op = {}

@@ -166,6 +166,31 @@ def test_unaligned_strides_take_generic_path(fmt, G, kind):
     assert_bits_equal(gy, oy, "decoded")
 
 
+@pytest.mark.parametrize("fmt,G", [("int4", 64), ("nvfp4", 16), ("fp8_row", 0)])
+@pytest.mark.parametrize("kind", KINDS)
+def test_head_stride_beyond_32bit_row_offsets(fmt, G, kind):
+    # 16-byte aligned, but a row spans more than 2^30 elements (heads 2^30 elements apart): the
+    # vector kernels address a row's elements by a 32-bit byte offset from the row start, so
+    # this view must take the generic path and still match the oracle
+    rng = np.random.default_rng(12)
+    T, H, D = 32, 2, 64
+    sh = (1 << 30) + 64
+    x = normal_kv(rng, T, H, D)
+    x1 = normal_kv(rng, T, H, D)
+    base = torch.zeros((T - 1) * D + (H - 1) * sh + D, dtype=torch.bfloat16, device="cuda")
+    view = torch.as_strided(base, (T, H, D), (D, sh, 1))
+    view.copy_(to_dev(x))
+    gp, op, gy, oy = roundtrip(x, kind, fmt, G, xdev=view)
+    assert_same_packed(gp, op, "huge head stride")
+    assert_bits_equal(gy, oy, "decoded")
+    r0 = to_dev(oy)
+    view.copy_(to_dev(x1))
+    gr = kvq.encode_residual(view, r0, kind, fmt, G)
+    orr = oracle.encode_residual(x1, oy, kind, fmt, G)
+    assert_same_packed(gr, orr, "huge head stride residual")
+    del base, view
+
+
 @pytest.mark.parametrize("fmt,G", [("int4", 64), ("nvfp4", 16)])
 @pytest.mark.parametrize("kind", KINDS)
 def test_empty_tensors(fmt, G, kind):
