@@ -352,11 +352,17 @@ kvq_status decode_run(const kvq_packed* p, int64_t rows, const kvq_tensor* prev,
 }
 
 // Copy `rows` rows of one strided bf16 view into another (the row-copy kernel).
+// Copies `rows` rows of a [rows, H, D] bf16 view; rows r >= split are read src_jump and
+// written dst_jump elements further on (both multiples of the row pitches).
 kvq_status copy_view_rows(const void* src, int64_t sst, int64_t ssh, void* dst, int64_t dst_t, int64_t dsh,
-                          int64_t rows, int64_t H, int64_t D, hipStream_t stream) {
+                          int64_t rows, int64_t H, int64_t D, hipStream_t stream, int64_t split = 0,
+                          int64_t src_jump = 0, int64_t dst_jump = 0) {
     if (rows * H * D == 0) return KVQ_OK;
     CopyArgs c;
     memset(&c, 0, sizeof c);
+    c.split = split;
+    c.src_jump = src_jump;
+    c.dst_jump = dst_jump;
     c.src = static_cast<const uint16_t*>(src);
     c.sst = sst;
     c.ssh = ssh;
@@ -633,9 +639,9 @@ kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int6
                             stream)))
         return st;
     out->full_T = T;
-    if ((st = copy_view_rows(cur->data, cur->stride_t, cur->stride_h, window, H * D, D, ns, H, D, stream))) return st;
-    return copy_view_rows(static_cast<const uint16_t*>(cur->data) + (T - nr) * cur->stride_t, cur->stride_t,
-                          cur->stride_h, static_cast<uint16_t*>(window) + ns * H * D, H * D, D, nr, H, D, stream);
+    // window rows [0, ns) <- cur rows [0, ns); window rows [ns, ns + nr) <- cur rows [T - nr, T)
+    return copy_view_rows(cur->data, cur->stride_t, cur->stride_h, window, H * D, D, ns + nr, H, D, stream, ns,
+                          mid * cur->stride_t, 0);
 }
 
 kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
@@ -664,10 +670,9 @@ kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t si
     kvq_tensor pm;
     if (prev) pm = row_slice(prev, ns, mid);
     if ((st = decode_run(p, mid, prev ? &pm : nullptr, view_of(&om), nullptr, nullptr, stream))) return st;
-    if ((st = copy_view_rows(window, H * D, D, out->data, out->stride_t, out->stride_h, ns, H, D, stream))) return st;
-    return copy_view_rows(static_cast<const uint16_t*>(window) + ns * H * D, H * D, D,
-                          static_cast<uint16_t*>(out->data) + (T - nr) * out->stride_t, out->stride_t, out->stride_h,
-                          nr, H, D, stream);
+    // out rows [0, ns) <- window rows [0, ns); out rows [T - nr, T) <- window rows [ns, ns + nr)
+    return copy_view_rows(window, H * D, D, out->data, out->stride_t, out->stride_h, ns + nr, H, D, stream, ns, 0,
+                          mid * out->stride_t);
 }
 
 size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq, int64_t D) {

@@ -185,7 +185,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
     }
 }
 
-// Row copy (out-of-place sparse decode: absent rows inherit prev bit for bit).
+// Row copy (out-of-place sparse decode: absent rows inherit prev bit for bit; the protected rows
+// of a BF16 window, front and back ranges in one launch).
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_copy_rows(CopyArgs a) {
     if constexpr (VEC) {
@@ -196,8 +197,9 @@ __global__ __launch_bounds__(kThreads) void k_copy_rows(CopyArgs a) {
         const uint32_t c8 = (uint32_t)u - r * (uint32_t)a.C8;
         const uint32_t h = fdiv(c8, a.div_D8);
         const uint32_t d = (c8 - h * (uint32_t)(a.D / 8)) * 8u;
-        *reinterpret_cast<uint4*>(a.dst + (int64_t)r * a.dst_t + (int64_t)h * a.dsh + d) =
-            *reinterpret_cast<const uint4*>(a.src + (int64_t)r * a.sst + (int64_t)h * a.ssh + d);
+        const bool far = (int64_t)r >= a.split;
+        *reinterpret_cast<uint4*>(a.dst + (far ? a.dst_jump : 0) + (int64_t)r * a.dst_t + (int64_t)h * a.dsh + d) =
+            *reinterpret_cast<const uint4*>(a.src + (far ? a.src_jump : 0) + (int64_t)r * a.sst + (int64_t)h * a.ssh + d);
     } else {
         const uint64_t total = (uint64_t)a.T * a.H * a.D;
         const uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -207,7 +209,8 @@ __global__ __launch_bounds__(kThreads) void k_copy_rows(CopyArgs a) {
         const int64_t rem = (int64_t)u - r * HD;
         const int64_t h = rem / a.D;
         const int64_t d = rem - h * a.D;
-        a.dst[r * a.dst_t + h * a.dsh + d] = a.src[r * a.sst + h * a.ssh + d];
+        const bool far = r >= a.split;
+        a.dst[(far ? a.dst_jump : 0) + r * a.dst_t + h * a.dsh + d] = a.src[(far ? a.src_jump : 0) + r * a.sst + h * a.ssh + d];
     }
 }
 

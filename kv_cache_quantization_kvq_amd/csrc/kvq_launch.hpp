@@ -111,12 +111,16 @@ __device__ __forceinline__ void task_lane(const Args& a, uint32_t task, int lane
     }
 }
 
+// Row copy: row r of src to row r of dst, except that rows r >= split are read src_jump
+// elements further on and written dst_jump elements further on (two row ranges in one launch;
+// jumps of 0 for a plain copy).
 struct CopyArgs {
     const uint16_t* src;
     int64_t sst, ssh;
     uint16_t* dst;
     int64_t dst_t, dsh;
     int64_t T;
+    int64_t split, src_jump, dst_jump;
     int32_t H, D, C8;
     FastDiv div_C8, div_D8;
 };
