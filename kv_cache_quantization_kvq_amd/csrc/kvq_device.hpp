@@ -260,12 +260,14 @@ __device__ __forceinline__ ushort2_t mag2(uint32_t w) { return as_us2(w & 0x7FFF
 
 // Row-local data-parallel-primitive moves, every lane active: quad_perm [1,0,3,2] = 0xB1
 // (xor 1), [2,3,0,1] = 0x4E (xor 2), row_half_mirror = 0x141 (i -> 7-i within 8), row_mirror =
-// 0x140 (i -> 15-i within 16). All read a valid lane of the same row, so the bound value (0) is
+// 0x140 (i -> 15-i within 16), row_ror:n = 0x120 + n (rotation within 16; n = 8 pairs i with
+// i xor 8). All read a valid lane of the same row, so the bound value (0) is
 // never used; asking for it (old = 0, bound_ctrl) lets the compiler fold the move into the
 // instruction that consumes it (v_min_u32_dpp and the like).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    static_assert((CTRL >= 0x00 && CTRL <= 0xFF) || CTRL == 0x140 || CTRL == 0x141, "in-row permutations only");
+    static_assert((CTRL >= 0x00 && CTRL <= 0xFF) || (CTRL >= 0x121 && CTRL <= 0x12F) || CTRL == 0x140 || CTRL == 0x141,
+                  "in-row permutations only");
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
