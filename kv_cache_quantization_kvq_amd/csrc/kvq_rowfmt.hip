@@ -115,144 +115,6 @@ __device__ __forceinline__ uint2 fp8_chunk(const u32x4& v, const Fp8Row& rs) {
     return o;
 }
 
-// NVFP4-row rows of a wave task of 8 rows, for rows of 8 or more lanes (head_dim >= 64). A
-// row's multiplier and a block's decode scale and reciprocal take about 100 VALU instructions
-// per row on every lane when each lane computes them for its own rows; here the work is split:
-//   - the 8 rows' chunk maxima are reduce-scattered over each group of 8 lanes (pairs j <-> 7-j,
-//     j <-> j^2, j <-> j^1) and then combined across the row's 8-lane groups, so that lane j of
-//     every group holds row j's amax and computes that row's g and its reciprocal pair;
-//   - the two lanes of a 16-channel block share the 8 rows' block constants: the even lane
-//     computes rows 0, 2, 4, 6 and the odd lane rows 1, 3, 5, 7, reading each row's g, y and
-//     ylo from the lane that holds it (ds_bpermute), and the two swap their results (DPP).
-// Every value is the same function of the same inputs as in the per-lane order, so the codes
-// and scales are the same bits.
-template <bool DIFF, bool GATHER>
-__device__ __forceinline__ void nvfp4_row_task(const EncArgs& a, const u32x4 (&v)[8], int lane, int64_t r0, int nr,
-                                               bool valid, uint32_t c8, uint32_t c8raw, uint32_t h, uint32_t dc,
-                                               int lpr) {
-    uint32_t am[8], bam[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        am[i] = chunk_amax(v[i]);
-        bam[i] = max(am[i], dpp<0xB1>(am[i]));  // the 16-channel block: this lane and its neighbour
-    }
-    const uint32_t j = (uint32_t)lane & 7u;
-    const bool b2 = (j & 4u) != 0u, b1 = (j & 2u) != 0u, b0 = (j & 1u) != 0u;
-    uint32_t m4[4], m2[2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) m4[k] = max(b2 ? am[k + 4] : am[k], dpp<0x141>(b2 ? am[k] : am[k + 4]));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) m2[k] = max(b1 ? m4[k + 2] : m4[k], dpp<0x4E>(b1 ? m4[k] : m4[k + 2]));
-    uint32_t mj = max(b0 ? m2[1] : m2[0], dpp<0xB1>(b0 ? m2[0] : m2[1]));  // row j, this 8-lane group
-    if (lpr >= 16) mj = max(mj, dpp<0x128>(mj));                           // the row's other group(s)
-    if (lpr >= 32) mj = max(mj, (uint32_t)__shfl_xor((int)mj, 16));
-    if (lpr >= 64) mj = max(mj, (uint32_t)__shfl_xor((int)mj, 32));
-    const float gj = fp4_global_rn(mj);
-    const RcpPair pj = rcp_pair(gj);
-
-    // this lane's four rows: i = 2m + e
-    const uint32_t e = (uint32_t)lane & 1u;
-    const int src = ((lane & ~7) + (int)e) * 4;  // ds_bpermute byte address of row e's lane
-    uint32_t code[8], flags[8];
-    float sdec[8], rcp[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int sa = src + 8 * m;  // lane (lane & ~7) + 2m + e
-        const float g = __int_as_float(__builtin_amdgcn_ds_bpermute(sa, __float_as_int(gj)));
-        RcpPair p;
-        p.b = g;
-        p.y = __int_as_float(__builtin_amdgcn_ds_bpermute(sa, __float_as_int(pj.y)));
-        p.ylo = __int_as_float(__builtin_amdgcn_ds_bpermute(sa, __float_as_int(pj.ylo)));
-        p.fast = g >= 7.888609052210118e-31f && g <= 1.2676506002282294e30f;  // as rcp_pair(g)
-        const Fp4Block fb = fp4_block_direct(e ? bam[2 * m + 1] : bam[2 * m], g, p);
-        // own row 2m + e, then the neighbour's row 2m + 1 - e
-        const uint32_t cf = fb.code | (fb.div ? 0x100u : 0u);
-        const uint32_t cf_o = dpp<0xB1>(cf);
-        const float sd_o = __uint_as_float(dpp<0xB1>(__float_as_uint(fb.s_dec)));
-        const float rc_o = __uint_as_float(dpp<0xB1>(__float_as_uint(fb.rcp)));
-        code[2 * m] = e ? cf_o : cf;
-        code[2 * m + 1] = e ? cf : cf_o;
-        sdec[2 * m] = e ? sd_o : fb.s_dec;
-        sdec[2 * m + 1] = e ? fb.s_dec : sd_o;
-        rcp[2 * m] = e ? rc_o : fb.rcp;
-        rcp[2 * m + 1] = e ? fb.rcp : rc_o;
-    }
-    const uint32_t nb = ((uint32_t)a.D + 15u) / 16u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t r = r0 + i;
-        const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
-        const size_t hr = (size_t)wr * (uint32_t)a.H + h;  // (packed row, head) index
-        Fp4Block fb;
-        fb.code = code[i] & 0xFFu;
-        fb.div = (code[i] & 0x100u) != 0u;
-        fb.s_dec = sdec[i];
-        fb.rcp = rcp[i];
-        const uint32_t word = fp4_word(v[i], &fb, 0);
-        if (i < nr && valid) {
-            st_code<!DIFF>(reinterpret_cast<uint32_t*>(a.codes) + (size_t)wr * (uint32_t)a.C8 + c8, word);
-            if (e == 0u) reinterpret_cast<uint8_t*>(a.meta0)[hr * nb + (dc >> 1)] = (uint8_t)fb.code;
-            if (dc == (uint32_t)i) reinterpret_cast<float*>(a.meta1)[hr] = gj;  // lane i of the row's first group
-        }
-        if constexpr (GATHER) {
-            if (i < nr && c8raw == 0) a.pos_out[r] = a.pos[r];
-        }
-    }
-}
-
-// FP8-row rows of a wave task of 8 rows, for rows of 8 or more lanes: the row maxima are
-// reduce-scattered as in nvfp4_row_task, lane j of every 8-lane group computes row j's scale
-// (an IEEE division) and reciprocal pair, and every lane reads the 8 rows' (s, y, ylo) from
-// those lanes (ds_bpermute); a row that needs the division path travels with y = -1, which the
-// quotient never uses. Same values as each lane computing every row's constants itself.
-template <bool DIFF, bool GATHER>
-__device__ __forceinline__ void fp8_row_task(const EncArgs& a, const u32x4 (&v)[8], int lane, int64_t r0, int nr,
-                                             bool valid, uint32_t c8, uint32_t c8raw, uint32_t h, uint32_t dc,
-                                             int lpr) {
-    uint32_t am[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am[i] = chunk_amax(v[i]);
-    const uint32_t j = (uint32_t)lane & 7u;
-    const bool b2 = (j & 4u) != 0u, b1 = (j & 2u) != 0u, b0 = (j & 1u) != 0u;
-    uint32_t m4[4], m2[2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) m4[k] = max(b2 ? am[k + 4] : am[k], dpp<0x141>(b2 ? am[k] : am[k + 4]));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) m2[k] = max(b1 ? m4[k + 2] : m4[k], dpp<0x4E>(b1 ? m4[k] : m4[k + 2]));
-    uint32_t mj = max(b0 ? m2[1] : m2[0], dpp<0xB1>(b0 ? m2[0] : m2[1]));
-    if (lpr >= 16) mj = max(mj, dpp<0x128>(mj));
-    if (lpr >= 32) mj = max(mj, (uint32_t)__shfl_xor((int)mj, 16));
-    if (lpr >= 64) mj = max(mj, (uint32_t)__shfl_xor((int)mj, 32));
-    const Fp8Row rj = fp8_row(bf16_to_f32(mj));
-    const float yj = rj.slow ? -1.0f : rj.y;
-    const int base = (lane & ~7) * 4;  // ds_bpermute byte address of the group's lane 0
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int sa = base + 4 * i;
-        Fp8Row rs;
-        rs.s = __int_as_float(__builtin_amdgcn_ds_bpermute(sa, __float_as_int(rj.s)));
-        const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(sa, __float_as_int(yj)));
-        rs.ylo = __int_as_float(__builtin_amdgcn_ds_bpermute(sa, __float_as_int(rj.ylo)));
-        rs.slow = y < 0.0f;
-        rs.y = y;
-        const uint2 o = fp8_chunk(v[i], rs);
-        const int64_t r = r0 + i;
-        const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
-        const size_t hr = (size_t)wr * (uint32_t)a.H + h;  // (packed row, head) index
-        if (i < nr && valid) {
-            if (a.dst == nullptr)
-                st_code_at<!DIFF>(wave_base_w(a.codes, r * (int64_t)a.H * a.D), (uint32_t)(h * (uint32_t)a.D + dc * 8u),
-                                  (u32x2){o.x, o.y});
-            else
-                st_code<!DIFF>(reinterpret_cast<u32x2*>(a.codes + hr * (uint32_t)a.D + dc * 8u), (u32x2){o.x, o.y});
-            if (dc == (uint32_t)i) reinterpret_cast<float*>(a.meta0)[hr] = rj.s;  // lane i of the row's first group
-        }
-        if constexpr (GATHER) {
-            if (i < nr && c8raw == 0) a.pos_out[r] = a.pos[r];
-        }
-    }
-}
-
 // One wave task: RW rows of a 64-chunk slab (the VALUE encoder's tiling).
 template <int FMT, bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
@@ -277,15 +139,6 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
     // for NVFP4-row (whose per-row scale work already keeps the scalar unit busy)
     constexpr bool UNI = !LG && FMT == FMT_FP8_ROW;
     row_chunks<RW, DIFF, GATHER, UNI>(a, r0, h, d, v);
-    if constexpr (!LG && RW == 8) {
-        if (lpr >= 8) {  // wave-uniform
-            if constexpr (FMT == FMT_NVFP4_ROW)
-                nvfp4_row_task<DIFF, GATHER>(a, v, lane, r0, nr, valid, c8, c8raw, h, dc, lpr);
-            else
-                fp8_row_task<DIFF, GATHER>(a, v, lane, r0, nr, valid, c8, c8raw, h, dc, lpr);
-            return;
-        }
-    }
 
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
