@@ -151,6 +151,12 @@ __device__ __forceinline__ uint32_t e4m3_encode(float s) {
     return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scaling, then nearest-even
 }
 
+// e4m3_encode(s) for 0 <= s <= 448 in one instruction: v_cvt_pk_fp8_f32, which the device probe
+// shows equal to e4m3_encode(|v|) with the sign bit of v for every binary32 |v| <= 448.
+__device__ __forceinline__ uint32_t e4m3_encode_hw(float s) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s, s, 0, false) & 0xFFu;
+}
+
 // E4M3fn code (sign bit clear, finite) -> binary32, exact.
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
     uint32_t E = (b >> 3) & 0xFu, M = b & 7u;
@@ -417,7 +423,7 @@ __device__ __forceinline__ Fp4Block fp4_block(uint32_t bamax_bits, float g, cons
     const float t6 = div_const<6>(bf16_to_f32(bamax_bits));  // fl(bamax / 6), exactly
     float s = __fmul_rn(g, t6);
     s = (s <= 448.0f) ? s : 448.0f;  // also maps +inf to 448
-    b.code = e4m3_encode(s);
+    b.code = e4m3_encode_hw(s);  // s in [0, 448]
     const f32x2 e = t.e[b.code];
     b.s_dec = e[0];
     b.div = __builtin_isinf(e[1]);
@@ -531,7 +537,7 @@ __device__ __forceinline__ Fp4Block fp4_block_direct(uint32_t bamax_bits, float 
     const float t6 = div_const<6>(bf16_to_f32(bamax_bits));
     float s = __fmul_rn(g, t6);
     s = (s <= 448.0f) ? s : 448.0f;
-    b.code = e4m3_encode(s);
+    b.code = e4m3_encode_hw(s);  // s in [0, 448]
     const f32x2 e = fp4_code_scales_rn(b.code, gp);
     b.s_dec = e[0];
     b.rcp = e[1];
