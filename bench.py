@@ -358,7 +358,7 @@ def main() -> int:
         torch.cuda.synchronize()
         print(f"copy calibration: {x0.numel() * 2} bytes read and written", file=sys.stderr)
 
-    # per-op table from an instrumented pass (events around every op; not the timed region)
+    # per-op table from up to 20 instrumented steps (events around every op; not the timed region)
     prof = []
     for _ in range(min(20, max(1, args.steps))):
         step(events=prof)
