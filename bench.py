@@ -396,6 +396,28 @@ def main() -> int:
     extras = None
     if not args.no_extras:
         extras = run_extras(kvq, torch, X, T, dev)
+        # context: the same step captured once as a HIP graph and replayed (every call only
+        # enqueues kernels, so it can be captured); the difference to `value` is the launch gaps
+        side = torch.cuda.Stream(dev)
+        with torch.cuda.stream(side):
+            step()  # the NVFP4 workspace of this stream exists before capture
+            side.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                step()
+            graph.replay()
+            side.synchronize()
+            t_g = time.perf_counter()
+            for _ in range(args.steps):
+                graph.replay()
+            side.synchronize()
+            g_step = (time.perf_counter() - t_g) / args.steps
+        del graph
+        g_gbs = step_bytes / g_step / 1e9
+        extras["context-step_as_hip_graph"] = {"us": round(g_step * 1e6, 1), "GBps": round(g_gbs, 1),
+                                               "pct_peak": round(100 * g_gbs / PEAK_HBM_GBS, 1)}
+        print(f"extra {'context-step_as_hip_graph':38s} {g_step * 1e6:9.1f} us per step  {g_gbs:7.1f} GB/s  "
+              f"{100 * g_gbs / PEAK_HBM_GBS:5.1f}% of peak", file=sys.stderr)
 
     cpu = None
     if not args.no_cpu_baseline:
