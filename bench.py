@@ -282,7 +282,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this codec build measures one GPU only; multi-GPU runs are not part of it "
+        print("bench.py measures one GPU only: the codec has no multi-GPU path "
               f"(got --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         return 2
 
