@@ -234,8 +234,29 @@ def measured_traffic(op_name: str):
     return float(op["traffic_bytes"])
 
 
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rmse_np(y_bits: np.ndarray, x_bits: np.ndarray) -> float:
+    d = bf16_to_f64(y_bits) - bf16_to_f64(x_bits)
+    return float(np.sqrt(np.mean(d * d)))
+
+
+def rmse_dev(torch, y, x, chunk: int = 8192) -> float:
+    """Root-mean-square of y - x (bf16 [T, H, D] device tensors), accumulated in float64."""
+    acc, n = 0.0, 0
+    for t in range(0, y.shape[0], chunk):
+        d = y[t:t + chunk].double() - x[t:t + chunk].double()
+        acc += float((d * d).sum())
+        n += d.numel()
+    return (acc / max(n, 1)) ** 0.5
+
+
 def cpu_baseline(T_sample: int):
-    """The oracle (single-threaded plain C) on the leading T_sample rows of the same workload."""
+    """The oracle (single-threaded plain C) on the leading T_sample rows of the same workload.
+    Returns the baseline record and the oracle's reconstruction RMSE (unpack and residual decode)
+    for each format and kind on those rows."""
     import oracle
     from workloads import c4_residual_target, c4_tensors
 
@@ -245,15 +266,19 @@ def cpu_baseline(T_sample: int):
     n = T_sample * H * D
     total_bytes = 0.0
     t0 = time.perf_counter()
+    outs = {}
     for fmt, G in FORMS:
         for kind in KINDS:
             X0, X1 = data[kind]
             p = oracle.pack(X0, kind, fmt, G)
             R0 = oracle.unpack(p)
             r = oracle.encode_residual(X1, R0, kind, fmt, G)
-            oracle.decode_residual(r, R0)
+            R1 = oracle.decode_residual(r, R0)
             total_bytes += sum(algo_bytes(op, fmt, n) for op in OPS)
+            outs[(fmt, kind)] = (R0, R1)
     dt = time.perf_counter() - t0
+    rmse = {f"{fmt}-{kind}": (rmse_np(R0, data[kind][0]), rmse_np(R1, data[kind][1]))
+            for (fmt, kind), (R0, R1) in outs.items()}
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -263,7 +288,7 @@ def cpu_baseline(T_sample: int):
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"leading {T_sample} of {T_FULL} tokens (H=8, D=128), all 16 ops of one step, "
                       f"single-threaded C oracle, {dt:.1f} s",
-            "cpu": cpu_model}
+            "cpu": cpu_model}, rmse
 
 
 def main() -> int:
@@ -419,9 +444,38 @@ def main() -> int:
         print(f"extra {'context-step_as_hip_graph':38s} {g_step * 1e6:9.1f} us per step  {g_gbs:7.1f} GB/s  "
               f"{100 * g_gbs / PEAK_HBM_GBS:5.1f}% of peak", file=sys.stderr)
 
+    # reconstruction RMSE: unpack (R0 - X0) and residual decode (R1 - X1) of the full tensors, and
+    # the same ops on the leading sample rows encoded as tensors of their own (as the oracle does
+    # below), whose RMSE must match the oracle's
+    Ts = min(args.cpu_sample_tokens, T)
+    quality = {}
+    for fmt, G in FORMS:
+        for kind in KINDS:
+            b = bufs[(fmt, kind)]
+            x0, x1 = X[kind]
+            s0, s1 = x0[:Ts], x1[:Ts]
+            r0s = kvq.unpack(kvq.pack(s0, kind, fmt, G))
+            r1s = kvq.decode_residual(kvq.encode_residual(s1, r0s, kind, fmt, G), r0s)
+            quality[f"{fmt}-{kind}"] = dict(
+                unpack=rmse_dev(torch, b["R0"], x0), residual=rmse_dev(torch, b["R1"], x1),
+                sample_unpack=rmse_dev(torch, r0s, s0), sample_residual=rmse_dev(torch, r1s, s1))
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(min(args.cpu_sample_tokens, T))
+        cpu, oracle_rmse = cpu_baseline(Ts)
+        worst = 0.0
+        for key, (ou, orr) in oracle_rmse.items():
+            q = quality[key]
+            q["oracle_sample_unpack"], q["oracle_sample_residual"] = ou, orr
+            worst = max(worst, abs(q["sample_unpack"] - ou) / max(ou, 1e-300),
+                        abs(q["sample_residual"] - orr) / max(orr, 1e-300))
+        quality["max_rel_diff_vs_oracle"] = worst
+    for key, q in quality.items():
+        if isinstance(q, dict):
+            print(f"rmse {key:12s} unpack {q['unpack']:.6e}  residual {q['residual']:.6e}  (sample of {Ts}: "
+                  f"{q['sample_unpack']:.6e} / {q['sample_residual']:.6e}"
+                  + (f"; oracle {q['oracle_sample_unpack']:.6e} / {q['oracle_sample_residual']:.6e})"
+                     if "oracle_sample_unpack" in q else ")"), file=sys.stderr)
 
     line = {
         "metric": "codec GB/s and % HBM peak (pack/unpack/residual), INT4-G64 & NVFP4-G16",
@@ -454,6 +508,8 @@ def main() -> int:
             "traffic": measured_traffic(dom_name),
         },
         "cpu_baseline": cpu,
+        "rmse": {k: ({kk: float(f"{vv:.7g}") for kk, vv in v.items()} if isinstance(v, dict) else float(f"{v:.3g}"))
+                 for k, v in quality.items()},
         "extras": extras,
     }
     if args.detail:
