@@ -255,8 +255,8 @@ def rmse_dev(torch, y, x, chunk: int = 8192) -> float:
 
 def cpu_baseline(T_sample: int):
     """The oracle (single-threaded plain C) on the leading T_sample rows of the same workload.
-    Returns the baseline record and the oracle's reconstruction RMSE (unpack and residual decode)
-    for each format and kind on those rows."""
+    Returns the baseline record and, for each format and kind on those rows, the oracle's
+    reconstruction RMSE (unpack, residual decode) and the reconstructions themselves."""
     import oracle
     from workloads import c4_residual_target, c4_tensors
 
@@ -277,7 +277,7 @@ def cpu_baseline(T_sample: int):
             total_bytes += sum(algo_bytes(op, fmt, n) for op in OPS)
             outs[(fmt, kind)] = (R0, R1)
     dt = time.perf_counter() - t0
-    rmse = {f"{fmt}-{kind}": (rmse_np(R0, data[kind][0]), rmse_np(R1, data[kind][1]))
+    rmse = {f"{fmt}-{kind}": (rmse_np(R0, data[kind][0]), rmse_np(R1, data[kind][1]), R0, R1)
             for (fmt, kind), (R0, R1) in outs.items()}
     cpu_model = ""
     try:
@@ -449,6 +449,7 @@ def main() -> int:
     # below), whose RMSE must match the oracle's
     Ts = min(args.cpu_sample_tokens, T)
     quality = {}
+    samples = {}
     for fmt, G in FORMS:
         for kind in KINDS:
             b = bufs[(fmt, kind)]
@@ -459,14 +460,18 @@ def main() -> int:
             quality[f"{fmt}-{kind}"] = dict(
                 unpack=rmse_dev(torch, b["R0"], x0), residual=rmse_dev(torch, b["R1"], x1),
                 sample_unpack=rmse_dev(torch, r0s, s0), sample_residual=rmse_dev(torch, r1s, s1))
+            samples[f"{fmt}-{kind}"] = (r0s, r1s)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu, oracle_rmse = cpu_baseline(Ts)
         worst = 0.0
-        for key, (ou, orr) in oracle_rmse.items():
+        for key, (ou, orr, oR0, oR1) in oracle_rmse.items():
             q = quality[key]
             q["oracle_sample_unpack"], q["oracle_sample_residual"] = ou, orr
+            # parity verdict: the sample reconstructions bit for bit against the oracle's
+            g0, g1 = (t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for t in samples[key])
+            q["bit_exact_sample"] = bool(np.array_equal(g0, oR0) and np.array_equal(g1, oR1))
             worst = max(worst, abs(q["sample_unpack"] - ou) / max(ou, 1e-300),
                         abs(q["sample_residual"] - orr) / max(orr, 1e-300))
         quality["max_rel_diff_vs_oracle"] = worst
@@ -474,8 +479,8 @@ def main() -> int:
         if isinstance(q, dict):
             print(f"rmse {key:12s} unpack {q['unpack']:.6e}  residual {q['residual']:.6e}  (sample of {Ts}: "
                   f"{q['sample_unpack']:.6e} / {q['sample_residual']:.6e}"
-                  + (f"; oracle {q['oracle_sample_unpack']:.6e} / {q['oracle_sample_residual']:.6e})"
-                     if "oracle_sample_unpack" in q else ")"), file=sys.stderr)
+                  + (f"; oracle {q['oracle_sample_unpack']:.6e} / {q['oracle_sample_residual']:.6e}, "
+                     f"bit-exact {q['bit_exact_sample']})" if "oracle_sample_unpack" in q else ")"), file=sys.stderr)
 
     line = {
         "metric": "codec GB/s and % HBM peak (pack/unpack/residual), INT4-G64 & NVFP4-G16",
@@ -508,7 +513,8 @@ def main() -> int:
             "traffic": measured_traffic(dom_name),
         },
         "cpu_baseline": cpu,
-        "rmse": {k: ({kk: float(f"{vv:.7g}") for kk, vv in v.items()} if isinstance(v, dict) else float(f"{v:.3g}"))
+        "rmse": {k: ({kk: (vv if isinstance(vv, bool) else float(f"{vv:.7g}")) for kk, vv in v.items()}
+                     if isinstance(v, dict) else float(f"{v:.3g}"))
                  for k, v in quality.items()},
         "extras": extras,
     }
