@@ -264,7 +264,9 @@ kvq_status encode_common(const View& cur, const kvq_tensor* prev, const int32_t*
     if (sz[KVQ_PLANE_META0] && !out->meta0) return KVQ_ERR_NULL;
     if (sz[KVQ_PLANE_META1] && !out->meta1) return KVQ_ERR_NULL;
     if (sz[KVQ_PLANE_GLOBAL] && !out->global_scale) return KVQ_ERR_NULL;
-    if (sz[KVQ_PLANE_POSITIONS] && !out->positions) return KVQ_ERR_NULL;
+    // a sparse residual always owns a position plane, also with M == 0: a NULL plane would
+    // make the descriptor read as dense
+    if (sparse && !out->positions) return KVQ_ERR_NULL;
     if (format == KVQ_NVFP4 && !workspace) return KVQ_ERR_WORKSPACE;
 
     out->format = format;

@@ -145,6 +145,9 @@ def test_residual_and_decode_argument_errors():
     # sparse without a positions plane in the descriptor
     assert lib.kvq_encode_residual(ctypes.byref(x), ctypes.byref(x), ctypes.c_void_p(0x7000), 4, 0, 0, 64,
                                    ctypes.byref(_packed(positions=None)), None, None) == 1
+    # ... also with M == 0: a sparse residual always owns a position plane
+    assert lib.kvq_encode_residual(ctypes.byref(x), ctypes.byref(x), ctypes.c_void_p(0x7000), 0, 0, 0, 64,
+                                   ctypes.byref(_packed(positions=None)), None, None) == 1
     # unpack: descriptor/tensor mismatch
     d = _packed(format=0, kind=0, group_size=16, dtype=0, rows=16, H=2, D=16, full_T=16)
     assert lib.kvq_unpack(ctypes.byref(d), ctypes.byref(y), None) == 7
