@@ -25,6 +25,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
+_LIB_OMP = os.path.join(_HERE, "libkvq_oracle_omp.so")
 
 KIND = {"key": 0, "value": 1}
 FORMAT = {"int4": 0, "nvfp4": 1, "nvfp4_row": 2, "fp8_row": 3}
@@ -34,23 +35,40 @@ CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-s
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc into ``oracle/libkvq_oracle.so``."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
+    """Compile the oracle with gcc: ``oracle/libkvq_oracle.so`` (single-threaded) and
+    ``oracle/libkvq_oracle_omp.so`` (the same source with -fopenmp: loops over independent
+    groups and rows on all threads, same bits)."""
+    for path, extra in ((_LIB, []), (_LIB_OMP, ["-fopenmp"])):
+        if force or not os.path.exists(path):
+            tmp = path + ".tmp"
+            subprocess.run(["gcc", *CFLAGS, *extra, _SRC, "-o", tmp, "-lm"], check=True)
+            os.replace(tmp, path)
     return _LIB
 
 
-_lib_handle = None
+_handles = {}
+_threaded = False
+
+
+def set_threaded(on: bool) -> bool:
+    """Route every call below to the OpenMP build (True) or the single-threaded build (False).
+    Returns the previous setting."""
+    global _threaded
+    prev, _threaded = _threaded, bool(on)
+    return prev
+
+
+def threads() -> int:
+    """Threads the active build runs its loops on (1 for the single-threaded build)."""
+    return int(_lib().kvq_oracle_threads())
 
 
 def _lib():
-    global _lib_handle
-    if _lib_handle is None:
-        if not os.path.exists(_LIB):
-            build()
-        lib = ctypes.CDLL(_LIB)
+    path = _LIB_OMP if _threaded else _LIB
+    if path not in _handles:
+        if not os.path.exists(path):
+            build(force=False)
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         i32 = ctypes.c_int32
@@ -96,8 +114,10 @@ def _lib():
         lib.kvq_oracle_e4m3_to_f32.restype = ctypes.c_float
         lib.kvq_oracle_e2m1_to_f32.argtypes = [ctypes.c_uint8]
         lib.kvq_oracle_e2m1_to_f32.restype = ctypes.c_float
-        _lib_handle = lib
-    return _lib_handle
+        lib.kvq_oracle_threads.argtypes = []
+        lib.kvq_oracle_threads.restype = ci
+        _handles[path] = lib
+    return _handles[path]
 
 
 def _ptr(a: Optional[np.ndarray]):

@@ -27,12 +27,20 @@
  * double arithmetic, not with bit tricks.
  *
  * Readings taken where the pages are silent are marked READING below.
+ *
+ * Threads. Built plainly, this is single-threaded C. Built with -fopenmp (a second library),
+ * the loops over independent groups and rows run on all threads; every group is still
+ * computed by the same statements, and the tensor amax is a max of per-thread maxima (exact
+ * and order-independent), so both builds give the same bits.
  */
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define KVQO_KEY 0
 #define KVQO_VALUE 1
@@ -40,6 +48,15 @@
 #define KVQO_NVFP4 1
 #define KVQO_NVFP4_ROW 2
 #define KVQO_FP8_ROW 3
+
+/* Threads the loops below run on: 1 for the plain build. */
+int kvq_oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* status codes (mirrors nothing; the oracle has its own) */
 #define KVQO_OK 0
@@ -257,6 +274,7 @@ static float load_bf16(const uint16_t* base, int64_t st, int64_t sh, int64_t t, 
 static void materialize(const uint16_t* cur, int64_t cst, int64_t csh, const uint16_t* prev, int64_t pst,
                         int64_t psh, const int32_t* positions, int64_t rows, int64_t H, int64_t D,
                         float* dense) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
         int64_t t = positions ? (int64_t)positions[i] : i;
         for (int64_t h = 0; h < H; ++h)
@@ -279,6 +297,7 @@ static void materialize(const uint16_t* cur, int64_t cst, int64_t csh, const uin
  * "low first", which is taken for both formats. */
 static void pack_nibbles(const uint8_t* c, int64_t rows, int64_t H, int64_t D, uint8_t* codes) {
     int64_t Dp = ceil_div(D, 2);
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < rows; ++t)
         for (int64_t h = 0; h < H; ++h)
             for (int64_t j = 0; j < Dp; ++j) {
@@ -301,27 +320,25 @@ static uint8_t nibble_at(const uint8_t* codes, int64_t H, int64_t D, int64_t t, 
 typedef void (*group_fn)(void* ctx, int64_t gid, int64_t n, const int64_t* idx);
 
 static void for_each_group(int kind, int32_t G, int64_t rows, int64_t H, int64_t D, group_fn f, void* ctx) {
-    int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)G);
-    if (kind == KVQO_KEY) {
-        int64_t nb = ceil_div(rows, G);
-        for (int64_t b = 0; b < nb; ++b)
-            for (int64_t h = 0; h < H; ++h)
-                for (int64_t d = 0; d < D; ++d) {
-                    int64_t n = 0;
-                    for (int64_t t = b * G; t < rows && t < (b + 1) * G; ++t) idx[n++] = (t * H + h) * D + d;
-                    f(ctx, (b * H + h) * D + d, n, idx);
-                }
-    } else {
-        int64_t nc = ceil_div(D, G);
-        for (int64_t t = 0; t < rows; ++t)
-            for (int64_t h = 0; h < H; ++h)
-                for (int64_t c = 0; c < nc; ++c) {
-                    int64_t n = 0;
-                    for (int64_t d = c * G; d < D && d < (c + 1) * G; ++d) idx[n++] = (t * H + h) * D + d;
-                    f(ctx, (t * H + h) * nc + c, n, idx);
-                }
+    int64_t ngroups = n_groups(kind, G, rows, H, D);
+    int64_t nc = ceil_div(D, G);
+#pragma omp parallel
+    {
+        int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)G);
+#pragma omp for schedule(static)
+        for (int64_t gid = 0; gid < ngroups; ++gid) {
+            int64_t n = 0;
+            if (kind == KVQO_KEY) { /* gid = (b * H + h) * D + d: tokens [bG, min(rows, (b+1)G)) */
+                int64_t b = gid / (H * D), h = (gid / D) % H, d = gid % D;
+                for (int64_t t = b * G; t < rows && t < (b + 1) * G; ++t) idx[n++] = (t * H + h) * D + d;
+            } else { /* gid = (t * H + h) * nc + c: channels [cG, min(D, (c+1)G)) */
+                int64_t t = gid / (H * nc), h = (gid / nc) % H, c = gid % nc;
+                for (int64_t d = c * G; d < D && d < (c + 1) * G; ++d) idx[n++] = (t * H + h) * D + d;
+            }
+            f(ctx, gid, n, idx);
+        }
+        free(idx);
     }
-    free(idx);
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -457,6 +474,7 @@ static void nvfp4_group(void* vctx, int64_t gid, int64_t n, const int64_t* idx) 
 /* Tensor amax over every encoded element ([PR166] "Purpose": one scale per encoded tensor). */
 static float dense_amax(const float* dense, int64_t n) {
     float amax = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : amax)
     for (int64_t i = 0; i < n; ++i) {
         float a = fabsf(dense[i]);
         if (a > amax) amax = a;
@@ -503,6 +521,7 @@ static int nvfp4_row_encode(const float* dense, int64_t rows, int64_t H, int64_t
     int64_t nb = ceil_div(D, 16);
     uint8_t* c = (uint8_t*)calloc((size_t)(rows * H * D) + 1, 1);
     if (!c) return KVQO_NOMEM;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows * H; ++r) {
         float g = kvq_oracle_nvfp4_global(dense_amax(dense + r * D, D));
         grow[r] = g;
@@ -521,6 +540,7 @@ static int nvfp4_row_encode(const float* dense, int64_t rows, int64_t H, int64_t
  * e4m3(min(|q|, 448)) with sign bit signbit(x). A zero scale (an all-zero row, or an amax so
  * small that amax / 448 underflows to 0) gives q = +-0. */
 static int fp8_row_encode(const float* dense, int64_t rows, int64_t H, int64_t D, uint8_t* codes, float* srow) {
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows * H; ++r) {
         const float* x = dense + r * D;
         float s = dense_amax(x, D) / 448.0f;
@@ -613,6 +633,7 @@ int kvq_oracle_unpack(int kind, int format, int32_t G, int64_t rows, int64_t H, 
     int rc = check_common(kind, format, G, rows, H, D);
     if (rc) return rc;
     float g = (format == KVQO_NVFP4) ? *gscale : 0.0f;
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < rows; ++t)
         for (int64_t h = 0; h < H; ++h)
             for (int64_t d = 0; d < D; ++d) {
@@ -660,14 +681,19 @@ int kvq_oracle_decode_residual(int kind, int format, int32_t G, int64_t rows, in
     if (!positions && rows != T) return KVQO_BAD_ARG;
     float g = (format == KVQO_NVFP4) ? *gscale : 0.0f;
     if (positions) {
-        if (out != prev || ost != pst || osh != psh)
+        for (int64_t i = 0; i < rows; ++i)
+            if (positions[i] < 0 || positions[i] >= T) return KVQO_BAD_ARG;
+        if (out != prev || ost != pst || osh != psh) {
+#pragma omp parallel for schedule(static)
             for (int64_t t = 0; t < T; ++t)
                 for (int64_t h = 0; h < H; ++h)
                     for (int64_t d = 0; d < D; ++d) out[t * ost + h * osh + d] = prev[t * pst + h * psh + d];
+        }
     }
+    /* kept rows are distinct (precondition), so the rows below never share an output element */
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
         int64_t t = positions ? (int64_t)positions[i] : i;
-        if (t < 0 || t >= T) return KVQO_BAD_ARG;
         for (int64_t h = 0; h < H; ++h)
             for (int64_t d = 0; d < D; ++d) {
                 float delta = decode_at(kind, format, G, H, D, codes, meta0, meta1, g, i, h, d);
@@ -685,18 +711,22 @@ float kvq_oracle_tensor_amax(const uint16_t* cur, int64_t cst, int64_t csh, cons
                              int64_t psh, int64_t T, int64_t H, int64_t D, const int32_t* positions, int64_t M) {
     int64_t rows = positions ? M : T;
     float amax = 0.0f;
-    float* row = (float*)malloc(sizeof(float) * (size_t)(H * D) + 4);
-    for (int64_t i = 0; i < rows; ++i) {
-        const int32_t* p = positions ? positions + i : NULL;
-        if (p) {
-            materialize(cur, cst, csh, prev, pst, psh, p, 1, H, D, row);
-        } else {
-            materialize(cur + i * cst, cst, csh, prev ? prev + i * pst : NULL, pst, psh, NULL, 1, H, D, row);
+#pragma omp parallel reduction(max : amax)
+    {
+        float* row = (float*)malloc(sizeof(float) * (size_t)(H * D) + 4);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            const int32_t* p = positions ? positions + i : NULL;
+            if (p) {
+                materialize(cur, cst, csh, prev, pst, psh, p, 1, H, D, row);
+            } else {
+                materialize(cur + i * cst, cst, csh, prev ? prev + i * pst : NULL, pst, psh, NULL, 1, H, D, row);
+            }
+            float a = dense_amax(row, H * D);
+            if (a > amax) amax = a;
         }
-        float a = dense_amax(row, H * D);
-        if (a > amax) amax = a;
+        free(row);
     }
-    free(row);
     return amax;
 }
 
