@@ -57,7 +57,8 @@ typedef enum kvq_status {
     KVQ_ERR_DTYPE = 6,     /* tensor dtype other than bf16 */
     KVQ_ERR_MISMATCH = 7,  /* packed descriptor disagrees with the tensors it is used with */
     KVQ_ERR_HIP = 8,       /* a kernel launch failed */
-    KVQ_ERR_WORKSPACE = 9  /* NVFP4 encode without a workspace */
+    KVQ_ERR_WORKSPACE = 9, /* NVFP4 encode without a workspace, or a workspace too small */
+    KVQ_ERR_SCRATCH = 10   /* the call needs more than the library's static scratch holds */
 } kvq_status;
 
 /* Group axis follows the kind ([PR166] "Purpose", third bullet): KEY groups run over token rows
@@ -283,12 +284,28 @@ kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, 
                                 const kvq_packed* k_res, const kvq_packed* v_res, float softmax_scale, float* out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kvq_decode_attention without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, results (bit for bit: the same kernels and
+ * split), layouts and errors as kvq_decode_attention; the per-block partials go to a static
+ * device buffer of 32 MiB (KVQ_ATTN_STATIC_SCRATCH_BYTES) that the library holds on every GPU it
+ * runs on until the process ends. A call whose kvq_attention_workspace_bytes(T, H, Hq, D)
+ * exceeds 32 MiB returns KVQ_ERR_SCRATCH before launching anything (head_dim 64 or 128 with
+ * Hq / H <= 16, and head_dim 256 with Hq / H <= 8, always fit). The buffer needs no
+ * initialization. All calls on one GPU share it: calls that overlap in time on the same GPU
+ * (concurrent streams, or several threads) race and must be serialized by the caller.
+ * Errors: as kvq_decode_attention, plus SCRATCH; HIP also if the buffer's address cannot be
+ * obtained on the current device. */
+kvq_status kvq_decode_attention_noalloc(const void* q, int64_t Hq, const kvq_packed* k, const kvq_packed* v,
+                                        const kvq_packed* k_res, const kvq_packed* v_res, float softmax_scale,
+                                        float* out, hipStream_t stream);
+
 /* Opt-in device-side check of a position map (the codec page's interface review asks that
  * validation never force a host sync). Writes *status (device int32): 0 = valid, bit 0 = some
- * position outside [0, T), bit 1 = some position repeated. `scratch` is a device buffer of
+ * position outside [0, T), bit 1 = some position repeated. `seen` is a device buffer of
  * ceil(T/32) uint32 words, overwritten. Nothing is read back on the host.
  * Errors: NULL, SHAPE, HIP. */
-kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* scratch,
+kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* seen,
                                   int32_t* status, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -37,12 +37,14 @@ FORMAT = {"int4": 0, "nvfp4": 1, "nvfp4_row": 2, "fp8_row": 3}
 KIND_NAME = {v: k for k, v in KIND.items()}
 FORMAT_NAME = {v: k for k, v in FORMAT.items()}
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_SHAPE", 3: "KVQ_ERR_LAYOUT", 4: "KVQ_ERR_FORMAT",
-          5: "KVQ_ERR_GROUP", 6: "KVQ_ERR_DTYPE", 7: "KVQ_ERR_MISMATCH", 8: "KVQ_ERR_HIP", 9: "KVQ_ERR_WORKSPACE"}
+          5: "KVQ_ERR_GROUP", 6: "KVQ_ERR_DTYPE", 7: "KVQ_ERR_MISMATCH", 8: "KVQ_ERR_HIP", 9: "KVQ_ERR_WORKSPACE",
+          10: "KVQ_ERR_SCRATCH"}
 PLANES = ("codes", "meta0", "meta1", "global_scale", "positions")
 EXPORTS = ("kvq_version", "kvq_status_string", "kvq_storage_bytes", "kvq_plane_bytes", "kvq_workspace_bytes",
            "kvq_pack", "kvq_unpack", "kvq_encode_residual", "kvq_decode_residual", "kvq_validate_positions",
            "kvq_pack_paged", "kvq_unpack_paged", "kvq_store_rows", "kvq_load_rows", "kvq_encode_window",
-           "kvq_decode_window", "kvq_attention_workspace_bytes", "kvq_decode_attention")
+           "kvq_decode_window", "kvq_attention_workspace_bytes", "kvq_decode_attention",
+           "kvq_decode_attention_noalloc")
 
 
 class KvqError(RuntimeError):
@@ -121,6 +123,8 @@ def library() -> ctypes.CDLL:
         lib.kvq_attention_workspace_bytes.restype = ctypes.c_size_t
         lib.kvq_decode_attention.argtypes = [P, I64, PP, PP, PP, PP, ctypes.c_float, P, P, ctypes.c_size_t, P]
         lib.kvq_decode_attention.restype = ctypes.c_int
+        lib.kvq_decode_attention_noalloc.argtypes = [P, I64, PP, PP, PP, PP, ctypes.c_float, P, P]
+        lib.kvq_decode_attention_noalloc.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -502,6 +506,28 @@ def decode_attention(q: torch.Tensor, k: Packed, v: Packed, k_res: Optional[Pack
     return out
 
 
+def decode_attention_noalloc(q: torch.Tensor, k: Packed, v: Packed, k_res: Optional[Packed] = None,
+                             v_res: Optional[Packed] = None, scale: Optional[float] = None,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_attention through the entry point that takes no workspace: its partials go to the
+    library's static per-GPU scratch (calls overlapping on one GPU race). Pass ``out`` to make
+    the call allocate nothing at all."""
+    dev = _device_of(q)
+    if q.dtype != torch.bfloat16 or q.dim() != 2 or not q.is_contiguous():
+        raise ValueError("kvq: q must be a contiguous bf16 [Hq, head_dim] tensor")
+    Hq, Dq = q.shape
+    if out is None:
+        out = torch.empty((Hq, Dq), dtype=torch.float32, device=dev)
+    dk, dv = k.descriptor(), v.descriptor()
+    drk = k_res.descriptor() if k_res is not None else None
+    drv = v_res.descriptor() if v_res is not None else None
+    scale = (1.0 / Dq ** 0.5) if scale is None else float(scale)
+    _check("kvq_decode_attention_noalloc", library().kvq_decode_attention_noalloc(
+        _ptr(q), Hq, ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(drk) if drk is not None else None,
+        ctypes.byref(drv) if drv is not None else None, scale, _ptr(out), _stream(dev)))
+    return out
+
+
 def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
     """Device-side check of a position map; returns a device int32 status (0 = valid, bit 0 =
     out of range, bit 1 = repeated) without synchronizing."""
@@ -515,5 +541,5 @@ def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
 
 __all__ = ["pack", "unpack", "encode_residual", "decode_residual", "storage_bytes", "plane_bytes",
            "validate_positions", "pack_paged", "unpack_paged", "store_rows", "load_rows", "alloc_cache",
-           "encode_window", "decode_window", "Windowed", "decode_attention",
+           "encode_window", "decode_window", "Windowed", "decode_attention", "decode_attention_noalloc",
            "Packed", "KvqError", "library", "version", "workspace", "alloc_packed"]

@@ -3,17 +3,43 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq.h"
 #include "kvq_launch.hpp"
 
 using namespace kvq;
 
+// Scratch memory of kvq_decode_attention_noalloc: the per-block partials (unnormalized outputs,
+// maxima and sums) that kvq_decode_attention keeps in a caller workspace live here instead.
+// Every GPU the library runs on holds its own copy until the process ends. In host code this
+// name is only a stand-in for the symbol: the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[KVQ_ATTN_STATIC_SCRATCH_BYTES / sizeof(float)];
+
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxElems = (int64_t)1 << 36;
 constexpr size_t kWorkspaceBytes = KVQ_AMAX_MAX_BLOCKS * sizeof(uint32_t);
+
+// Device address of `scratch` on each device, looked up once per device (with that device
+// current) on the first kvq_decode_attention_noalloc call there.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+kvq_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -469,6 +495,7 @@ const char* kvq_status_string(kvq_status s) {
         case KVQ_ERR_MISMATCH: return "descriptor does not match tensor";
         case KVQ_ERR_HIP: return "HIP launch failed";
         case KVQ_ERR_WORKSPACE: return "missing workspace";
+        case KVQ_ERR_SCRATCH: return "needs more scratch than the static buffer holds";
     }
     return "unknown status";
 }
@@ -721,11 +748,25 @@ kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, 
     return hip_status(launch_attention(k->format, rfmt, a, stream));
 }
 
-kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* scratch, int32_t* status,
+kvq_status kvq_decode_attention_noalloc(const void* q, int64_t Hq, const kvq_packed* k, const kvq_packed* v,
+                                        const kvq_packed* k_res, const kvq_packed* v_res, float softmax_scale,
+                                        float* out, hipStream_t stream) {
+    if (!q || !out || !k || !v) return KVQ_ERR_NULL;
+    // sizes the regular entry point rejects give 0 here and are rejected there, before any launch
+    if (kvq_attention_workspace_bytes(k->rows, k->H, Hq, k->D) > KVQ_ATTN_STATIC_SCRATCH_BYTES)
+        return KVQ_ERR_SCRATCH;
+    void* ws = nullptr;
+    kvq_status st = scratch_address(&ws);
+    if (st) return st;
+    return kvq_decode_attention(q, Hq, k, v, k_res, v_res, softmax_scale, out, ws, KVQ_ATTN_STATIC_SCRATCH_BYTES,
+                                stream);
+}
+
+kvq_status kvq_validate_positions(const int32_t* positions, int64_t M, int64_t T, uint32_t* seen, int32_t* status,
                                   hipStream_t stream) {
     if (M < 0 || T < 0 || T >= kMaxDim || M >= kMaxDim) return KVQ_ERR_SHAPE;
-    if (!status || (M > 0 && !positions) || (T > 0 && !scratch)) return KVQ_ERR_NULL;
-    return hip_status(launch_validate_positions(positions, M, T, scratch, status, stream));
+    if (!status || (M > 0 && !positions) || (T > 0 && !seen)) return KVQ_ERR_NULL;
+    return hip_status(launch_validate_positions(positions, M, T, seen, status, stream));
 }
 
 }  // extern "C"

@@ -128,6 +128,7 @@ struct CopyArgs {
 // Decode attention over packed K/V (head_dim 64, 128 or 256; KVQ_ATTN_NO_RESIDUAL: no residual).
 #define KVQ_ATTN_NO_RESIDUAL (-1)
 #define KVQ_ATTN_MAX_SPLIT 2048  // token blocks per KV head at most
+#define KVQ_ATTN_STATIC_SCRATCH_BYTES (32u << 20)  // kvq_decode_attention_noalloc's scratch
 struct AttnPlanes {
     const uint8_t* codes;
     const void* meta0;

@@ -23,13 +23,13 @@ HEADER = os.path.join(ROOT, "include", "kvq.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_exported():
     lib = kvq.library()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert sorted(kvq.EXPORTS) == names
@@ -38,7 +38,7 @@ def test_header_symbols_exported():
 def test_version_and_status_strings():
     assert "gfx950" in kvq.version()
     lib = kvq.library()
-    for code in range(10):
+    for code in range(11):
         assert lib.kvq_status_string(code)
     assert lib.kvq_workspace_bytes() >= 8
 
@@ -274,3 +274,21 @@ def test_binding_has_no_cpu_path():
     x = torch.zeros((4, 1, 8), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="ROCm device"):
         kvq.pack(x, "key", "int4")
+
+
+def test_noalloc_attention_rejects_oversized_scratch_before_launch():
+    """kvq_decode_attention_noalloc refuses a call whose partials exceed its static 32 MiB
+    scratch (here 2^20 tokens, 128 query heads on one KV head, head_dim 256: 2048 splits x 128
+    rows x 258 floats) with KVQ_ERR_SCRATCH, before touching the device; NULL arguments first."""
+    lib = kvq.library()
+    T, H, Hq, Dh = 1 << 20, 1, 128, 256
+    assert lib.kvq_attention_workspace_bytes(T, H, Hq, Dh) > 32 << 20
+    k = _packed(format=0, kind=0, group_size=64, dtype=0, rows=T, H=H, D=Dh, full_T=T)
+    v = _packed(format=0, kind=1, group_size=64, dtype=0, rows=T, H=H, D=Dh, full_T=T)
+    q, out = ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000)
+    assert lib.kvq_decode_attention_noalloc(q, Hq, ctypes.byref(k), ctypes.byref(v), None, None, 0.1, out,
+                                            None) == 10
+    assert lib.kvq_decode_attention_noalloc(None, Hq, ctypes.byref(k), ctypes.byref(v), None, None, 0.1, out,
+                                            None) == 1
+    assert lib.kvq_status_string(10) == b"needs more scratch than the static buffer holds"
+
