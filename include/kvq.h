@@ -253,6 +253,21 @@ kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int6
 kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
                              const kvq_tensor* prev, const kvq_tensor* out, hipStream_t stream);
 
+/* The NVFP4 global encoding multiplier alone ([PR166] "Purpose", second bullet: one FP32
+ * multiplier per encoded tensor, recomputed on every encoding call): g = fl(2688 / amax), with
+ * amax = max |x| over exactly the rows an NVFP4 kvq_pack (prev == NULL) or kvq_encode_residual
+ * of the same arguments would encode -- the plain tensor, the residual rows bf16(cur - prev), or
+ * the M rows gathered by `positions` -- and g = 1 when amax is 0 or there are no rows, FLT_MAX
+ * if the quotient overflows. Writes the same bits that encode stores in its global_scale plane.
+ * Useful on its own to combine the multipliers of several shards (a max over their amaxes).
+ *   cur, prev     as in kvq_encode_residual (prev may be NULL: plain tensor)
+ *   positions, M  as in kvq_encode_residual (NULL and 0 for dense)
+ *   global_scale  device float, written
+ *   workspace     kvq_workspace_bytes() of device memory (per-block partial maxima)
+ * Errors: NULL, SHAPE, LAYOUT, DTYPE, WORKSPACE, HIP. */
+kvq_status kvq_nvfp4_global_scale(const kvq_tensor* cur, const kvq_tensor* prev, const int32_t* positions, int64_t M,
+                                  float* global_scale, void* workspace, hipStream_t stream);
+
 /* Bytes of device workspace kvq_decode_attention needs for T cached tokens, H KV heads, Hq
  * query heads and head_dim D (per-block partial maxima, sums and unnormalized outputs); 0 for
  * invalid sizes. No initialization is needed. Calls that may run concurrently need distinct

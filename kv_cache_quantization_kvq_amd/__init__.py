@@ -44,7 +44,7 @@ EXPORTS = ("kvq_version", "kvq_status_string", "kvq_storage_bytes", "kvq_plane_b
            "kvq_pack", "kvq_unpack", "kvq_encode_residual", "kvq_decode_residual", "kvq_validate_positions",
            "kvq_pack_paged", "kvq_unpack_paged", "kvq_store_rows", "kvq_load_rows", "kvq_encode_window",
            "kvq_decode_window", "kvq_attention_workspace_bytes", "kvq_decode_attention",
-           "kvq_decode_attention_noalloc")
+           "kvq_decode_attention_noalloc", "kvq_nvfp4_global_scale")
 
 
 class KvqError(RuntimeError):
@@ -125,6 +125,8 @@ def library() -> ctypes.CDLL:
         lib.kvq_decode_attention.restype = ctypes.c_int
         lib.kvq_decode_attention_noalloc.argtypes = [P, I64, PP, PP, PP, PP, ctypes.c_float, P, P]
         lib.kvq_decode_attention_noalloc.restype = ctypes.c_int
+        lib.kvq_nvfp4_global_scale.argtypes = [TP, TP, P, I64, P, P, P]
+        lib.kvq_nvfp4_global_scale.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -320,6 +322,27 @@ def encode_residual(current: torch.Tensor, previous: torch.Tensor, kind: str = "
            library().kvq_encode_residual(ctypes.byref(_view(current)), ctypes.byref(_view(previous)), pos_ptr, M,
                                          KIND[kind], FORMAT[format], G, ctypes.byref(desc), _ptr(ws), _stream(dev)))
     out.full_T = T
+    return out
+
+
+def nvfp4_global_scale(current: torch.Tensor, previous: Optional[torch.Tensor] = None,
+                       positions: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The NVFP4 multiplier fl(2688 / amax) that an NVFP4 pack (previous None) or residual
+    encode of the same arguments stores, as a device float32 [1] tensor."""
+    dev = _device_of(current)
+    M = 0
+    pos_ptr = None
+    if positions is not None:
+        if positions.dtype != torch.int32 or positions.device != current.device or positions.dim() != 1:
+            raise ValueError("kvq: positions must be a 1-D int32 tensor on the tensors' device")
+        positions = positions.contiguous()
+        M = positions.numel()
+        pos_ptr = _ptr(positions if M > 0 else _empty_map(dev))
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=dev)
+    prev = ctypes.byref(_view(previous)) if previous is not None else None
+    _check("kvq_nvfp4_global_scale", library().kvq_nvfp4_global_scale(
+        ctypes.byref(_view(current)), prev, pos_ptr, M, _ptr(out), _ptr(workspace(dev)), _stream(dev)))
     return out
 
 
@@ -542,4 +565,5 @@ def validate_positions(positions: torch.Tensor, T: int) -> torch.Tensor:
 __all__ = ["pack", "unpack", "encode_residual", "decode_residual", "storage_bytes", "plane_bytes",
            "validate_positions", "pack_paged", "unpack_paged", "store_rows", "load_rows", "alloc_cache",
            "encode_window", "decode_window", "Windowed", "decode_attention", "decode_attention_noalloc",
+           "nvfp4_global_scale",
            "Packed", "KvqError", "library", "version", "workspace", "alloc_packed"]

@@ -203,10 +203,12 @@ void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, i
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
 // Fill the encoder arguments for `rows` encoded rows of `cur` (optionally minus prev, gathered
-// by positions, written to packed rows dst[r]) into the planes of `planes`, and launch.
+// by positions, written to packed rows dst[r]) into the planes of `planes`, and launch. With
+// amax_only, only the NVFP4 tensor-amax pass runs, storing the multiplier in
+// planes->global_scale.
 kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* positions, int64_t rows, int kind,
                       int format, int32_t G, const kvq_packed* planes, void* workspace, const int32_t* dst,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool amax_only = false) {
     const int64_t H = cur.H, D = cur.D;
     const bool sparse = positions != nullptr;
     EncArgs a;
@@ -261,6 +263,7 @@ kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* po
         a.div_C8 = fastdiv_make((uint32_t)a.C8);
     }
 
+    if (amax_only) return hip_status(launch_amax(a, prev != nullptr, sparse, vec, stream));
     hipError_t e = hipSuccess;
     if (row_format(format)) return hip_status(launch_row_encode(format, a, prev != nullptr, sparse, vec, stream));
     if (format == KVQ_NVFP4) e = launch_amax(a, prev != nullptr, sparse, vec, stream);
@@ -746,6 +749,27 @@ kvq_status kvq_decode_attention(const void* q, int64_t Hq, const kvq_packed* k, 
     a.part_o = static_cast<float*>(workspace);      // the launcher places part_ml after its split
     a.out = out;
     return hip_status(launch_attention(k->format, rfmt, a, stream));
+}
+
+kvq_status kvq_nvfp4_global_scale(const kvq_tensor* cur, const kvq_tensor* prev, const int32_t* positions, int64_t M,
+                                  float* global_scale, void* workspace, hipStream_t stream) {
+    kvq_status st = check_tensor(cur);
+    if (st) return st;
+    const View v = view_of(cur);
+    if (prev) {
+        if ((st = check_tensor(prev))) return st;
+        if (prev->T != v.T || prev->H != v.H || prev->D != v.D) return KVQ_ERR_SHAPE;
+    }
+    const bool sparse = positions != nullptr;
+    if (M < 0 || (sparse && M > v.T) || (!sparse && M != 0)) return KVQ_ERR_SHAPE;
+    if (!global_scale) return KVQ_ERR_NULL;
+    if (!workspace) return KVQ_ERR_WORKSPACE;
+    const int64_t rows = sparse ? M : v.T;
+    if (rows * v.H * v.D == 0) return hip_status(launch_set_global(global_scale, 0x3F800000u, stream));  // g = 1
+    kvq_packed planes;
+    memset(&planes, 0, sizeof planes);
+    planes.global_scale = global_scale;
+    return encode_run(v, prev, positions, rows, KVQ_VALUE, KVQ_NVFP4, 16, &planes, workspace, nullptr, stream, true);
 }
 
 kvq_status kvq_decode_attention_noalloc(const void* q, int64_t Hq, const kvq_packed* k, const kvq_packed* v,

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = kvq.library()
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert sorted(kvq.EXPORTS) == names
@@ -292,3 +292,16 @@ def test_noalloc_attention_rejects_oversized_scratch_before_launch():
                                             None) == 1
     assert lib.kvq_status_string(10) == b"needs more scratch than the static buffer holds"
 
+
+def test_global_scale_argument_errors_return_before_launch():
+    lib = kvq.library()
+    x = _tensor(16, 2, 16)
+    y = _tensor(15, 2, 16)
+    g, ws = ctypes.c_void_p(0x5000), ctypes.c_void_p(0x6000)
+    assert lib.kvq_nvfp4_global_scale(None, None, None, 0, g, ws, None) == 1
+    assert lib.kvq_nvfp4_global_scale(ctypes.byref(x), ctypes.byref(y), None, 0, g, ws, None) == 2
+    assert lib.kvq_nvfp4_global_scale(ctypes.byref(x), None, None, 3, g, ws, None) == 2  # dense with M
+    assert lib.kvq_nvfp4_global_scale(ctypes.byref(x), None, ctypes.c_void_p(0x7000), 17, g, ws, None) == 2
+    assert lib.kvq_nvfp4_global_scale(ctypes.byref(x), None, None, 0, None, ws, None) == 1
+    assert lib.kvq_nvfp4_global_scale(ctypes.byref(x), None, None, 0, g, None, None) == 9
+    assert lib.kvq_nvfp4_global_scale(ctypes.byref(_tensor(16, 2, 16, dtype=1)), None, None, 0, g, ws, None) == 6
