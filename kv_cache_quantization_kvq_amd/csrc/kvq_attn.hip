@@ -15,13 +15,15 @@
 // softmax; the waves meet in LDS, the block writes one partial (max, sum, unnormalized output) per
 // query row, and a second kernel folds the partials of all blocks.
 //
-// MFMA v_mfma_f32_16x16x16_bf16 (lane l, q = l / 16, j = 0..3): A[l % 16][4q + j],
-// B[4q + j][l % 16], D[4q + j][l % 16] (checked on the device). Scores are computed transposed,
-// S^T = K Q^T: A = K (lane: token l % 16; the reduction axis is permuted so that lane group q
-// covers channels (D/4) q .. (D/4) q + D/4 - 1, one contiguous load of codes), B = Q^T, D/16
-// steps. The accumulator then holds S[row l % 16][token 4q + j], which is exactly the B operand
-// P^T of O^T = V^T P^T; there A = V^T with D/16 output tiles N (lane: channels (D/16)(l % 16) + N
-// of tokens 4q + j, one contiguous load per token), and the accumulator of tile N holds
+// MFMA (lane l, q = l / 16): v_mfma_f32_16x16x16_bf16 takes A[l % 16][4q + j], B[4q + j][l % 16]
+// for j = 0..3 and v_mfma_f32_16x16x32_bf16 A[l % 16][8q + j], B[8q + j][l % 16] for j = 0..7;
+// both leave D[4q + j][l % 16], j = 0..3 (checked on the device). Scores are computed transposed,
+// S^T = K Q^T, with the 16x16x32 form: A = K (lane: token l % 16; the reduction axis is permuted so
+// that lane group q covers channels (D/4) q .. (D/4) q + D/4 - 1, one contiguous load of codes),
+// B = Q^T, D/32 steps. The accumulator then holds S[row l % 16][token 4q + j], which is exactly
+// the B operand P^T of O^T = V^T P^T in the 16x16x16 form (16 tokens per sub-tile); there
+// A = V^T with D/16 output tiles N (lane: channels (D/16)(l % 16) + N of tokens 4q + j, one
+// contiguous load per token), and the accumulator of tile N holds
 // O[row l % 16][channel (D/16)(4q + j) + N].
 #include <algorithm>
 #include <atomic>
@@ -41,9 +43,14 @@ typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
 
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of one query row), with the
+// gfx950 lane-swap moves (VALU) instead of two LDS-routed shuffles: swapping a register with
+// itself across halves (rows) leaves each lane's partner value in one of the two results.
 __device__ __forceinline__ float lane_max(float v) {
-    v = __builtin_fmaxf(v, __shfl_xor(v, 16));
-    return __builtin_fmaxf(v, __shfl_xor(v, 32));
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <bool ON>
@@ -417,6 +424,13 @@ __device__ __forceinline__ s4_t as_s4(uint32_t lo, uint32_t hi) {
     return __builtin_bit_cast(s4_t, v);
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8_t as_bf8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    const u32x4 v = {w0, w1, w2, w3};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
 template <int RFMT>
 constexpr int kResFmt = RFMT == kNone ? FMT_INT4 : RFMT;  // a placeholder type when unused
 
@@ -470,8 +484,9 @@ __device__ __forceinline__ void sub_compute(const AttnArgs& a, int n_valid, int 
     constexpr bool RES = RFMT != kNone;
     constexpr int RF = kResFmt<RFMT>;
     constexpr int NT = D / 16;  // output tiles
-    // ---- scores S^T = K Q^T, 8 channels (two MFMA steps) at a time ----
-    f4_t sacc = (f4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    // ---- scores S^T = K Q^T, 8 channels (one 16x16x32 bf16 MFMA step) at a time, in two
+    // accumulators so that consecutive products do not wait for each other ----
+    f4_t sacc = (f4_t){0.0f, 0.0f, 0.0f, 0.0f}, sacc2 = sacc;
     KPrep<D> kpb, kpr;
     k_prep<D, FMT>(s.b, kpb);
     if constexpr (RES) k_prep<D, RF>(s.r, kpr);
@@ -480,15 +495,18 @@ __device__ __forceinline__ void sub_compute(const AttnArgs& a, int n_valid, int 
         float kv[8], kr[8];
         k_decode8<D, FMT>(s.b, kpb, kslot, q, i, kv);
         if constexpr (RES) k_decode8<D, RF>(s.r, kpr, rkslot, q, i, kr);
+        uint32_t kw[4];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int c = 4 * h2, st4 = 2 * i + h2;
-            const uint32_t k01 = rebuild2(kv[c], kv[c + 1], RES ? kr[c] : 0.0f, RES ? kr[c + 1] : 0.0f, RES);
-            const uint32_t k23 = rebuild2(kv[c + 2], kv[c + 3], RES ? kr[c + 2] : 0.0f, RES ? kr[c + 3] : 0.0f, RES);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s4(k01, k23), as_s4(qw[2 * st4], qw[2 * st4 + 1]),
-                                                             sacc, 0, 0, 0);
-        }
+        for (int c = 0; c < 4; ++c)
+            kw[c] = rebuild2(kv[2 * c], kv[2 * c + 1], RES ? kr[2 * c] : 0.0f, RES ? kr[2 * c + 1] : 0.0f, RES);
+        const bf16x8_t ka = as_bf8(kw[0], kw[1], kw[2], kw[3]);
+        const bf16x8_t qb = as_bf8(qw[4 * i], qw[4 * i + 1], qw[4 * i + 2], qw[4 * i + 3]);
+        if (i & 1)
+            sacc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, sacc2, 0, 0, 0);
+        else
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, sacc, 0, 0, 0);
     }
+    sacc += sacc2;
     // ---- online softmax: lane holds S[row r][token t0 + 4q + j] ----
     float sc[4];
 #pragma unroll
@@ -796,6 +814,9 @@ int resident_blocks() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_attn_split<D, FMT, RFMT>, 64 * kWaves, 0) != hipSuccess)
         return 0;
+    // residual kernels at head dim 64 or 128 (three resident per unit by registers) split as if
+    // four were: measured faster with the extra splits (T = 131072, INT4 pair: 125-135 -> 114 us)
+    if (RFMT != kNone && D <= 128 && per < 4) per = 4;
     n = cus * per;
     if (n > 0) cache[dev].store(n, std::memory_order_relaxed);
     return n;
