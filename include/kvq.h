@@ -240,7 +240,8 @@ kvq_status kvq_load_rows(const kvq_packed* cache, const int32_t* slots, const kv
  * *out as a tensor of their own (out->rows = T - n_sink - n_recent, out->full_T = T): packed
  * when prev == NULL, as the residual bf16(cur - prev) otherwise (the window still holds cur,
  * so protected rows reconstruct exactly). The middle encode is the same as kvq_encode_residual
- * with positions = [n_sink, T - n_recent). Workspace rule and errors as kvq_pack /
+ * with positions = [n_sink, T - n_recent). The row copy runs in the encode launch, so `window`
+ * must not overlap cur, prev or the planes. Workspace rule and errors as kvq_pack /
  * kvq_encode_residual; KVQ_ERR_SHAPE for a negative window. */
 kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int64_t sink, int64_t recent,
                              kvq_kind kind, kvq_format format, int32_t group_size, kvq_packed* out, void* window,
@@ -248,8 +249,8 @@ kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int6
 
 /* Decode a windowed tensor into `out` ([T, H, D], T = p->full_T): the middle rows are decoded
  * (prev == NULL) or added to prev in the input dtype (residual), the protected rows are copied
- * bit for bit from `window`. out may be exactly prev. Errors as kvq_unpack /
- * kvq_decode_residual. */
+ * bit for bit from `window` in the same launch (window must not overlap out or prev). out may be
+ * exactly prev. Errors as kvq_unpack / kvq_decode_residual. */
 kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
                              const kvq_tensor* prev, const kvq_tensor* out, hipStream_t stream);
 

@@ -202,13 +202,62 @@ void fill_vec_geometry(Args& a, int64_t rows, int64_t H, int64_t D, int32_t G, i
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
+// A row copy with the path it can take: the 16-byte vector copy (D % 8 == 0, aligned views,
+// rows * H * D / 8 below 2^31) or one element per thread.
+struct RowCopy {
+    CopyArgs c;
+    bool vec;
+};
+
+// Rows of a [rows, H, D] bf16 view copied into another; rows r >= split are read src_jump and
+// written dst_jump elements further on (both multiples of the row pitches).
+RowCopy make_row_copy(const void* src, int64_t sst, int64_t ssh, void* dst, int64_t dst_t, int64_t dsh, int64_t rows,
+                      int64_t H, int64_t D, int64_t split, int64_t src_jump, int64_t dst_jump) {
+    RowCopy r;
+    CopyArgs& c = r.c;
+    memset(&c, 0, sizeof c);
+    c.split = split;
+    c.src_jump = src_jump;
+    c.dst_jump = dst_jump;
+    c.src = static_cast<const uint16_t*>(src);
+    c.sst = sst;
+    c.ssh = ssh;
+    c.dst = static_cast<uint16_t*>(dst);
+    c.dst_t = dst_t;
+    c.dsh = dsh;
+    c.T = rows;
+    c.H = (int32_t)H;
+    c.D = (int32_t)D;
+    r.vec = rows * H * D > 0 && (D % 8 == 0) && view_vec_ok(src, sst, ssh) && view_vec_ok(dst, dst_t, dsh) &&
+            (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
+    if (r.vec) {
+        c.C8 = (int32_t)(H * D / 8);
+        c.div_C8 = fastdiv_make((uint32_t)c.C8);
+        c.div_D8 = fastdiv_make((uint32_t)(D / 8));
+    }
+    return r;
+}
+
+hipError_t launch_row_copy(const RowCopy& r, hipStream_t stream) { return launch_copy_rows(r.c, r.vec, stream); }
+
+// Hands a vector row copy to a vector encode or decode launch, which runs it in blocks appended
+// to its grid (one launch instead of two). False when either side takes another path; the
+// caller then launches the copy on its own.
+template <class Args>
+bool carry_copy(const RowCopy* win, bool vec, Args& a) {
+    if (!win || !win->vec || !vec || win->c.T == 0) return false;
+    a.win = win->c;
+    a.win_tasks = (uint32_t)cdiv(win->c.T * (int64_t)win->c.C8, (int64_t)kWinChunks);
+    return true;
+}
+
 // Fill the encoder arguments for `rows` encoded rows of `cur` (optionally minus prev, gathered
 // by positions, written to packed rows dst[r]) into the planes of `planes`, and launch. With
 // amax_only, only the NVFP4 tensor-amax pass runs, storing the multiplier in
 // planes->global_scale.
 kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* positions, int64_t rows, int kind,
                       int format, int32_t G, const kvq_packed* planes, void* workspace, const int32_t* dst,
-                      hipStream_t stream, bool amax_only = false) {
+                      hipStream_t stream, bool amax_only = false, const RowCopy* win = nullptr) {
     const int64_t H = cur.H, D = cur.D;
     const bool sparse = positions != nullptr;
     EncArgs a;
@@ -264,15 +313,21 @@ kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* po
     }
 
     if (amax_only) return hip_status(launch_amax(a, prev != nullptr, sparse, vec, stream));
+    const bool carry = carry_copy(win, vec, a);
     hipError_t e = hipSuccess;
-    if (row_format(format)) return hip_status(launch_row_encode(format, a, prev != nullptr, sparse, vec, stream));
-    if (format == KVQ_NVFP4) e = launch_amax(a, prev != nullptr, sparse, vec, stream);
-    if (e == hipSuccess) e = launch_encode(format, kind, a, prev != nullptr, sparse, vec, stream);
+    if (row_format(format)) {
+        e = launch_row_encode(format, a, prev != nullptr, sparse, vec, stream);
+    } else {
+        if (format == KVQ_NVFP4) e = launch_amax(a, prev != nullptr, sparse, vec, stream);
+        if (e == hipSuccess) e = launch_encode(format, kind, a, prev != nullptr, sparse, vec, stream);
+    }
+    if (e == hipSuccess && win && !carry) e = launch_row_copy(*win, stream);
     return hip_status(e);
 }
 
 kvq_status encode_common(const View& cur, const kvq_tensor* prev, const int32_t* positions, int64_t M, int kind,
-                         int format, int32_t G, kvq_packed* out, void* workspace, hipStream_t stream) {
+                         int format, int32_t G, kvq_packed* out, void* workspace, hipStream_t stream,
+                         const RowCopy* win = nullptr) {
     kvq_status st = check_kind_format(kind, format);
     if (st) return st;
     G = resolve_group(format, G);
@@ -313,9 +368,10 @@ kvq_status encode_common(const View& cur, const kvq_tensor* prev, const int32_t*
         hipError_t e = hipSuccess;
         if (format == KVQ_NVFP4) e = launch_set_global(out->global_scale, 0x3F800000u, stream);  // g = 1
         if (e == hipSuccess && sparse && M > 0) e = launch_copy_i32(out->positions, positions, M, stream);
+        if (e == hipSuccess && win) e = launch_row_copy(*win, stream);
         return hip_status(e);
     }
-    return encode_run(cur, prev, positions, rows, kind, format, G, out, workspace, nullptr, stream);
+    return encode_run(cur, prev, positions, rows, kind, format, G, out, workspace, nullptr, stream, false, win);
 }
 
 kvq_status check_packed(const kvq_packed* p) {
@@ -337,9 +393,9 @@ kvq_status check_packed(const kvq_packed* p) {
 // Decode `rows` rows of p into `out` (optionally adding prev): output row r reads packed row
 // src ? src[r] : r and lands in row positions ? positions[r] : r.
 kvq_status decode_run(const kvq_packed* p, int64_t rows, const kvq_tensor* prev, const View& out,
-                      const int32_t* positions, const int32_t* src, hipStream_t stream) {
+                      const int32_t* positions, const int32_t* src, hipStream_t stream, const RowCopy* win = nullptr) {
     const int64_t H = p->H, D = p->D;
-    if (rows * H * D == 0) return KVQ_OK;
+    if (rows * H * D == 0) return win ? hip_status(launch_row_copy(*win, stream)) : KVQ_OK;
     DecArgs a;
     memset(&a, 0, sizeof a);
     a.codes = p->codes;
@@ -366,51 +422,27 @@ kvq_status decode_run(const kvq_packed* p, int64_t rows, const kvq_tensor* prev,
     bool vec = (D % 8 == 0) && view_vec_ok(out) && aligned(p->codes, 4) &&
                (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
     if (prev) vec = vec && view_vec_ok(prev->data, prev->stride_t, prev->stride_h);
+    hipError_t e;
+    bool carry;
     if (row_format(p->format)) {
         vec = vec && row_vec_dims(D) && (p->format != KVQ_FP8_ROW || aligned(p->codes, 8));
         if (vec) fill_vec_geometry(a, rows, H, D, 8, KVQ_DECODE_ROWS);
-        return hip_status(launch_row_decode(p->format, a, prev != nullptr, positions != nullptr, vec, stream));
-    }
-    if (p->kind == KVQ_VALUE) {
-        vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8);
+        carry = carry_copy(win, vec, a);
+        e = launch_row_decode(p->format, a, prev != nullptr, positions != nullptr, vec, stream);
     } else {
-        // a KEY task loads its token group's metadata once, so slot reads take the generic path
-        vec = vec && !src && (G % 8 == 0) && (G % KVQ_DECODE_ROWS == 0) &&
-              (p->format == KVQ_INT4 ? (aligned(p->meta0, 16) && aligned(p->meta1, 16)) : aligned(p->meta0, 8));
+        if (p->kind == KVQ_VALUE) {
+            vec = vec && (G % 8 == 0) && (D % G == 0) && is_pow2(G / 8);
+        } else {
+            // a KEY task loads its token group's metadata once, so slot reads take the generic path
+            vec = vec && !src && (G % 8 == 0) && (G % KVQ_DECODE_ROWS == 0) &&
+                  (p->format == KVQ_INT4 ? (aligned(p->meta0, 16) && aligned(p->meta1, 16)) : aligned(p->meta0, 8));
+        }
+        if (vec) fill_vec_geometry(a, rows, H, D, G, KVQ_DECODE_ROWS, p->kind == KVQ_VALUE);
+        carry = carry_copy(win, vec, a);
+        e = launch_decode(p->format, p->kind, a, prev != nullptr, positions != nullptr, vec, stream);
     }
-    if (vec) fill_vec_geometry(a, rows, H, D, G, KVQ_DECODE_ROWS, p->kind == KVQ_VALUE);
-    return hip_status(launch_decode(p->format, p->kind, a, prev != nullptr, positions != nullptr, vec, stream));
-}
-
-// Copy `rows` rows of one strided bf16 view into another (the row-copy kernel).
-// Copies `rows` rows of a [rows, H, D] bf16 view; rows r >= split are read src_jump and
-// written dst_jump elements further on (both multiples of the row pitches).
-kvq_status copy_view_rows(const void* src, int64_t sst, int64_t ssh, void* dst, int64_t dst_t, int64_t dsh,
-                          int64_t rows, int64_t H, int64_t D, hipStream_t stream, int64_t split = 0,
-                          int64_t src_jump = 0, int64_t dst_jump = 0) {
-    if (rows * H * D == 0) return KVQ_OK;
-    CopyArgs c;
-    memset(&c, 0, sizeof c);
-    c.split = split;
-    c.src_jump = src_jump;
-    c.dst_jump = dst_jump;
-    c.src = static_cast<const uint16_t*>(src);
-    c.sst = sst;
-    c.ssh = ssh;
-    c.dst = static_cast<uint16_t*>(dst);
-    c.dst_t = dst_t;
-    c.dsh = dsh;
-    c.T = rows;
-    c.H = (int32_t)H;
-    c.D = (int32_t)D;
-    const bool vec = (D % 8 == 0) && view_vec_ok(src, sst, ssh) && view_vec_ok(dst, dst_t, dsh) &&
-                     (uint64_t)rows * (uint64_t)(H * D / 8) < ((uint64_t)1 << 31);
-    if (vec) {
-        c.C8 = (int32_t)(H * D / 8);
-        c.div_C8 = fastdiv_make((uint32_t)c.C8);
-        c.div_D8 = fastdiv_make((uint32_t)(D / 8));
-    }
-    return hip_status(launch_copy_rows(c, vec, stream));
+    if (e == hipSuccess && win && !carry) e = launch_row_copy(*win, stream);
+    return hip_status(e);
 }
 
 // Rows kept by a BF16 window over T tokens: min(sink, T) in front, then up to `recent` at the end.
@@ -565,30 +597,11 @@ kvq_status kvq_decode_residual(const kvq_packed* r, const kvq_tensor* prev, cons
         view_span(out, &olo, &ohi);
         if (plo < ohi && olo < phi) return KVQ_ERR_LAYOUT;  // partial overlap
     }
-    if (sparse && !same) {
-        CopyArgs c;
-        memset(&c, 0, sizeof c);
-        c.src = static_cast<const uint16_t*>(prev->data);
-        c.sst = prev->stride_t;
-        c.ssh = prev->stride_h;
-        c.dst = static_cast<uint16_t*>(out->data);
-        c.dst_t = out->stride_t;
-        c.dsh = out->stride_h;
-        c.T = prev->T;
-        c.H = (int32_t)prev->H;
-        c.D = (int32_t)prev->D;
-        const bool vec = (prev->D % 8 == 0) && view_vec_ok(prev->data, prev->stride_t, prev->stride_h) &&
-                         view_vec_ok(out->data, out->stride_t, out->stride_h) &&
-                         (uint64_t)prev->T * (uint64_t)(prev->H * prev->D / 8) < ((uint64_t)1 << 31);
-        if (vec) {
-            c.C8 = (int32_t)(prev->H * prev->D / 8);
-            c.div_C8 = fastdiv_make((uint32_t)(c.C8 > 0 ? c.C8 : 1));
-            c.div_D8 = fastdiv_make((uint32_t)(prev->D / 8 > 0 ? prev->D / 8 : 1));
-        }
-        if (prev->T * prev->H * prev->D > 0) {
-            hipError_t e = launch_copy_rows(c, vec, stream);
-            if (e != hipSuccess) return KVQ_ERR_HIP;
-        }
+    if (sparse && !same && prev->T * prev->H * prev->D > 0) {
+        // absent rows inherit prev: copy it whole, then decode the named rows over it
+        const RowCopy c = make_row_copy(prev->data, prev->stride_t, prev->stride_h, out->data, out->stride_t,
+                                        out->stride_h, prev->T, prev->H, prev->D, 0, 0, 0);
+        if (launch_row_copy(c, stream) != hipSuccess) return KVQ_ERR_HIP;
     }
     return decode_run(r, r->rows, prev, view_of(out), r->positions, nullptr, stream);
 }
@@ -667,13 +680,14 @@ kvq_status kvq_encode_window(const kvq_tensor* cur, const kvq_tensor* prev, int6
     const kvq_tensor cm = row_slice(cur, ns, mid);
     kvq_tensor pm;
     if (prev) pm = row_slice(prev, ns, mid);
+    // window rows [0, ns) <- cur rows [0, ns); window rows [ns, ns + nr) <- cur rows [T - nr, T)
+    const RowCopy wc = make_row_copy(cur->data, cur->stride_t, cur->stride_h, window, H * D, D, ns + nr, H, D, ns,
+                                     mid * cur->stride_t, 0);
     if ((st = encode_common(view_of(&cm), prev ? &pm : nullptr, nullptr, 0, kind, format, group_size, out, workspace,
-                            stream)))
+                            stream, (ns + nr) * H * D > 0 ? &wc : nullptr)))
         return st;
     out->full_T = T;
-    // window rows [0, ns) <- cur rows [0, ns); window rows [ns, ns + nr) <- cur rows [T - nr, T)
-    return copy_view_rows(cur->data, cur->stride_t, cur->stride_h, window, H * D, D, ns + nr, H, D, stream, ns,
-                          mid * cur->stride_t, 0);
+    return KVQ_OK;
 }
 
 kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t sink, int64_t recent,
@@ -701,10 +715,11 @@ kvq_status kvq_decode_window(const kvq_packed* p, const void* window, int64_t si
     const kvq_tensor om = row_slice(out, ns, mid);
     kvq_tensor pm;
     if (prev) pm = row_slice(prev, ns, mid);
-    if ((st = decode_run(p, mid, prev ? &pm : nullptr, view_of(&om), nullptr, nullptr, stream))) return st;
     // out rows [0, ns) <- window rows [0, ns); out rows [T - nr, T) <- window rows [ns, ns + nr)
-    return copy_view_rows(window, H * D, D, out->data, out->stride_t, out->stride_h, ns + nr, H, D, stream, ns, 0,
-                          mid * out->stride_t);
+    const RowCopy wc = make_row_copy(window, H * D, D, out->data, out->stride_t, out->stride_h, ns + nr, H, D, ns, 0,
+                                     mid * out->stride_t);
+    return decode_run(p, mid, prev ? &pm : nullptr, view_of(&om), nullptr, nullptr, stream,
+                      (ns + nr) * H * D > 0 ? &wc : nullptr);
 }
 
 size_t kvq_attention_workspace_bytes(int64_t T, int64_t H, int64_t Hq, int64_t D) {

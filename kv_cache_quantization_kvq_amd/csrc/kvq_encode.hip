@@ -201,6 +201,11 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
 template <int FMT, bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
     constexpr int RW = kEncodeRowsV;
+    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+        window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
+                         threadIdx.x & 63);
+        return;
+    }
     __shared__ std::conditional_t<FMT == FMT_NVFP4, Fp4Table, char> tab;
     float g = 0.0f;
     if constexpr (FMT == FMT_NVFP4) {
@@ -281,6 +286,12 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
     constexpr int IPB = WPB / WPG;
     constexpr int NW = (FMT == FMT_INT4) ? 8 : 4;  // exchanged words per lane
     static_assert(WPB <= 16 && WPB % WPG == 0, "KEY encoder block shape");
+    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+        window_copy_wave(a.win,
+                         __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * (uint32_t)WPB + (threadIdx.x >> 6)),
+                         threadIdx.x & 63);
+        return;
+    }
     __shared__ uint32_t lds[WPG > 1 ? WPB * NW * 64 : 1];
     // INT4 with a group split over waves: each item's 8 channels' constants per lane
     constexpr bool SPLIT = FMT == FMT_INT4 && WPG > 1;
@@ -723,24 +734,26 @@ inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 
 template <int FMT, int G, bool DIFF, bool GATHER>
 void launch_key_vec(const EncArgs& a, hipStream_t s) {
     constexpr uint32_t ipb = (uint32_t)(key_waves_per_block(G) / key_waves_per_group(G));
+    EncArgs b = a;
+    const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, ipb), (uint32_t)key_waves_per_block(G));
     if (a.ri_shift > 0)
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true>), dim3(ceil_div_u(a.n_tasks, ipb)),
-                           dim3(64 * key_waves_per_block(G)), 0, s, a);
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true>), grid, dim3(64 * key_waves_per_block(G)), 0, s,
+                           b);
     else
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false>), dim3(ceil_div_u(a.n_tasks, ipb)),
-                           dim3(64 * key_waves_per_block(G)), 0, s, a);
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false>), grid, dim3(64 * key_waves_per_block(G)), 0,
+                           s, b);
 }
 
 template <int FMT, bool DIFF, bool GATHER>
 hipError_t encode_dispatch(int kind, const EncArgs& a, bool vec, hipStream_t s) {
     if (vec) {
         if (kind == KIND_VALUE) {
+            EncArgs b = a;
+            const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, 4), 4u);
             if (a.ri_shift > 0)
-                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, true>), dim3(ceil_div_u(a.n_tasks, 4)),
-                                   dim3(kThreads), 0, s, a);
+                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, true>), grid, dim3(kThreads), 0, s, b);
             else
-                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, false>), dim3(ceil_div_u(a.n_tasks, 4)),
-                                   dim3(kThreads), 0, s, a);
+                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, false>), grid, dim3(kThreads), 0, s, b);
         } else {
             switch (a.G) {
                 case 16:

@@ -45,6 +45,25 @@ constexpr int key_waves_per_group(int G) { return G / key_rows_per_wave(G); }
 constexpr int key_waves_per_block(int G) { return key_waves_per_group(G) > 4 ? key_waves_per_group(G) : 4; }
 enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 
+// Row copy: row r of src to row r of dst, except that rows r >= split are read src_jump
+// elements further on and written dst_jump elements further on (two row ranges in one launch;
+// jumps of 0 for a plain copy).
+struct CopyArgs {
+    const uint16_t* src;
+    int64_t sst, ssh;
+    uint16_t* dst;
+    int64_t dst_t, dsh;
+    int64_t T;
+    int64_t split, src_jump, dst_jump;
+    int32_t H, D, C8;
+    FastDiv div_C8, div_D8;
+};
+
+// A launch of the vector encoder or decoder can carry a row copy (a BF16 window's protected
+// rows): the launcher appends blocks from win_block0 on, and their waves copy kWinChunks
+// 16-byte chunks each (win_tasks such waves; 0: no copy).
+constexpr uint32_t kWinChunks = 256;
+
 // Rows being encoded: row r is source row t = pos ? pos[r] : r; the element value is
 // cur[t, h, d], or bf16(cur[t, h, d] - prev[t, h, d]) for a residual.
 struct EncArgs {
@@ -70,6 +89,8 @@ struct EncArgs {
     void* meta1;
     float* gscale;
     uint32_t* ws;  // NVFP4: per-block partial maxima of the amax pass
+    CopyArgs win;
+    uint32_t win_tasks, win_block0;
 };
 
 // Rows being decoded: output row r reads packed row src ? src[r] : r and goes to output row
@@ -93,6 +114,8 @@ struct DecArgs {
     int32_t ri_shift, c8_shift;  // lane groups of short rows (see task_lane); 0 when unused
     uint32_t n_tasks;
     FastDiv div_D8, div_slabs;
+    CopyArgs win;
+    uint32_t win_tasks, win_block0;
 };
 
 // Lanes of a vector-path task. Rows of 64 or more 8-channel chunks (or a count that does not
@@ -110,20 +133,6 @@ __device__ __forceinline__ void task_lane(const Args& a, uint32_t task, int lane
         c8raw = (task - rtile * (uint32_t)a.n_slabs) * 64u + (uint32_t)lane;
     }
 }
-
-// Row copy: row r of src to row r of dst, except that rows r >= split are read src_jump
-// elements further on and written dst_jump elements further on (two row ranges in one launch;
-// jumps of 0 for a plain copy).
-struct CopyArgs {
-    const uint16_t* src;
-    int64_t sst, ssh;
-    uint16_t* dst;
-    int64_t dst_t, dsh;
-    int64_t T;
-    int64_t split, src_jump, dst_jump;
-    int32_t H, D, C8;
-    FastDiv div_C8, div_D8;
-};
 
 // Decode attention over packed K/V (head_dim 64, 128 or 256; KVQ_ATTN_NO_RESIDUAL: no residual).
 #define KVQ_ATTN_NO_RESIDUAL (-1)
@@ -152,6 +161,39 @@ struct AttnArgs {
     float* part_ml;     // [H, n_split, rep, 2]
     float* out;         // [H * rep, D] fp32
 };
+
+// One wave of a carried row copy: chunks [task * kWinChunks, (task + 1) * kWinChunks) of the
+// copy's rows * C8, all loads before the stores (the host keeps rows * C8 below 2^31).
+__device__ __forceinline__ void window_copy_wave(const CopyArgs& c, uint32_t task, int lane) {
+    constexpr int K = (int)(kWinChunks / 64);
+    const uint32_t total = (uint32_t)c.T * (uint32_t)c.C8;
+    const uint32_t D8 = (uint32_t)c.D / 8u;
+    u32x4 v[K];
+    int64_t dofs[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint32_t u = min(task * kWinChunks + (uint32_t)(k * 64 + lane), total - 1u);
+        const uint32_t r = fdiv(u, c.div_C8);
+        const uint32_t c8 = u - r * (uint32_t)c.C8;
+        const uint32_t h = fdiv(c8, c.div_D8);
+        const uint32_t d = (c8 - h * D8) * 8u;
+        const bool far = (int64_t)r >= c.split;
+        v[k] = *reinterpret_cast<const u32x4*>(c.src + (far ? c.src_jump : 0) + (int64_t)r * c.sst +
+                                                (int64_t)h * c.ssh + d);
+        dofs[k] = (far ? c.dst_jump : 0) + (int64_t)r * c.dst_t + (int64_t)h * c.dsh + d;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        if (task * kWinChunks + (uint32_t)(k * 64 + lane) < total) *reinterpret_cast<u32x4*>(c.dst + dofs[k]) = v[k];
+}
+
+// Grid of a vector launch: `main` blocks of `wpb` waves, then the blocks of the row copy the
+// arguments carry (sets win_block0).
+template <class Args>
+inline dim3 grid_with_copy(Args& b, uint32_t main, uint32_t wpb) {
+    b.win_block0 = main;
+    return dim3(main + (b.win_tasks + wpb - 1u) / wpb);
+}
 
 // ---- launchers (return hipGetLastError() of the launch) ----
 // vec: the 8-channel vector path is legal for these arguments (alignment, strides, G).

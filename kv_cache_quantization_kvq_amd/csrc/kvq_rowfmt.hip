@@ -119,6 +119,11 @@ __device__ __forceinline__ uint2 fp8_chunk(const u32x4& v, const Fp8Row& rs) {
 template <int FMT, bool DIFF, bool GATHER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
     constexpr int RW = KVQ_ENCODE_ROWS_V;
+    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+        window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
+                         threadIdx.x & 63);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const uint32_t task = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
@@ -242,9 +247,14 @@ __device__ __forceinline__ uint32_t row_finish(float y0, float y1, uint32_t prev
 template <int FMT, bool ADD, bool SCATTER, bool LG>
 __global__ __launch_bounds__(kThreads) void k_row_decode_vec(DecArgs a) {
     constexpr int RW = KVQ_DECODE_ROWS;
+    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+        window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
+                         threadIdx.x & 63);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const uint32_t task =
-        __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, gridDim.x) * 4u + (threadIdx.x >> 6));
+        __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, a.win_block0) * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
     uint32_t rtile, c8raw;
     task_lane<LG>(a, task, lane, rtile, c8raw);
@@ -357,12 +367,12 @@ inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 
 
 template <int FMT, bool DIFF, bool GATHER>
 void row_encode_launch(const EncArgs& a, bool vec, hipStream_t s) {
+    EncArgs b = a;
+    const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, 4), 4u);
     if (vec && a.ri_shift > 0)
-        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, true>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
-                           0, s, a);
+        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, true>), grid, dim3(kThreads), 0, s, b);
     else if (vec)
-        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, false>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
-                           0, s, a);
+        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, false>), grid, dim3(kThreads), 0, s, b);
     else
         hipLaunchKernelGGL((k_row_encode_gen<FMT, DIFF, GATHER>), dim3(ceil_div_u((uint64_t)a.rows * a.H, kThreads)),
                            dim3(kThreads), 0, s, a);
@@ -370,12 +380,13 @@ void row_encode_launch(const EncArgs& a, bool vec, hipStream_t s) {
 
 template <int FMT, bool ADD, bool SCATTER>
 void row_decode_launch(const DecArgs& a, bool vec, hipStream_t s) {
-    if (vec && a.ri_shift > 0) {
-        hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, true>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
-                           0, s, a);
-    } else if (vec) {
-        hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, false>), dim3(ceil_div_u(a.n_tasks, 4)), dim3(kThreads),
-                           0, s, a);
+    if (vec) {
+        DecArgs b = a;
+        const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, 4), 4u);
+        if (a.ri_shift > 0)
+            hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, true>), grid, dim3(kThreads), 0, s, b);
+        else
+            hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, false>), grid, dim3(kThreads), 0, s, b);
     } else {
         const uint64_t n = (uint64_t)a.rows * a.H * ((a.D + 1) / 2);
         hipLaunchKernelGGL((k_row_decode_gen<FMT, ADD, SCATTER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0, s,

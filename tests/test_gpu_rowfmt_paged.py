@@ -212,3 +212,42 @@ def test_window_pack_and_residual(fmt, G, kind, T, sink, recent):
     buf = R0d.clone()
     kvq.decode_window(gr, previous=buf, out=buf)
     assert_bits_equal(to_host(buf), oracle.decode_window(orr, prev=R0o), "window residual decode")
+
+
+# The protected-row copy runs inside the encode / decode launch when both take the vector path
+# (blocks appended to the grid, 256 chunks of 8 channels per wave), and as a launch of its own
+# otherwise (INT4 G=5 takes the generic encoder; an all-window tensor has no encode).
+@pytest.mark.parametrize("fmt,G,kind", [("int4", 64, "key"), ("int4", 64, "value"), ("nvfp4", 16, "key"),
+                                        ("nvfp4", 16, "value"), ("nvfp4_row", 16, "key"), ("fp8_row", 0, "value"),
+                                        ("int4", 5, "key")])
+@pytest.mark.parametrize("T,sink,recent", [(2100, 5, 999), (1040, 1, 1)])
+def test_window_copy_in_launch(fmt, G, kind, T, sink, recent):
+    rng = np.random.default_rng(T + sink)
+    H, D = 8, 128
+    x0 = normal_kv(rng, T, H, D)
+    x1 = bf16_bits(oracle.bf16_to_f32(x0).astype(np.float64) + 0.1 * rng.standard_normal((T, H, D)))
+    # current as the middle third of a fused [T, 3, H, D] buffer (token pitch 3HD)
+    fused = torch.zeros((T, 3, H, D), dtype=torch.bfloat16, device=dev())
+    fused[:, 1] = to_dev(x1)
+    x1d = fused[:, 1]
+    x0d = to_dev(x0)
+    gw = kvq.encode_window(x0d, kind, fmt, G, sink, recent)
+    ow = oracle.encode_window(x0, kind, fmt, G, sink, recent)
+    assert_same_packed(gw.packed, ow.packed, "window payload")
+    assert_bits_equal(to_host(gw.window), ow.window, "window rows")
+    R0d = kvq.decode_window(gw)
+    R0o = oracle.decode_window(ow)
+    assert_bits_equal(to_host(R0d), R0o, "window decode")
+    gr = kvq.encode_window(x1d, kind, fmt, G, sink, recent, previous=R0d)
+    orr = oracle.encode_window(x1, kind, fmt, G, sink, recent, prev=R0o)
+    assert_same_packed(gr.packed, orr.packed, "window residual payload")
+    assert_bits_equal(to_host(gr.window), orr.window, "window residual rows")
+    # out of place into a strided view (token pitch 2HD), and in place
+    wide = torch.full((T, 2, H, D), float("nan"), dtype=torch.bfloat16, device=dev())
+    kvq.decode_window(gr, previous=R0d, out=wide[:, 0])
+    want = oracle.decode_window(orr, prev=R0o)
+    assert_bits_equal(to_host(wide[:, 0].contiguous()), want, "window residual decode, strided out")
+    assert torch.isnan(wide[:, 1].float()).all()
+    buf = R0d.clone()
+    kvq.decode_window(gr, previous=buf, out=buf)
+    assert_bits_equal(to_host(buf), want, "window residual decode, in place")
