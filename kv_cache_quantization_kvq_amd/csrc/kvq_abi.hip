@@ -240,12 +240,12 @@ RowCopy make_row_copy(const void* src, int64_t sst, int64_t ssh, void* dst, int6
 
 hipError_t launch_row_copy(const RowCopy& r, hipStream_t stream) { return launch_copy_rows(r.c, r.vec, stream); }
 
-// Hands a vector row copy to a vector encode or decode launch, which runs it in blocks appended
-// to its grid (one launch instead of two). False when either side takes another path; the
-// caller then launches the copy on its own.
+// Hands a vector row copy to a dense vector encode or decode launch, which runs it in blocks
+// appended to its grid (one launch instead of two). False when either side takes another path
+// or the launch gathers or scatters rows; the caller then launches the copy on its own.
 template <class Args>
 bool carry_copy(const RowCopy* win, bool vec, Args& a) {
-    if (!win || !win->vec || !vec || win->c.T == 0) return false;
+    if (!win || !win->vec || !vec || win->c.T == 0 || a.pos) return false;
     a.win = win->c;
     a.win_tasks = (uint32_t)cdiv(win->c.T * (int64_t)win->c.C8, (int64_t)kWinChunks);
     return true;

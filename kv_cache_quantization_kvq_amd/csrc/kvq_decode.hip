@@ -31,10 +31,10 @@ __device__ __forceinline__ uint32_t finish_pair(float y0, float y1, uint32_t pre
     return pack_bf16x2(__fadd_rn(bf16lo(prev_word), bf16lo(yb)), __fadd_rn(bf16hi(prev_word), bf16hi(yb)));
 }
 
-template <int FMT, int KIND, bool ADD, bool SCATTER, bool LG>
+template <int FMT, int KIND, bool ADD, bool SCATTER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     constexpr int RW = KVQ_DECODE_ROWS;
-    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+    if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
         return;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     if constexpr (FMT == FMT_NVFP4) fp4_table_fill(tab, *a.gscale);
     const int lane = threadIdx.x & 63;
     const uint32_t task =
-        __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, a.win_block0) * 4u + (threadIdx.x >> 6));
+        __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, WIN ? a.win_block0 : gridDim.x) * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
     uint32_t rtile, c8raw;
     task_lane<LG>(a, task, lane, rtile, c8raw);  // with LG a lane group past the last row tile stores nothing
@@ -252,10 +252,14 @@ hipError_t decode_launch(const DecArgs& a, bool vec, hipStream_t s) {
     if (vec) {
         DecArgs b = a;
         const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, 4), 4u);
-        if (a.ri_shift > 0)
-            hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, SCATTER, true>), grid, dim3(kThreads), 0, s, b);
-        else
-            hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, SCATTER, false>), grid, dim3(kThreads), 0, s, b);
+        const bool win = !SCATTER && a.win_tasks;  // a window never scatters
+        if (a.ri_shift > 0) {
+            if (win) hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, false, true, true>), grid, dim3(kThreads), 0, s, b);
+            else hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, SCATTER, true, false>), grid, dim3(kThreads), 0, s, b);
+        } else {
+            if (win) hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, false, false, true>), grid, dim3(kThreads), 0, s, b);
+            else hipLaunchKernelGGL((k_decode_vec<FMT, KIND, ADD, SCATTER, false, false>), grid, dim3(kThreads), 0, s, b);
+        }
     } else {
         const uint64_t n = (uint64_t)a.rows * a.H * ((a.D + 1) / 2);
         hipLaunchKernelGGL((k_decode_gen<FMT, KIND, ADD, SCATTER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0,

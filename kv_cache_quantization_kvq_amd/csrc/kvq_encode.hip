@@ -198,10 +198,10 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
 }
 
 // A wave task is RW consecutive rows of one 64-chunk column slab.
-template <int FMT, bool DIFF, bool GATHER, bool LG>
+template <int FMT, bool DIFF, bool GATHER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
     constexpr int RW = kEncodeRowsV;
-    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+    if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
         return;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 
 // An item is one token group (G rows) of one 64-chunk column slab. WPG waves share an item,
 // RPW rows each; a block of WPB waves holds WPB/WPG items.
-template <int FMT, int G, bool DIFF, bool GATHER, bool LG>
+template <int FMT, int G, bool DIFF, bool GATHER, bool LG, bool WIN>
 __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(EncArgs a) {
     constexpr int WPG = key_waves_per_group(G);
     constexpr int RPW = key_rows_per_wave(G);
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
     constexpr int IPB = WPB / WPG;
     constexpr int NW = (FMT == FMT_INT4) ? 8 : 4;  // exchanged words per lane
     static_assert(WPB <= 16 && WPB % WPG == 0, "KEY encoder block shape");
-    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+    if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win,
                          __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * (uint32_t)WPB + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
@@ -730,18 +730,27 @@ __global__ void k_set_global(float* gscale, uint32_t bits) { *gscale = __uint_as
 
 inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
 
-// One block per WPB / WPG token-group items.
-template <int FMT, int G, bool DIFF, bool GATHER>
-void launch_key_vec(const EncArgs& a, hipStream_t s) {
+// One block per WPB / WPG token-group items (and the blocks of a carried row copy).
+template <int FMT, int G, bool DIFF, bool GATHER, bool WIN>
+void launch_key_vec_w(const EncArgs& a, hipStream_t s) {
     constexpr uint32_t ipb = (uint32_t)(key_waves_per_block(G) / key_waves_per_group(G));
     EncArgs b = a;
     const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, ipb), (uint32_t)key_waves_per_block(G));
     if (a.ri_shift > 0)
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true>), grid, dim3(64 * key_waves_per_block(G)), 0, s,
-                           b);
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true, WIN>), grid, dim3(64 * key_waves_per_block(G)),
+                           0, s, b);
     else
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false>), grid, dim3(64 * key_waves_per_block(G)), 0,
-                           s, b);
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false, WIN>), grid, dim3(64 * key_waves_per_block(G)),
+                           0, s, b);
+}
+
+// A row copy rides only on dense launches (a window never gathers).
+template <int FMT, int G, bool DIFF, bool GATHER>
+void launch_key_vec(const EncArgs& a, hipStream_t s) {
+    if constexpr (!GATHER) {
+        if (a.win_tasks) return launch_key_vec_w<FMT, G, DIFF, GATHER, true>(a, s);
+    }
+    launch_key_vec_w<FMT, G, DIFF, GATHER, false>(a, s);
 }
 
 template <int FMT, bool DIFF, bool GATHER>
@@ -750,10 +759,14 @@ hipError_t encode_dispatch(int kind, const EncArgs& a, bool vec, hipStream_t s) 
         if (kind == KIND_VALUE) {
             EncArgs b = a;
             const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, 4), 4u);
-            if (a.ri_shift > 0)
-                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, true>), grid, dim3(kThreads), 0, s, b);
-            else
-                hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, false>), grid, dim3(kThreads), 0, s, b);
+            const bool win = !GATHER && a.win_tasks;
+            if (a.ri_shift > 0) {
+                if (win) hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, false, true, true>), grid, dim3(kThreads), 0, s, b);
+                else hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, true, false>), grid, dim3(kThreads), 0, s, b);
+            } else {
+                if (win) hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, false, false, true>), grid, dim3(kThreads), 0, s, b);
+                else hipLaunchKernelGGL((k_encode_v_vec<FMT, DIFF, GATHER, false, false>), grid, dim3(kThreads), 0, s, b);
+            }
         } else {
             switch (a.G) {
                 case 16:

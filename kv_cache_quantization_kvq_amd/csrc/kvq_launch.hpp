@@ -163,12 +163,15 @@ struct AttnArgs {
 };
 
 // One wave of a carried row copy: chunks [task * kWinChunks, (task + 1) * kWinChunks) of the
-// copy's rows * C8, all loads before the stores (the host keeps rows * C8 below 2^31).
+// copy's rows * C8, all loads before the stores (the host keeps rows * C8 below 2^31). A chunk
+// moves as two 64-bit words (merged into 16-byte accesses): accessed as a vector of 32-bit
+// words, the copy's stores would be taken to alias the codec blocks' wave-uniform int and float
+// loads (row maps, the NVFP4 multiplier), which would then lose their scalar form.
 __device__ __forceinline__ void window_copy_wave(const CopyArgs& c, uint32_t task, int lane) {
     constexpr int K = (int)(kWinChunks / 64);
     const uint32_t total = (uint32_t)c.T * (uint32_t)c.C8;
     const uint32_t D8 = (uint32_t)c.D / 8u;
-    u32x4 v[K];
+    uint64_t v[K][2];
     int64_t dofs[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -178,13 +181,20 @@ __device__ __forceinline__ void window_copy_wave(const CopyArgs& c, uint32_t tas
         const uint32_t h = fdiv(c8, c.div_D8);
         const uint32_t d = (c8 - h * D8) * 8u;
         const bool far = (int64_t)r >= c.split;
-        v[k] = *reinterpret_cast<const u32x4*>(c.src + (far ? c.src_jump : 0) + (int64_t)r * c.sst +
-                                                (int64_t)h * c.ssh + d);
+        const uint64_t* sp = reinterpret_cast<const uint64_t*>(c.src + (far ? c.src_jump : 0) + (int64_t)r * c.sst +
+                                                               (int64_t)h * c.ssh + d);
+        v[k][0] = sp[0];
+        v[k][1] = sp[1];
         dofs[k] = (far ? c.dst_jump : 0) + (int64_t)r * c.dst_t + (int64_t)h * c.dsh + d;
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        if (task * kWinChunks + (uint32_t)(k * 64 + lane) < total) *reinterpret_cast<u32x4*>(c.dst + dofs[k]) = v[k];
+    for (int k = 0; k < K; ++k) {
+        if (task * kWinChunks + (uint32_t)(k * 64 + lane) < total) {
+            uint64_t* dp = reinterpret_cast<uint64_t*>(c.dst + dofs[k]);
+            dp[0] = v[k][0];
+            dp[1] = v[k][1];
+        }
+    }
 }
 
 // Grid of a vector launch: `main` blocks of `wpb` waves, then the blocks of the row copy the

@@ -116,10 +116,10 @@ __device__ __forceinline__ uint2 fp8_chunk(const u32x4& v, const Fp8Row& rs) {
 }
 
 // One wave task: RW rows of a 64-chunk slab (the VALUE encoder's tiling).
-template <int FMT, bool DIFF, bool GATHER, bool LG>
+template <int FMT, bool DIFF, bool GATHER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
     constexpr int RW = KVQ_ENCODE_ROWS_V;
-    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+    if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
         return;
@@ -244,17 +244,17 @@ __device__ __forceinline__ uint32_t row_finish(float y0, float y1, uint32_t prev
     return pack_bf16x2(__fadd_rn(bf16lo(prev_word), bf16lo(yb)), __fadd_rn(bf16hi(prev_word), bf16hi(yb)));
 }
 
-template <int FMT, bool ADD, bool SCATTER, bool LG>
+template <int FMT, bool ADD, bool SCATTER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_row_decode_vec(DecArgs a) {
     constexpr int RW = KVQ_DECODE_ROWS;
-    if (blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
+    if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
         return;
     }
     const int lane = threadIdx.x & 63;
     const uint32_t task =
-        __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, a.win_block0) * 4u + (threadIdx.x >> 6));
+        __builtin_amdgcn_readfirstlane(xcd_block(blockIdx.x, WIN ? a.win_block0 : gridDim.x) * 4u + (threadIdx.x >> 6));
     if (task >= a.n_tasks) return;
     uint32_t rtile, c8raw;
     task_lane<LG>(a, task, lane, rtile, c8raw);
@@ -369,11 +369,14 @@ template <int FMT, bool DIFF, bool GATHER>
 void row_encode_launch(const EncArgs& a, bool vec, hipStream_t s) {
     EncArgs b = a;
     const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, 4), 4u);
-    if (vec && a.ri_shift > 0)
-        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, true>), grid, dim3(kThreads), 0, s, b);
-    else if (vec)
-        hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, false>), grid, dim3(kThreads), 0, s, b);
-    else
+    const bool win = !GATHER && a.win_tasks;  // a window never gathers
+    if (vec && a.ri_shift > 0) {
+        if (win) hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, false, true, true>), grid, dim3(kThreads), 0, s, b);
+        else hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, true, false>), grid, dim3(kThreads), 0, s, b);
+    } else if (vec) {
+        if (win) hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, false, false, true>), grid, dim3(kThreads), 0, s, b);
+        else hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, false, false>), grid, dim3(kThreads), 0, s, b);
+    } else
         hipLaunchKernelGGL((k_row_encode_gen<FMT, DIFF, GATHER>), dim3(ceil_div_u((uint64_t)a.rows * a.H, kThreads)),
                            dim3(kThreads), 0, s, a);
 }
@@ -383,10 +386,14 @@ void row_decode_launch(const DecArgs& a, bool vec, hipStream_t s) {
     if (vec) {
         DecArgs b = a;
         const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, 4), 4u);
-        if (a.ri_shift > 0)
-            hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, true>), grid, dim3(kThreads), 0, s, b);
-        else
-            hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, false>), grid, dim3(kThreads), 0, s, b);
+        const bool win = !SCATTER && a.win_tasks;  // a window never scatters
+        if (a.ri_shift > 0) {
+            if (win) hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, false, true, true>), grid, dim3(kThreads), 0, s, b);
+            else hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, true, false>), grid, dim3(kThreads), 0, s, b);
+        } else {
+            if (win) hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, false, false, true>), grid, dim3(kThreads), 0, s, b);
+            else hipLaunchKernelGGL((k_row_decode_vec<FMT, ADD, SCATTER, false, false>), grid, dim3(kThreads), 0, s, b);
+        }
     } else {
         const uint64_t n = (uint64_t)a.rows * a.H * ((a.D + 1) / 2);
         hipLaunchKernelGGL((k_row_decode_gen<FMT, ADD, SCATTER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0, s,
