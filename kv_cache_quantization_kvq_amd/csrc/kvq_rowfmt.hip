@@ -119,6 +119,7 @@ __device__ __forceinline__ uint2 fp8_chunk(const u32x4& v, const Fp8Row& rs) {
 template <int FMT, bool DIFF, bool GATHER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
     constexpr int RW = KVQ_ENCODE_ROWS_V;
+    static_assert(RW % 2 == 0, "NVFP4-row encode splits a task's rows over a lane pair");
     if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
@@ -145,15 +146,22 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
     constexpr bool UNI = !LG && FMT == FMT_FP8_ROW;
     row_chunks<RW, DIFF, GATHER, UNI>(a, r0, h, d, v);
 
+    // NVFP4-row: a row pair's multipliers g and this lane's block constants, worked out before
+    // the pair's codes. A 16-channel block is a lane pair (l, l ^ 1) whose lanes hold the same row
+    // and block maxima, so the even lane works out the even row and the odd lane the odd row, and
+    // the two swap the results (one lane per block when D = 8).
+    float gq[2];
+    Fp4Block fq[2];
+    const bool odd = (c8raw & 1u) != 0u;
+
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
         const int64_t r = r0 + i;
         const int64_t wr = a.dst ? (int64_t)a.dst[min<int64_t>(r, a.rows - 1)] : r;
         const bool sbase = UNI && a.dst == nullptr;  // packed row r0 + i, the same on every lane
-        const uint32_t am = chunk_amax(v[i]);
-        const uint32_t amax = lanes_umax(am, lpr);
         const size_t hr = (size_t)wr * (uint32_t)a.H + h;  // (packed row, head) index
         if constexpr (FMT == FMT_FP8_ROW) {
+            const uint32_t amax = lanes_umax(chunk_amax(v[i]), lpr);
             const Fp8Row rs = fp8_row(bf16_to_f32(amax));
             const uint2 o = fp8_chunk(v[i], rs);
             if (i < nr) {
@@ -167,10 +175,38 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
                 if (row_leader) reinterpret_cast<float*>(a.meta0)[hr] = rs.s;
             }
         } else {
-            const float g = fp4_global_rn(amax);
-            // a 16-channel block is this lane and its neighbour (one lane when D = 8)
-            const uint32_t bam = (lpr >= 2) ? max(am, dpp<0xB1>(am)) : am;
-            const Fp4Block fb = fp4_block_direct(bam, g, rcp_pair(g));
+            if ((i & 1) == 0) {
+                uint32_t amx[2], bam[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const uint32_t am = chunk_amax(v[i + k]);
+                    amx[k] = lanes_umax(am, lpr);
+                    bam[k] = (lpr >= 2) ? max(am, dpp<0xB1>(am)) : am;
+                }
+                if (lpr >= 2) {
+                    const float gm = fp4_global_rn(odd ? amx[1] : amx[0]);
+                    const Fp4Block bm = fp4_block_direct(odd ? bam[1] : bam[0], gm, rcp_pair(gm));
+                    const float go = __uint_as_float(dpp<0xB1>(__float_as_uint(gm)));
+                    Fp4Block bo;
+                    bo.rcp = __uint_as_float(dpp<0xB1>(__float_as_uint(bm.rcp)));
+                    bo.s_dec = __uint_as_float(dpp<0xB1>(__float_as_uint(bm.s_dec)));
+                    const uint32_t cd = dpp<0xB1>(bm.code | (bm.div ? 0x100u : 0u));
+                    bo.code = cd & 0xFFu;
+                    bo.div = (cd >> 8) != 0u;
+                    gq[0] = odd ? go : gm;
+                    gq[1] = odd ? gm : go;
+                    fq[0] = odd ? bo : bm;
+                    fq[1] = odd ? bm : bo;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        gq[k] = fp4_global_rn(amx[k]);
+                        fq[k] = fp4_block_direct(bam[k], gq[k], rcp_pair(gq[k]));
+                    }
+                }
+            }
+            const float g = gq[i & 1];
+            const Fp4Block fb = fq[i & 1];
             const uint32_t word = fp4_word(v[i], &fb, 0);
             if (i < nr && valid) {
                 if (sbase)
@@ -247,6 +283,7 @@ __device__ __forceinline__ uint32_t row_finish(float y0, float y1, uint32_t prev
 template <int FMT, bool ADD, bool SCATTER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_row_decode_vec(DecArgs a) {
     constexpr int RW = KVQ_DECODE_ROWS;
+    static_assert(RW % 2 == 0, "NVFP4-row decode splits a task's rows over a lane pair");
     if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
@@ -289,15 +326,30 @@ __global__ __launch_bounds__(kThreads) void k_row_decode_vec(DecArgs a) {
         for (int i = 0; i < RW; ++i) pv[i] = ld_stream(a.prev + tt[i] * a.pst + (int64_t)h * a.psh + d);
     }
     float sc[RW];
+    if constexpr (FMT == FMT_FP8_ROW) {
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-        const size_t hr = (size_t)rs[i] * (uint32_t)a.H + h;
-        if constexpr (FMT == FMT_FP8_ROW) {
-            sc[i] = reinterpret_cast<const float*>(a.meta0)[hr];
-        } else {
-            const uint32_t nb = ((uint32_t)a.D + 15u) / 16u;
+        for (int i = 0; i < RW; ++i) sc[i] = reinterpret_cast<const float*>(a.meta0)[(size_t)rs[i] * (uint32_t)a.H + h];
+    } else {
+        const uint32_t nb = ((uint32_t)a.D + 15u) / 16u;
+        const auto s_dec = [&](int i) {
+            const size_t hr = (size_t)rs[i] * (uint32_t)a.H + h;
             const uint32_t code = reinterpret_cast<const uint8_t*>(a.meta0)[hr * nb + (dc >> 1)] & 0x7Fu;
-            sc[i] = fp4_code_scales(code, reinterpret_cast<const float*>(a.meta1)[hr])[0];
+            return fp4_code_scales(code, reinterpret_cast<const float*>(a.meta1)[hr])[0];
+        };
+        if (a.D8 >= 2) {
+            // A 16-channel block is a lane pair (l, l ^ 1): the even lane divides for the even
+            // rows, the odd lane for the odd rows, and the two swap their quotients.
+            const bool odd = (c8raw & 1u) != 0u;
+#pragma unroll
+            for (int j = 0; j < RW / 2; ++j) {
+                const float mine = s_dec(2 * j + (odd ? 1 : 0));
+                const float other = __uint_as_float(dpp<0xB1>(__float_as_uint(mine)));
+                sc[2 * j] = odd ? other : mine;
+                sc[2 * j + 1] = odd ? mine : other;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RW; ++i) sc[i] = s_dec(i);
         }
     }
 #pragma unroll
