@@ -179,7 +179,6 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
         g.mn = __shfl(gj.mn, gbase + i);
         g.scale = __shfl(gj.scale, gbase + i);
         g.y = __shfl(gj.y, gbase + i);
-        g.ylo = __shfl(gj.ylo, gbase + i);
         g.slow = ((slow8 >> i) & 1u) != 0u;
         const uint32_t word = int4_word(v[i], &g, 0, g.slow);
         if (i < nr) {
@@ -379,7 +378,7 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
             }
             const short2_t ms = as_s2(m), xs = as_s2(x);
             const Int4Group gc = int4_group(key_to_f32((c & 1) ? ms.y : ms.x), key_to_f32((c & 1) ? xs.y : xs.x));
-            cst[(il * 8 + c) * 64 + lane] = (f4_t){gc.mn, gc.scale, gc.slow ? -1.0f : gc.y, gc.ylo};
+            cst[(il * 8 + c) * 64 + lane] = (f4_t){gc.mn, gc.scale, gc.slow ? -1.0f : gc.y, 0.0f};
         }
         __syncthreads();
     } else if constexpr (WPG > 1) {
@@ -418,8 +417,8 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(En
         for (int j = 0; j < 4; ++j) {
             const f4_t t0 = cst[(il * 8 + 2 * j) * 64 + lane], t1 = cst[(il * 8 + 2 * j + 1) * 64 + lane];
             Int4Group g0, g1;
-            g0.mn = t0[0]; g0.scale = t0[1]; g0.y = t0[2]; g0.ylo = t0[3]; g0.slow = t0[2] < 0.0f;
-            g1.mn = t1[0]; g1.scale = t1[1]; g1.y = t1[2]; g1.ylo = t1[3]; g1.slow = t1[2] < 0.0f;
+            g0.mn = t0[0]; g0.scale = t0[1]; g0.y = t0[2]; g0.slow = t0[2] < 0.0f;
+            g1.mn = t1[0]; g1.scale = t1[1]; g1.y = t1[2]; g1.slow = t1[2] < 0.0f;
             if (__builtin_expect(g0.slow || g1.slow, 0)) {
 #pragma unroll
                 for (int i = 0; i < RPW; ++i) {
