@@ -276,8 +276,12 @@ __device__ __forceinline__ void tile_load(const AttnPlanes& pk, const AttnPlanes
     }
 }
 
-// NVFP4-row decode scale of one block: fl(e4m3(code) / g), the codec's own division.
-__device__ __forceinline__ float nvfp4_row_sdec(uint32_t code, float g) { return e4m3_decode(code & 0x7Fu) / g; }
+// NVFP4-row decode scale of one block: fl(e4m3(code) / g), by the Markstein quotient that the
+// device probe shows equal to the IEEE division for every g in [2^-100, 2^100] and every code
+// (others divide); gp = rcp_pair(g).
+__device__ __forceinline__ float nvfp4_row_sdec(uint32_t code, const RcpPair& gp) {
+    return quot_rn(e4m3_decode(code & 0x7Fu), gp);
+}
 
 // Per-sub-tile K constants of a row format: NVFP4-row the block decode scales of the lane's
 // channels, FP8-row the row scale.
@@ -288,10 +292,12 @@ struct KPrep {
 
 template <int D, int FMT>
 __device__ __forceinline__ void k_prep(const TileRaw<D, FMT>& x, KPrep<D>& k) {
+    RcpPair gp;
+    if constexpr (FMT == FMT_NVFP4_ROW) gp = rcp_pair(x.kg);  // the lane's token row
 #pragma unroll
     for (int b = 0; b < D / 64; ++b) {
         if constexpr (FMT == FMT_NVFP4_ROW)
-            k.s[b] = nvfp4_row_sdec((x.km >> (8 * b)) & 0xFFu, x.kg);
+            k.s[b] = nvfp4_row_sdec((x.km >> (8 * b)) & 0xFFu, gp);
         else if constexpr (FMT == FMT_FP8_ROW)
             k.s[b] = x.kg;
         else
@@ -379,8 +385,21 @@ __device__ __forceinline__ void v_prep(const TileRaw<D, FMT>& x, const Fp4Table*
             v.s[j] = tab->e[x.vm[j] & 0x7Fu][0];
             v.m[j] = 0.0f;
         } else {
-            v.s[j] = nvfp4_row_sdec(x.vm[j], x.vg[j]);
             v.m[j] = 0.0f;
+            if constexpr (D >= 256) v.s[j] = nvfp4_row_sdec(x.vm[j], rcp_pair(x.vg[j]));
+        }
+    }
+    if constexpr (FMT == FMT_NVFP4_ROW && D < 256) {
+        // a 16-channel block spans the lane pair (l, l ^ 1), which holds the same tokens: the even
+        // lane works out tokens 0 and 2, the odd lane 1 and 3, and the two swap the quotients
+        const bool odd = (__lane_id() & 1) != 0;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const float mine = nvfp4_row_sdec(odd ? x.vm[2 * jj + 1] : x.vm[2 * jj],
+                                              rcp_pair(odd ? x.vg[2 * jj + 1] : x.vg[2 * jj]));
+            const float other = __uint_as_float(dpp<0xB1>(__float_as_uint(mine)));
+            v.s[2 * jj] = odd ? other : mine;
+            v.s[2 * jj + 1] = odd ? mine : other;
         }
     }
 }

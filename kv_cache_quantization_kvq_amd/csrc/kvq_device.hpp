@@ -484,7 +484,8 @@ __device__ __forceinline__ float fp4_global(uint32_t amax_bits) {
 //
 // The encoder's per-row constants: a row's multiplier g = fl(2688 / amax), a block's decode scale
 // s_dec = fl(sf / g) and its reciprocal fl(1 / s_dec), by the Markstein correction of the INT4
-// quotient (decoders keep the plain division, which measured faster there): y = RN(1/b)
+// quotient (the unpack decoders keep the plain division, which measured faster there; decode
+// attention uses this one for s_dec): y = RN(1/b)
 // (rcp_rn), q0 = RN(a y), q = fma(fma(-b, q0, a), y, q0), for divisors b in [2^-100, 2^100];
 // other divisors divide. The inputs are finite positive bf16 amax values (2^15 of them) and the
 // 126 positive E4M3 scales, so the device probe compares all three with the IEEE quotients

@@ -41,6 +41,10 @@
 //   [17] its reciprocal [1] == fl(1 / s_dec) (+inf where that overflows, 0 for code 0)
 //   [18] v_cvt_pk_u8_f32 of every binary32 in [+0, 15.5] (and -0) == its round-to-nearest-even
 //        integer in the selected byte, the other bytes kept
+// and, in a fifth kernel, the NVFP4-row decode scale for any stored row multiplier (decoders
+// read g from memory, so it need not come from a bf16 amax):
+//   [19] kvq::quot_rn(e4m3(c), rcp_pair(g)) == the IEEE e4m3(c) / g for every g significand
+//        (2^23) at six exponents from 2^-100 to 2^99 and every E4M3 code 0 ... 126
 // counting mismatches and recording the smallest mismatching input of each check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,7 +55,7 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kChecks = 19;
+constexpr int kChecks = 20;
 
 __global__ __launch_bounds__(256) void k_probe(unsigned long long* counts, uint32_t* first) {
     unsigned long long c[kChecks] = {};
@@ -268,6 +272,26 @@ __global__ __launch_bounds__(256) void k_probe_nvfp4row(unsigned long long* coun
     }
 }
 
+// NVFP4-row decode scale for arbitrary multipliers: one g significand per thread.
+__global__ __launch_bounds__(256) void k_probe_sdec(unsigned long long* counts, uint32_t* first) {
+    const uint32_t sig = blockIdx.x * blockDim.x + threadIdx.x;
+    if (sig >= (1u << 23)) return;
+    const int kExp[6] = {-100, -99, -40, 0, 63, 99};
+    unsigned long long c = 0;
+    for (int ei = 0; ei < 6; ++ei) {
+        const float g = __builtin_ldexpf(__uint_as_float(0x3F800000u | sig), kExp[ei]);
+        const RcpPair gp = rcp_pair(g);
+        for (uint32_t code = 0; code <= 126u; ++code) {
+            const float sf = e4m3_decode(code);
+            if (__float_as_uint(quot_rn(sf, gp)) != __float_as_uint(sf / g)) ++c;
+        }
+    }
+    if (c) {
+        atomicAdd(&counts[19], c);
+        atomicMin(&first[19], sig);
+    }
+}
+
 }  // namespace
 
 extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_host) {
@@ -284,6 +308,8 @@ extern "C" int kvq_probe_cvt(unsigned long long* counts_host, uint32_t* first_ho
     hipLaunchKernelGGL(k_probe_fp8div, dim3(4096), dim3(256), 0, 0, counts, first);
     if (hipGetLastError() != hipSuccess) return 3;
     hipLaunchKernelGGL(k_probe_nvfp4row, dim3((0x7F7Fu + 255u) / 256u), dim3(256), 0, 0, counts, first);
+    if (hipGetLastError() != hipSuccess) return 3;
+    hipLaunchKernelGGL(k_probe_sdec, dim3((1u << 23) / 256u), dim3(256), 0, 0, counts, first);
     if (hipGetLastError() != hipSuccess) return 3;
     if (hipDeviceSynchronize() != hipSuccess) return 4;
     hipMemcpy(counts_host, counts, kChecks * sizeof(unsigned long long), hipMemcpyDeviceToHost);

@@ -39,7 +39,8 @@ NAMES = ["bf16", "f16", "fp4 encode (all finite)", "fp4 encode (|x| <= 8)", "fp4
          "NVFP4-row g = 2688 / amax without division (every bf16 amax)",
          "NVFP4-row s_dec = e4m3 / g without division (every amax x code)",
          "NVFP4-row 1 / s_dec without division (every amax x code)",
-         "v_cvt_pk_u8_f32 rounds [0, 15.5] to nearest even"]
+         "v_cvt_pk_u8_f32 rounds [0, 15.5] to nearest even",
+         "NVFP4-row s_dec = e4m3 / g without division (every g significand x code)"]
 
 
 def test_conversion_instructions_match_software_rounding():
