@@ -220,10 +220,12 @@ def test_window_pack_and_residual(fmt, G, kind, T, sink, recent):
 @pytest.mark.parametrize("fmt,G,kind", [("int4", 64, "key"), ("int4", 64, "value"), ("nvfp4", 16, "key"),
                                         ("nvfp4", 16, "value"), ("nvfp4_row", 16, "key"), ("fp8_row", 0, "value"),
                                         ("int4", 5, "key")])
-@pytest.mark.parametrize("T,sink,recent", [(2100, 5, 999), (1040, 1, 1)])
-def test_window_copy_in_launch(fmt, G, kind, T, sink, recent):
+@pytest.mark.parametrize("T,sink,recent,H,D", [(2100, 5, 999, 8, 128), (1040, 1, 1, 8, 128), (700, 4, 16, 1, 128),
+                                               (700, 4, 16, 2, 64), (300, 3, 40, 2, 256)])
+def test_window_copy_in_launch(fmt, G, kind, T, sink, recent, H, D):
+    # H = 1, D = 128 and H = 2, D = 64 (16 chunks per row) run the short-row (lane group) kernels
+    # with the copy appended
     rng = np.random.default_rng(T + sink)
-    H, D = 8, 128
     x0 = normal_kv(rng, T, H, D)
     x1 = bf16_bits(oracle.bf16_to_f32(x0).astype(np.float64) + 0.1 * rng.standard_normal((T, H, D)))
     # current as the middle third of a fused [T, 3, H, D] buffer (token pitch 3HD)
