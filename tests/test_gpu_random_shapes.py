@@ -16,7 +16,7 @@ import torch
 
 import kv_cache_quantization_kvq_amd as kvq
 import oracle
-from gpu_util import assert_bits_equal, assert_same_packed, dev, to_dev, to_host
+from gpu_util import assert_bits_equal, assert_same_packed, dev, planes, to_dev, to_host
 from workloads import bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -98,3 +98,66 @@ def test_random_shape_chain(i):
     else:
         got = kvq.decode_residual(gr, R0g)
     assert_bits_equal(to_host(got), want, what + " residual decode")
+
+
+N_POOL_CASES = 24
+
+
+def draw_pool_case(i):
+    rng = np.random.default_rng(5000 + i)
+    fmt, kind, G = [("int4", "key", int(rng.choice([16, 32, 64]))), ("int4", "value", int(rng.choice([8, 16, 64]))),
+                    ("nvfp4", "key", 16), ("nvfp4_row", "value", 16), ("fp8_row", "key", 0)][i % 5]
+    return dict(seed=5000 + i, fmt=fmt, kind=kind, G=G, P=int(rng.integers(1, 20)),
+                S=int(rng.choice([1, 4, 16, 32, 48])), H=int(rng.integers(1, 5)), D=int(rng.choice([8, 24, 64, 128])),
+                pad=int(rng.choice([0, 2])), local=bool(rng.integers(0, 2)), sink=int(rng.integers(0, 6)),
+                recent=int(rng.integers(0, 40)))
+
+
+@pytest.mark.parametrize("i", range(N_POOL_CASES))
+def test_random_pool_window_and_slots(i):
+    c = draw_pool_case(i)
+    rng = np.random.default_rng(c["seed"])
+    fmt, kind, G, P, S, H, D, pad = c["fmt"], c["kind"], c["G"], c["P"], c["S"], c["H"], c["D"], c["pad"]
+    what = f"case {i} {c}"
+    if fmt == "int4" and kind == "value" and D % G:
+        G = 8
+    # paged pack / unpack of a pool of P pages of S slots (padded page stride when pad > 0)
+    T = P * S
+    buf = values(rng, P * (S + pad), H, D).reshape(P, S + pad, H, D)
+    bd = to_dev(buf)
+    local = c["local"]
+    # page-local KEY groups must tile a page: INT4 G | S or S | G, NVFP4 16 | S
+    if local and kind == "key" and ((fmt == "int4" and G % S and S % G) or (fmt == "nvfp4" and S % 16)):
+        with pytest.raises(kvq.KvqError):
+            kvq.pack_paged(bd[:, :S], kind, fmt, G, page_local=True)
+        local = False
+    gp = kvq.pack_paged(bd[:, :S], kind, fmt, G, page_local=local)
+    op = oracle.pack_paged(buf[:, :S], kind, fmt, G, page_local=local)
+    g, o = planes(gp), planes(op)  # page-local KEY groups: the descriptor records min(G, S), the oracle G
+    assert set(g) == set(o), what
+    for k in o:
+        assert_bits_equal(g[k], o[k], f"{what} pack_paged {k}")
+    assert (gp.rows, gp.H, gp.D) == (T, H, D)
+    out = torch.zeros((P, S + pad, H, D), dtype=torch.bfloat16, device=dev())
+    kvq.unpack_paged(gp, out[:, :S])
+    assert_bits_equal(to_host(out)[:, :S], oracle.unpack_paged(op, P, S), what + " unpack_paged")
+    # the same tokens as one tensor with a BF16 window
+    x = np.ascontiguousarray(buf[:, :S]).reshape(T, H, D)
+    gw = kvq.encode_window(to_dev(x), kind, fmt, G, c["sink"], c["recent"])
+    ow = oracle.encode_window(x, kind, fmt, G, c["sink"], c["recent"])
+    assert_same_packed(gw.packed, ow.packed, what + " window payload")
+    assert_bits_equal(to_host(gw.window), ow.window, what + " window rows")
+    assert_bits_equal(to_host(kvq.decode_window(gw)), oracle.decode_window(ow), what + " window decode")
+    # slot writes and reads where every row carries its own metadata
+    if (fmt, kind) in (("int4", "value"), ("nvfp4_row", "value"), ("fp8_row", "key")):
+        cache = kvq.pack(to_dev(x), kind, fmt, G)
+        ocache = oracle.pack(x, kind, fmt, G)
+        N = int(rng.integers(1, T + 1))
+        slots = rng.permutation(T)[:N].astype(np.int32)
+        new = values(rng, N, H, D)
+        kvq.store_rows(cache, to_dev(new), torch.from_numpy(slots).to(dev()))
+        oracle.store_rows(ocache, new, slots)
+        assert_same_packed(cache, ocache, what + " store_rows")
+        rd = rng.integers(0, T, int(rng.integers(1, 2 * T + 1))).astype(np.int32)
+        got = to_host(kvq.load_rows(cache, torch.from_numpy(rd).to(dev())))
+        assert_bits_equal(got, oracle.load_rows(ocache, rd), what + " load_rows")
