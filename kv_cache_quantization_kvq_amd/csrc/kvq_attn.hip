@@ -746,78 +746,76 @@ __global__ __launch_bounds__(64 * kWaves, (kMinWaves<D, RFMT>)) void k_attn_spli
     }
 }
 
-// out[hq][c] = sum_s O_s e^(m_s - M) / sum_s l_s e^(m_s - M) over the blocks' partials. One
-// block per query head: the weights are spread over the 256 threads, then 256 / (D/4) groups of
-// D/4 threads (4 channels each, one row per group) sum every (256 / (D/4))-th partial.
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* s_w) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_xor(v, d);
-        v = is_max ? __builtin_fmaxf(v, o) : v + o;
-    }
-    __syncthreads();  // s_w may still be read by a previous reduction
-    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = s_w[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) v = is_max ? __builtin_fmaxf(v, s_w[w]) : v + s_w[w];
-    return v;
-}
-
+// out[hq][c] = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) over the blocks' partials (M the
+// largest m_s). One wave per (query head, 32 channels): lane 8 g + c holds channels 4 c .. 4 c + 3
+// of the chunk and takes splits g, g + 8, g + 16, ... in batches of kBatch, all of a batch's loads
+// issued before any arithmetic; three butterfly steps then merge the eight split groups.
 typedef float f4v __attribute__((ext_vector_type(4)));
 
+constexpr int kBatch = 16;
+
+struct Fold {
+    float m, l;
+    f4v o;
+};
+
+// (m, l, o) of two disjoint sets of splits -> that of their union (a side with m = -inf is empty)
+__device__ __forceinline__ Fold fold_merge(const Fold& x, const Fold& y) {
+    const float m = __builtin_fmaxf(x.m, y.m);
+    const float fa = (x.m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(x.m - m);
+    const float fb = (y.m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(y.m - m);
+    return {m, x.l * fa + y.l * fb, x.o * fa + y.o * fb};
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-    constexpr int kPer = KVQ_ATTN_MAX_SPLIT / 256;  // partials per thread in the weight pass
-    constexpr int CL = D / 4;                       // threads per output row (4 channels each)
-    constexpr int SL = 256 / CL;                    // rows of threads (splits summed in parallel)
-    __shared__ float s_f[KVQ_ATTN_MAX_SPLIT];
-    __shared__ float s_w[4];
-    __shared__ f4v s_o[SL][CL];
-    const int hq = blockIdx.x;
+__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
+    constexpr int CH = D / 32;  // 32-channel chunks per output row
+    const int hq = blockIdx.x / CH, ch = blockIdx.x - hq * CH;
     const int h = hq / a.rep, row = hq - h * a.rep;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
+    const int c4 = lane & 7, g = lane >> 3;
     const size_t base = (size_t)h * a.n_split * a.rep + row;  // partial index of split 0
     const size_t step = (size_t)a.rep;                       // partial index step per split
     const float* ml = a.part_ml + base * 2;
-
-    float mv[kPer], lv[kPer];
-    float m = -__builtin_inff();
+    const f4v* po = reinterpret_cast<const f4v*>(a.part_o + base * D + 32 * ch) + c4;
+    Fold f = {-__builtin_inff(), 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
+    for (int s0 = g; s0 < a.n_split; s0 += 8 * kBatch) {
+        float mb[kBatch], lb[kBatch];
+        f4v ob[kBatch];
+        // every load is issued (splits past the end re-read the last one, then count as empty), so
+        // that no branch separates them
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int s = tid + 256 * i;
-        mv[i] = -__builtin_inff();
-        lv[i] = 0.0f;
-        if (s < a.n_split) {
-            mv[i] = ml[s * step * 2];
-            lv[i] = ml[s * step * 2 + 1];
+        for (int i = 0; i < kBatch; ++i) {
+            const int s = min(s0 + 8 * i, a.n_split - 1);
+            mb[i] = ml[(size_t)s * step * 2];
+            lb[i] = ml[(size_t)s * step * 2 + 1];
+            ob[i] = po[(size_t)s * step * (D / 4)];
         }
-        m = __builtin_fmaxf(m, mv[i]);
-    }
-    const float M = block_reduce(m, true, s_w);
-    float l = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int s = tid + 256 * i;
-        const float f = (mv[i] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mv[i] - M);
-        if (s < a.n_split) s_f[s] = f;
-        l += lv[i] * f;
-    }
-    const float L = block_reduce(l, false, s_w);  // its barriers also publish s_f
-
-    const int c4 = tid % CL, sl = tid / CL;  // channels 4 c4 .. 4 c4 + 3; splits sl, sl + SL, ...
-    const f4v* po = reinterpret_cast<const f4v*>(a.part_o + base * D) + c4;
-    f4v o = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-    for (int s = sl; s < a.n_split; s += SL) o += s_f[s] * po[s * step * (D / 4)];
-    s_o[sl][c4] = o;
-    __syncthreads();
-    if (sl == 0) {
-        f4v t = s_o[0][c4];
+        for (int i = 0; i < kBatch; ++i)
+            if (s0 + 8 * i >= a.n_split) mb[i] = -__builtin_inff();
+        Fold b = {mb[0], 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-        for (int i = 1; i < SL; ++i) t += s_o[i][c4];
-        reinterpret_cast<f4v*>(a.out + (size_t)hq * D)[c4] = t / L;
+        for (int i = 1; i < kBatch; ++i) b.m = __builtin_fmaxf(b.m, mb[i]);
+        if (b.m != -__builtin_inff()) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const float w = (mb[i] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mb[i] - b.m);
+                b.l += lb[i] * w;
+                b.o += ob[i] * w;
+            }
+        }
+        f = fold_merge(f, b);
     }
+#pragma unroll
+    for (int x = 8; x < 64; x <<= 1) {
+        Fold y;
+        y.m = __shfl_xor(f.m, x);
+        y.l = __shfl_xor(f.l, x);
+        y.o = (f4v){__shfl_xor(f.o.x, x), __shfl_xor(f.o.y, x), __shfl_xor(f.o.z, x), __shfl_xor(f.o.w, x)};
+        f = fold_merge(f, y);
+    }
+    if (g == 0) reinterpret_cast<f4v*>(a.out + (size_t)hq * D + 32 * ch)[c4] = f.o / f.l;
 }
 
 // Resident blocks of a kernel on the current device (compute units x blocks per unit), cached
@@ -846,7 +844,7 @@ int resident_blocks() {
 template <int D, int FMT, int RFMT>
 hipError_t attn_launch(AttnArgs a, hipStream_t s) {
     const int32_t bound = a.n_split;
-    if (bound < 1 || bound > KVQ_ATTN_MAX_SPLIT) return hipErrorInvalidValue;  // combine's weight table
+    if (bound < 1 || bound > KVQ_ATTN_MAX_SPLIT) return hipErrorInvalidValue;  // the bound the workspace was sized for
     const int n_qt = (a.rep + 15) / 16;  // 16-row query tiles per KV head (grid z)
     const int resident = resident_blocks<D, FMT, RFMT>();
     const int64_t want = resident > 0 ? std::max<int64_t>(1, resident / ((int64_t)a.H * n_qt)) : bound;
@@ -858,7 +856,7 @@ hipError_t attn_launch(AttnArgs a, hipStream_t s) {
     hipLaunchKernelGGL((k_attn_split<D, FMT, RFMT>), dim3(a.n_split, a.H, n_qt), dim3(64 * kWaves), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_combine<D>, dim3((unsigned)(a.H * a.rep)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_combine<D>, dim3((unsigned)(a.H * a.rep * (D / 32))), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
