@@ -631,7 +631,8 @@ def main() -> int:
                 "clean_cache_us": round(amax_clean_us, 2),
             },
         },
-        "per_op": {k: {"p50_us": round(v["p50_us"], 2), "pct_peak": round(100 * v["gbs"] / PEAK_HBM_GBS, 1),
+        "per_op": {k: {"mean_us": round(v["mean_us"], 2), "p50_us": round(v["p50_us"], 2),
+                       "p90_us": round(v["p90_us"], 2), "pct_peak": round(100 * v["gbs"] / PEAK_HBM_GBS, 1),
                        "clean_p50_us": round(v["clean_p50_us"], 2),
                        "clean_pct_peak": round(100 * v["clean_gbs"] / PEAK_HBM_GBS, 1)}
                    for k, v in per_op.items()},
