@@ -237,18 +237,35 @@ __device__ __forceinline__ void lane_offsets(const AttnPlanes& pk, const AttnPla
     }
 }
 
+// The sub-tile's K part (codes and row metadata of the lane's token) and V part (codes and
+// metadata of its four tokens) load separately, so that each can be issued as soon as the
+// previous sub-tile has finished with the registers it fills.
 template <int D, int FMT>
-__device__ __forceinline__ void tile_load(const AttnPlanes& pk, const AttnPlanes& pv, int64_t t0, int H,
-                                          const LaneOffsets& o, TileRaw<D, FMT>& x) {
+__device__ __forceinline__ void tile_load_k(const AttnPlanes& pk, int64_t t0, int H, const LaneOffsets& o,
+                                            TileRaw<D, FMT>& x) {
     using G = Geo<D, FMT>;
     const size_t rows = (size_t)t0 * H;  // (token, head) rows before the sub-tile
-    gptr kcb = sbase(pk.codes, rows * G::RB);
+    ld_codes<G::KB>(sbase(pk.codes, rows * G::RB), o.kc, x.kc);
+    if constexpr (FMT == FMT_FP8_ROW) {
+        x.kg = __uint_as_float(ld_at<uint32_t>(sbase(pk.meta0, rows * 4), o.kg));
+    } else if constexpr (FMT == FMT_NVFP4_ROW) {
+        gptr kmb = sbase(pk.meta0, rows * (D / 16));
+        if constexpr (G::KBLK == 1) x.km = ld_at<uint8_t>(kmb, o.km);
+        else if constexpr (G::KBLK == 2) x.km = ld_at<uint16_t>(kmb, o.km);
+        else x.km = ld_at<uint32_t>(kmb, o.km);
+        x.kg = __uint_as_float(ld_at<uint32_t>(sbase(pk.meta1, rows * 4), o.kg));
+    }
+}
+
+template <int D, int FMT>
+__device__ __forceinline__ void tile_load_v(const AttnPlanes& pv, int64_t t0, int H, const LaneOffsets& o,
+                                            TileRaw<D, FMT>& x) {
+    using G = Geo<D, FMT>;
+    const size_t rows = (size_t)t0 * H;
     gptr vcb = sbase(pv.codes, rows * G::RB);
-    ld_codes<G::KB>(kcb, o.kc, x.kc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) ld_codes<G::VB>(vcb, o.vc[j], x.vc[j]);
     if constexpr (FMT == FMT_FP8_ROW) {
-        x.kg = __uint_as_float(ld_at<uint32_t>(sbase(pk.meta0, rows * 4), o.kg));
         gptr vsb = sbase(pv.meta0, rows * 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) x.vm[j] = ld_at<uint32_t>(vsb, o.vm[j]);
@@ -261,11 +278,6 @@ __device__ __forceinline__ void tile_load(const AttnPlanes& pk, const AttnPlanes
             x.vm[j] = (uint32_t)ld_at<uint16_t>(mb, o.vm[j]) | ((uint32_t)ld_at<uint16_t>(sb, o.vm[j]) << 16);
     } else {
         if constexpr (FMT == FMT_NVFP4_ROW) {
-            gptr kmb = sbase(pk.meta0, rows * (D / 16));
-            if constexpr (G::KBLK == 1) x.km = ld_at<uint8_t>(kmb, o.km);
-            else if constexpr (G::KBLK == 2) x.km = ld_at<uint16_t>(kmb, o.km);
-            else x.km = ld_at<uint32_t>(kmb, o.km);
-            x.kg = __uint_as_float(ld_at<uint32_t>(sbase(pk.meta1, rows * 4), o.kg));
             gptr gb = sbase(pv.meta1, rows * 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) x.vg[j] = __uint_as_float(ld_at<uint32_t>(gb, o.vg[j]));
@@ -489,17 +501,26 @@ __device__ __forceinline__ void call_offsets(const AttnArgs& a, int h, int r, in
 }
 
 template <int D, int FMT, int RFMT>
-__device__ __forceinline__ void sub_load(const AttnArgs& a, int64_t t0, const CallOffsets& o,
-                                         SubRaw<D, FMT, RFMT>& s) {
-    tile_load<D, FMT>(a.k, a.v, t0, a.H, o.b, s.b);
-    if constexpr (RFMT != kNone) tile_load<D, RFMT>(a.rk, a.rv, t0, a.H, o.r, s.r);
+__device__ __forceinline__ void sub_load_k(const AttnArgs& a, int64_t t0, const CallOffsets& o,
+                                           SubRaw<D, FMT, RFMT>& s) {
+    tile_load_k<D, FMT>(a.k, t0, a.H, o.b, s.b);
+    if constexpr (RFMT != kNone) tile_load_k<D, RFMT>(a.rk, t0, a.H, o.r, s.r);
 }
 
-template <int D, int FMT, int RFMT, bool TAIL>
+template <int D, int FMT, int RFMT>
+__device__ __forceinline__ void sub_load_v(const AttnArgs& a, int64_t t0, const CallOffsets& o,
+                                           SubRaw<D, FMT, RFMT>& s) {
+    tile_load_v<D, FMT>(a.v, t0, a.H, o.b, s.b);
+    if constexpr (RFMT != kNone) tile_load_v<D, RFMT>(a.rv, t0, a.H, o.r, s.r);
+}
+
+// One sub-tile's scores, online softmax and PV product; `after_k` runs once the K codes have
+// been consumed (the caller issues the next sub-tile's K loads there).
+template <int D, int FMT, int RFMT, bool TAIL, class AfterK>
 __device__ __forceinline__ void sub_compute(const AttnArgs& a, int n_valid, int q, const uint32_t (&qw)[D / 8],
                                             const SubRaw<D, FMT, RFMT>& s, const uint32_t* kslot,
                                             const uint32_t* rkslot, const Fp4Table* ptv, const Fp4Table* ptrv,
-                                            WaveState<D>& st) {
+                                            WaveState<D>& st, AfterK&& after_k) {
     constexpr bool RES = RFMT != kNone;
     constexpr int RF = kResFmt<RFMT>;
     constexpr int NT = D / 16;  // output tiles
@@ -525,6 +546,7 @@ __device__ __forceinline__ void sub_compute(const AttnArgs& a, int n_valid, int 
         else
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, sacc, 0, 0, 0);
     }
+    after_k();
     sacc += sacc2;
     // ---- online softmax: lane holds S[row r][token t0 + 4q + j] ----
     float sc[4];
@@ -588,6 +610,7 @@ __global__ __launch_bounds__(64 * kWaves, (kMinWaves<D, RFMT>)) void k_attn_spli
     static_assert(kSlots<FMT, RFMT> <= 16, "metadata slots fit in the output rows");
     __shared__ uint32_t s_wave[kWaves][16 * D];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+    constexpr bool SKEW = !RES && FMT == FMT_FP8_ROW;  // next sub-tile's loads during this one
     constexpr bool GK = kGroupMeta<FMT>;        // base K metadata via LDS
     constexpr bool GR = RES && kGroupMeta<RF>;  // residual K metadata via LDS
     if constexpr (FMT == FMT_NVFP4) {
@@ -653,18 +676,25 @@ __global__ __launch_bounds__(64 * kWaves, (kMinWaves<D, RFMT>)) void k_attn_spli
     call_offsets<D, FMT, RFMT>(a, h, r, q, 0, kSub, full);
     const int64_t w_full = w_begin + ((w_end - w_begin) & ~(int64_t)(kSub - 1));
 
-    // One full sub-tile at t from `cur`: the next full sub-tile's codes (into `nxt`, with
-    // prefetching) and, where the next sub-tile opens a new K group, that group's metadata are
-    // fetched first; the metadata goes to its LDS slot (the one the current group does not use)
-    // afterwards.
+    // One full sub-tile at t from `cur`. With SKEW (FP8-row without a residual, the format that
+    // moves the most bytes per value decoded) its K and V loads went out during the sub-tile
+    // before it: the next full sub-tile's K loads (into `nxt`) are issued as soon as this one's K
+    // codes are consumed and its V loads after this one's PV product, so each is in flight over
+    // most of a sub-tile while one copy of each part is live. Otherwise the sub-tile loads its
+    // own data first, both tensors' K parts before their V parts. Where the next sub-tile opens a
+    // new K group, that group's metadata is fetched first and goes to its LDS slot (the one the
+    // current group does not use) afterwards.
     auto step = [&](int64_t t, SubRaw<D, FMT, RFMT>& cur, SubRaw<D, FMT, RFMT>& nxt) {
         const int64_t tn = t + kSub;
         const bool more = tn < w_end;
+        const bool pf = SKEW && tn < w_full;
+        if constexpr (!SKEW) {
+            sub_load_k<D, FMT, RFMT>(a, t, full, cur);
+            sub_load_v<D, FMT, RFMT>(a, t, full, cur);
+        }
         const bool nk = GK && more && (tn >> ks) != (t >> ks);
         const bool nr = GR && more && (tn >> rks) != (t >> rks);
         MetaStage mk, mr;
-        if (KVQ_ATTN_PREFETCH && tn < w_full) sub_load<D, FMT, RFMT>(a, tn, full, nxt);
-        if (!KVQ_ATTN_PREFETCH) sub_load<D, FMT, RFMT>(a, t, full, cur);
         if constexpr (GK) {
             if (nk) meta_fetch<D, FMT>(a.k, tn, a.H, h, lane, mk);
         }
@@ -672,7 +702,10 @@ __global__ __launch_bounds__(64 * kWaves, (kMinWaves<D, RFMT>)) void k_attn_spli
             if (nr) meta_fetch<D, RF>(a.rk, tn, a.H, h, lane, mr);
         }
         __builtin_amdgcn_wave_barrier();
-        sub_compute<D, FMT, RFMT, false>(a, kSub, q, qw, cur, kslot(t), rkslot(t), ptv, ptrv, st);
+        sub_compute<D, FMT, RFMT, false>(a, kSub, q, qw, cur, kslot(t), rkslot(t), ptv, ptrv, st, [&] {
+            if (pf) sub_load_k<D, FMT, RFMT>(a, tn, full, nxt);
+        });
+        if (pf) sub_load_v<D, FMT, RFMT>(a, tn, full, nxt);
         if constexpr (GK) {
             if (nk) meta_store<D, FMT>(kslot(tn), mk, lane, ptk);
         }
@@ -695,7 +728,10 @@ __global__ __launch_bounds__(64 * kWaves, (kMinWaves<D, RFMT>)) void k_attn_spli
             meta_store<D, RF>(rkslot(t0), m, lane, ptrk);
         }
     }
-    if (KVQ_ATTN_PREFETCH && t0 < w_full) sub_load<D, FMT, RFMT>(a, t0, full, A);
+    if (SKEW && t0 < w_full) {
+        sub_load_k<D, FMT, RFMT>(a, t0, full, A);
+        sub_load_v<D, FMT, RFMT>(a, t0, full, A);
+    }
     while (t0 < w_full) {  // unrolled twice so that the two raw buffers swap roles for free
         step(t0, A, B);
         t0 += kSub;
@@ -706,9 +742,11 @@ __global__ __launch_bounds__(64 * kWaves, (kMinWaves<D, RFMT>)) void k_attn_spli
     if (t0 < w_end) {  // the partial sub-tile (its group's metadata is already in place)
         CallOffsets tail;
         call_offsets<D, FMT, RFMT>(a, h, r, q, t0, w_end, tail);
-        sub_load<D, FMT, RFMT>(a, t0, tail, A);
+        sub_load_k<D, FMT, RFMT>(a, t0, tail, A);
+        sub_load_v<D, FMT, RFMT>(a, t0, tail, A);
         __builtin_amdgcn_wave_barrier();
-        sub_compute<D, FMT, RFMT, true>(a, (int)(w_end - t0), q, qw, A, kslot(t0), rkslot(t0), ptv, ptrv, st);
+        sub_compute<D, FMT, RFMT, true>(a, (int)(w_end - t0), q, qw, A, kslot(t0), rkslot(t0), ptv, ptrv, st,
+                                        [] {});
     }
 
     // ---- fold the block's 4 waves: lane holds O[row r][channel (D/16)(4q + j) + n] ----

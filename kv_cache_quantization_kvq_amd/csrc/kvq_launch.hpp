@@ -145,10 +145,6 @@ struct AttnPlanes {
     const float* gscale;
     int32_t gshift;  // log2 of the group size (INT4; NVFP4 blocks are 16)
 };
-// Load the next 16-token sub-tile's raw data before decoding the current one (1), or not (0).
-#ifndef KVQ_ATTN_PREFETCH
-#define KVQ_ATTN_PREFETCH 0
-#endif
 struct AttnArgs {
     const uint16_t* q;  // [H * rep, D] bf16
     AttnPlanes k, v, rk, rv;
