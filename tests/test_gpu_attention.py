@@ -67,6 +67,24 @@ def test_many_query_heads_per_kv_head(fmt, gk, gv, T, H, Hq):
     check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"{fmt} T={T} H={H} Hq={Hq}")
 
 
+@pytest.mark.parametrize("fmt,gk,gv", [("int4", 64, 64), ("nvfp4", 16, 16), ("fp8_row", 0, 0)])
+def test_many_token_blocks_per_head(fmt, gk, gv):
+    """One KV head over 20 000 tokens splits into 313 token blocks of 64 (one round of resident
+    blocks is far more), so the combine folds each query row's partials in three batches of 128."""
+    rng = np.random.default_rng(20000)
+    T, H, Hq = 20000, 1, 4
+    k, v = normal_kv(rng, T, H, D), normal_kv(rng, T, H, D)
+    q = bf16_bits(rng.standard_normal((Hq, D)))
+    gk_, gv_, ok, ov = packed_pair(k, v, fmt, gk, gv)
+    out = kvq.decode_attention(to_dev(q), gk_, gv_).cpu().numpy()
+    kr, vr = reconstruct(ok), reconstruct(ov)
+    want = decode_attention(q, kr, vr, 1.0 / np.sqrt(D))
+    check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"{fmt} T={T} H={H}")
+    out0 = kvq.decode_attention(torch.zeros((Hq, D), dtype=torch.bfloat16, device=dev()), gk_, gv_).cpu().numpy()
+    vf = oracle.bf16_to_f32(vr).astype(np.float64)
+    np.testing.assert_allclose(out0, np.repeat(vf.mean(axis=0), Hq, axis=0), rtol=0, atol=2e-6 * np.abs(vf).max())
+
+
 @pytest.mark.parametrize("fmt,gk,gv", FORMS)
 @pytest.mark.parametrize("T", [16, 333, 5000])
 def test_zero_query_is_mean_of_v(fmt, gk, gv, T):
