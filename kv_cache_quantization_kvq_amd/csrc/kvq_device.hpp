@@ -324,8 +324,8 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 //    the theorem alone does not cover it; the device probe does: for every scale significand at
 //    eight exponents from 2^-100 to 2^99, the corrected quotient equals the IEEE d / scale at
 //    and next to every half-integer and float midpoint near it (the only places where an ulp
-//    can move the code), and on random d. (A model of the same sweep in C with the IEEE
-//    operations agrees: no mismatch in 1.4e11 quotients.)
+//    can move the code), and on random d. (The same identity with the host's IEEE operations,
+//    on a sample of those inputs, is a CPU test: tests/test_quotient_identity.py.)
 //  * range: for 2^-100 <= scale <= 2^100 no intermediate underflows for any member whose quotient
 //    reaches 0.25 (smaller quotients give code 0 whatever their last bits), and none overflows.
 // Other scales: 0 gives y = 0 and every code 0; the rest (subnormal or huge) set `slow` and
