@@ -305,7 +305,9 @@ kvq_status encode_run(const View& cur, const kvq_tensor* prev, const int32_t* po
     }
     if (vec) {
         if (row_format(format) || kind == KVQ_VALUE) {
-            fill_vec_geometry(a, rows, H, D, row_format(format) ? 8 : G, KVQ_ENCODE_ROWS_V);
+            fill_vec_geometry(a, rows, H, D, row_format(format) ? 8 : G,
+                              row_format(format) ? KVQ_ROW_ENCODE_ROWS
+                                                 : value_encode_rows(format == KVQ_NVFP4, prev != nullptr));
         } else {
             fill_vec_geometry(a, rows, H, D, G, G, false);  // KEY groups run over tokens
         }

@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 typedef float f4_t __attribute__((ext_vector_type(4)));
-constexpr int kEncodeRowsV = KVQ_ENCODE_ROWS_V;           // rows per VALUE-encode wave task
 constexpr uint32_t kAmaxMaxBlocks = KVQ_AMAX_MAX_BLOCKS;  // partial maxima held in the workspace
 
 // ---- element access ----------------------------------------------------------------------------
@@ -126,20 +125,22 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
 
 // ---- VALUE, vector path ------------------------------------------------------------------------
 
-// INT4 VALUE groups of 64 channels (8 lanes) over 8 rows per task: instead of all-reducing every
-// row's minimum and maximum over the group's 8 lanes (and then computing the same group
-// constants on all 8), the statistics are reduce-scattered so that lane j of the group ends with
-// row j's, computes that row's constants alone, and the constants reach the other lanes by
-// ds_bpermute. Every lane then holds exactly the constants the all-reduce would give it, so the
-// codes and metadata are the same bits. Three butterfly steps pair lanes j <-> 7 - j (DPP
-// row_half_mirror), j <-> j ^ 2 and j <-> j ^ 1; at each step a lane keeps the half of its rows
-// whose index bit matches its own lane bit and sends the other half.
-template <bool DIFF, bool GATHER, bool LG>
-__device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v)[8], int lane, int64_t r0, int nr,
+// INT4 VALUE groups of 64 channels (8 lanes) over RW = 8 or 4 rows per task: instead of
+// all-reducing every row's minimum and maximum over the group's 8 lanes (and then computing the
+// same group constants on all 8), the statistics are reduce-scattered so that lane j of the group
+// ends with row j's (RW = 8; with RW = 4 lanes j and j ^ 1 both end with row j / 2), computes
+// that row's constants alone, and the constants reach the other lanes by ds_bpermute. Every lane
+// then holds exactly the constants the all-reduce would give it, so the codes and metadata are
+// the same bits. Three butterfly steps pair lanes j <-> 7 - j (DPP row_half_mirror), j <-> j ^ 2
+// and j <-> j ^ 1; at each step a lane keeps the half of its rows whose index bit matches its own
+// lane bit and sends the other half (with RW = 4 the last step combines the one row both hold).
+template <int RW, bool DIFF, bool GATHER, bool LG>
+__device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v)[RW], int lane, int64_t r0, int nr,
                                                bool valid, uint32_t c8, uint32_t c8raw) {
-    uint32_t mn8[8], mx8[8];  // unsigned keys
+    static_assert(RW == 8 || RW == 4, "G64 VALUE rows per task");
+    uint32_t mn8[RW], mx8[RW];  // unsigned keys
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RW; ++i) {
         ushort2_t k = as_us2(ukeys2(v[i].x)), mn = k, mx = k;
         k = as_us2(ukeys2(v[i].y)); mn = umin2(mn, k); mx = umax2(mx, k);
         k = as_us2(ukeys2(v[i].z)); mn = umin2(mn, k); mx = umax2(mx, k);
@@ -149,37 +150,46 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
     }
     const uint32_t j = (uint32_t)lane & 7u;
     const bool b2 = (j & 4u) != 0u, b1 = (j & 2u) != 0u, b0 = (j & 1u) != 0u;
-    uint32_t mn4[4], mx4[4];  // rows 4 b2 + k
+    constexpr int H1 = RW / 2, H2 = RW / 4;
+    uint32_t mn4[H1], mx4[H1];  // rows H1 b2 + k
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        mn4[k] = min(b2 ? mn8[k + 4] : mn8[k], dpp<0x141>(b2 ? mn8[k] : mn8[k + 4]));
-        mx4[k] = max(b2 ? mx8[k + 4] : mx8[k], dpp<0x141>(b2 ? mx8[k] : mx8[k + 4]));
+    for (int k = 0; k < H1; ++k) {
+        mn4[k] = min(b2 ? mn8[k + H1] : mn8[k], dpp<0x141>(b2 ? mn8[k] : mn8[k + H1]));
+        mx4[k] = max(b2 ? mx8[k + H1] : mx8[k], dpp<0x141>(b2 ? mx8[k] : mx8[k + H1]));
     }
-    uint32_t mn2[2], mx2[2];  // rows 4 b2 + 2 b1 + k
+    uint32_t mn2[H2], mx2[H2];  // rows H1 b2 + H2 b1 + k
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        mn2[k] = min(b1 ? mn4[k + 2] : mn4[k], dpp<0x4E>(b1 ? mn4[k] : mn4[k + 2]));
-        mx2[k] = max(b1 ? mx4[k + 2] : mx4[k], dpp<0x4E>(b1 ? mx4[k] : mx4[k + 2]));
+    for (int k = 0; k < H2; ++k) {
+        mn2[k] = min(b1 ? mn4[k + H2] : mn4[k], dpp<0x4E>(b1 ? mn4[k] : mn4[k + H2]));
+        mx2[k] = max(b1 ? mx4[k + H2] : mx4[k], dpp<0x4E>(b1 ? mx4[k] : mx4[k + H2]));
     }
-    const uint32_t gmn = min(b0 ? mn2[1] : mn2[0], dpp<0xB1>(b0 ? mn2[0] : mn2[1]));  // row j
-    const uint32_t gmx = max(b0 ? mx2[1] : mx2[0], dpp<0xB1>(b0 ? mx2[0] : mx2[1]));
+    uint32_t gmn, gmx;  // row jr of this lane
+    if constexpr (RW == 8) {
+        gmn = min(b0 ? mn2[1] : mn2[0], dpp<0xB1>(b0 ? mn2[0] : mn2[1]));
+        gmx = max(b0 ? mx2[1] : mx2[0], dpp<0xB1>(b0 ? mx2[0] : mx2[1]));
+    } else {
+        gmn = min(mn2[0], dpp<0xB1>(mn2[0]));
+        gmx = max(mx2[0], dpp<0xB1>(mx2[0]));
+    }
+    constexpr uint32_t LPR = 8 / RW;  // lanes per row after the scatter
+    const uint32_t jr = j / LPR;
     const Int4Group gj = int4_group(ukey_to_f32(gmn), ukey_to_f32(gmx));
-    if ((int)j < nr && valid) {  // row j's metadata (the group's 8 lanes are all valid or all idle)
-        const int64_t r = r0 + j;
+    if ((j % LPR) == 0 && (int)jr < nr && valid) {  // row jr's metadata (a group's 8 lanes are all valid or all idle)
+        const int64_t r = r0 + jr;
         const int64_t wr = a.dst ? (int64_t)a.dst[r] : r;
         const size_t midx = (size_t)wr * (uint32_t)a.ngr + (c8 >> 3);
         reinterpret_cast<uint16_t*>(a.meta0)[midx] = (uint16_t)f32_to_f16(gj.mn);
         reinterpret_cast<uint16_t*>(a.meta1)[midx] = (uint16_t)f32_to_f16(gj.scale);
     }
-    const uint32_t slow8 = (uint32_t)(__ballot(gj.slow) >> (lane & 56)) & 0xFFu;
+    const uint32_t slowb = (uint32_t)(__ballot(gj.slow) >> (lane & 56)) & 0xFFu;
     const int gbase = lane & ~7;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RW; ++i) {
         Int4Group g;
-        g.mn = __shfl(gj.mn, gbase + i);
-        g.scale = __shfl(gj.scale, gbase + i);
-        g.y = __shfl(gj.y, gbase + i);
-        g.slow = ((slow8 >> i) & 1u) != 0u;
+        g.mn = __shfl(gj.mn, gbase + (int)LPR * i);
+        g.scale = __shfl(gj.scale, gbase + (int)LPR * i);
+        g.y = __shfl(gj.y, gbase + (int)LPR * i);
+        g.slow = ((slowb >> (LPR * i)) & 1u) != 0u;
         const uint32_t word = int4_word(v[i], &g, 0, g.slow);
         if (i < nr) {
             const int64_t r = r0 + i;
@@ -199,7 +209,7 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
 // A wave task is RW consecutive rows of one 64-chunk column slab.
 template <int FMT, bool DIFF, bool GATHER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
-    constexpr int RW = kEncodeRowsV;
+    constexpr int RW = value_encode_rows(FMT == FMT_NVFP4, DIFF);
     if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
                          threadIdx.x & 63);
@@ -226,9 +236,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 
     u32x4 v[RW];
     load_rows8<RW, DIFF, GATHER, !LG>(a, r0, h, d, v);
-    if constexpr (FMT == FMT_INT4 && RW == 8) {
+    if constexpr (FMT == FMT_INT4 && (RW == 8 || RW == 4)) {
         if (lpg == 8) {  // G = 64 (wave-uniform)
-            int4_value_g64<DIFF, GATHER, LG>(a, v, lane, r0, nr, valid, c8, c8raw);
+            int4_value_g64<RW, DIFF, GATHER, LG>(a, v, lane, r0, nr, valid, c8, c8raw);
             return;
         }
     }
@@ -278,10 +288,11 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 // An item is one token group (G rows) of one 64-chunk column slab. WPG waves share an item,
 // RPW rows each; a block of WPB waves holds WPB/WPG items.
 template <int FMT, int G, bool DIFF, bool GATHER, bool LG, bool WIN>
-__global__ __launch_bounds__(64 * key_waves_per_block(G)) void k_encode_k_vec(EncArgs a) {
-    constexpr int WPG = key_waves_per_group(G);
-    constexpr int RPW = key_rows_per_wave(G);
-    constexpr int WPB = key_waves_per_block(G);
+__global__ __launch_bounds__(64 * key_waves_per_block(G, FMT == FMT_NVFP4 && DIFF)) void k_encode_k_vec(EncArgs a) {
+    constexpr bool NR = FMT == FMT_NVFP4 && DIFF;
+    constexpr int WPG = key_waves_per_group(G, NR);
+    constexpr int RPW = key_rows_per_wave(G, NR);
+    constexpr int WPB = key_waves_per_block(G, NR);
     constexpr int IPB = WPB / WPG;
     constexpr int NW = (FMT == FMT_INT4) ? 8 : 4;  // exchanged words per lane
     static_assert(WPB <= 16 && WPB % WPG == 0, "KEY encoder block shape");
@@ -732,14 +743,15 @@ inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 
 // One block per WPB / WPG token-group items (and the blocks of a carried row copy).
 template <int FMT, int G, bool DIFF, bool GATHER, bool WIN>
 void launch_key_vec_w(const EncArgs& a, hipStream_t s) {
-    constexpr uint32_t ipb = (uint32_t)(key_waves_per_block(G) / key_waves_per_group(G));
+    constexpr bool NR = FMT == FMT_NVFP4 && DIFF;
+    constexpr uint32_t ipb = (uint32_t)(key_waves_per_block(G, NR) / key_waves_per_group(G, NR));
     EncArgs b = a;
-    const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, ipb), (uint32_t)key_waves_per_block(G));
+    const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, ipb), (uint32_t)key_waves_per_block(G, NR));
     if (a.ri_shift > 0)
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true, WIN>), grid, dim3(64 * key_waves_per_block(G)),
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true, WIN>), grid, dim3(64 * key_waves_per_block(G, NR)),
                            0, s, b);
     else
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false, WIN>), grid, dim3(64 * key_waves_per_block(G)),
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false, WIN>), grid, dim3(64 * key_waves_per_block(G, NR)),
                            0, s, b);
 }
 

@@ -21,28 +21,35 @@ constexpr int32_t kNoPaging = 62;
 // The NVFP4 amax pass writes one partial maximum per block into the workspace.
 #define KVQ_AMAX_MAX_BLOCKS 4096u
 
-// Rows per wave task of the vector VALUE encoder and of the vector decoder (a KEY decode needs
-// G % KVQ_DECODE_ROWS == 0 so that a task's rows share one token group). Shared by the host
-// code that sizes the grids and the kernels. Four decode rows per wave measured 6-7% faster
-// than eight on residual decodes of the bulk shape (more, shorter waves), and the same on
-// plain unpacks; two rows slowed the unpacks.
-#ifndef KVQ_ENCODE_ROWS_V
-#define KVQ_ENCODE_ROWS_V 8
-#endif
+// Rows per wave task of the vector encoders and decoder, shared by the host code that sizes the
+// grids and the kernels. All measured on the bulk shape ([131072, 8, 128]) against eight rows:
+//  * decoder: four rows (a KEY decode needs G % KVQ_DECODE_ROWS == 0 so that a task's rows share
+//    one token group), 6-7% faster on residual decodes and plain unpacks; two rows were slower.
+//  * VALUE encoder: four rows, except eight for a plain NVFP4 pack (four were 2 us slower
+//    there). Residual encodes gained most: INT4 98.5 -> 96 us and NVFP4 198 -> 192 us in step,
+//    3-4 us on a clean cache; the INT4 pack about 1 us on a clean cache.
+//  * row-format encoders (NVFP4-row, FP8-row; an even count for NVFP4-row's lane pairs): four,
+//    packs 2-4 us and residual encodes 4-5 us faster, in step and on a clean cache.
+//  * KEY encoder: min(G, 8) rows per wave (a power of two), but at least G / 16 so that the
+//    G / rows waves sharing a token group fit one block of at most 1024 threads; an NVFP4
+//    residual encode takes min(G, 4) (199 -> 195.5 us in step). INT4 G64 keeps eight: its eight
+//    waves per group each own one of a lane's eight channels.
 #ifndef KVQ_DECODE_ROWS
 #define KVQ_DECODE_ROWS 4
 #endif
-// Rows per wave of the vector KEY encoder (a power of two): min(G, KVQ_KEY_ROWS), but at least
-// G / 16 so that the G / rows waves sharing a token group fit one block of at most 1024 threads.
-#ifndef KVQ_KEY_ROWS
-#define KVQ_KEY_ROWS 8
+#ifndef KVQ_ROW_ENCODE_ROWS
+#define KVQ_ROW_ENCODE_ROWS 4
 #endif
-constexpr int key_rows_per_wave(int G) {
-    const int r = G < KVQ_KEY_ROWS ? G : KVQ_KEY_ROWS;
+constexpr int value_encode_rows(bool nvfp4, bool residual) { return nvfp4 && !residual ? 8 : 4; }
+constexpr int key_rows_per_wave(int G, bool nvfp4_res = false) {
+    const int cap = nvfp4_res ? 4 : 8;
+    const int r = G < cap ? G : cap;
     return r < G / 16 ? G / 16 : r;
 }
-constexpr int key_waves_per_group(int G) { return G / key_rows_per_wave(G); }
-constexpr int key_waves_per_block(int G) { return key_waves_per_group(G) > 4 ? key_waves_per_group(G) : 4; }
+constexpr int key_waves_per_group(int G, bool nvfp4_res = false) { return G / key_rows_per_wave(G, nvfp4_res); }
+constexpr int key_waves_per_block(int G, bool nvfp4_res = false) {
+    return key_waves_per_group(G, nvfp4_res) > 4 ? key_waves_per_group(G, nvfp4_res) : 4;
+}
 enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 
 // Row copy: row r of src to row r of dst, except that rows r >= split are read src_jump

@@ -115,10 +115,10 @@ __device__ __forceinline__ uint2 fp8_chunk(const u32x4& v, const Fp8Row& rs) {
     return o;
 }
 
-// One wave task: RW rows of a 64-chunk slab (the VALUE encoder's tiling).
+// One wave task: RW = KVQ_ROW_ENCODE_ROWS rows of a 64-chunk slab.
 template <int FMT, bool DIFF, bool GATHER, bool LG, bool WIN>
 __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
-    constexpr int RW = KVQ_ENCODE_ROWS_V;
+    constexpr int RW = KVQ_ROW_ENCODE_ROWS;
     static_assert(RW % 2 == 0, "NVFP4-row encode splits a task's rows over a lane pair");
     if (WIN && blockIdx.x >= a.win_block0) {  // blocks of the carried row copy
         window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 4u + (threadIdx.x >> 6)),
