@@ -30,10 +30,10 @@ constexpr int32_t kNoPaging = 62;
 //    3-4 us on a clean cache; the INT4 pack about 1 us on a clean cache.
 //  * row-format encoders (NVFP4-row, FP8-row; an even count for NVFP4-row's lane pairs): four,
 //    packs 2-4 us and residual encodes 4-5 us faster, in step and on a clean cache.
-//  * KEY encoder: min(G, 8) rows per wave (a power of two), but at least G / 16 so that the
-//    G / rows waves sharing a token group fit one block of at most 1024 threads; an NVFP4
-//    residual encode takes min(G, 4) (199 -> 195.5 us in step). INT4 G64 keeps eight: its eight
-//    waves per group each own one of a lane's eight channels.
+//  * KEY encoder: min(G, 8) rows per wave for a pack, min(G, 4) for a residual encode (a power
+//    of two), but at least G / 16 so that the G / rows waves sharing a token group fit one block
+//    of at most 1024 threads. Four rows: INT4 G64 residual encode 100.5 -> 97.5 us and NVFP4
+//    199 -> 195.5 us in step (within 1 us on a clean cache); the INT4 pack was 1 us slower.
 #ifndef KVQ_DECODE_ROWS
 #define KVQ_DECODE_ROWS 4
 #endif
@@ -41,14 +41,14 @@ constexpr int32_t kNoPaging = 62;
 #define KVQ_ROW_ENCODE_ROWS 4
 #endif
 constexpr int value_encode_rows(bool nvfp4, bool residual) { return nvfp4 && !residual ? 8 : 4; }
-constexpr int key_rows_per_wave(int G, bool nvfp4_res = false) {
-    const int cap = nvfp4_res ? 4 : 8;
+constexpr int key_rows_per_wave(int G, bool residual) {
+    const int cap = residual ? 4 : 8;
     const int r = G < cap ? G : cap;
     return r < G / 16 ? G / 16 : r;
 }
-constexpr int key_waves_per_group(int G, bool nvfp4_res = false) { return G / key_rows_per_wave(G, nvfp4_res); }
-constexpr int key_waves_per_block(int G, bool nvfp4_res = false) {
-    return key_waves_per_group(G, nvfp4_res) > 4 ? key_waves_per_group(G, nvfp4_res) : 4;
+constexpr int key_waves_per_group(int G, bool residual) { return G / key_rows_per_wave(G, residual); }
+constexpr int key_waves_per_block(int G, bool residual) {
+    return key_waves_per_group(G, residual) > 4 ? key_waves_per_group(G, residual) : 4;
 }
 enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 
