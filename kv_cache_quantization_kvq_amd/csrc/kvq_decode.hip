@@ -92,8 +92,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_vec(DecArgs a) {
     // KEY: per-channel metadata of this task's token group (G % RW == 0), loaded once
     float ks[8], km[8];
     if constexpr (KIND == KIND_KEY) {
-        // (a lane group past the last row tile, which stores nothing, reads the last group's)
-        const size_t mbase = ((size_t)(min<int64_t>(r0, a.rows - 1) / a.G) * (uint32_t)a.C8 + c8) * 8u;
+        // (a lane group past the last row tile, which stores nothing, reads the last group's).
+        // Rows stay below 2^31, so the wave-uniform group index is a 32-bit shift for a
+        // power-of-two G and a 32-bit division otherwise.
+        const uint32_t rm = (uint32_t)min<int64_t>(r0, a.rows - 1), gsz = (uint32_t)a.G;
+        const uint32_t gi = (gsz & (gsz - 1u)) == 0u ? rm >> __builtin_ctz(gsz) : rm / gsz;
+        const size_t mbase = ((size_t)gi * (uint32_t)a.C8 + c8) * 8u;
         if constexpr (FMT == FMT_INT4) {
             const u32x4 mins = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.meta0) + mbase);
             const u32x4 scs = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.meta1) + mbase);
