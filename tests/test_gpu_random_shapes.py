@@ -21,7 +21,7 @@ from workloads import bf16_bits
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 160
 HEAD_DIMS = [8, 12, 16, 24, 40, 64, 72, 100, 128, 136, 256]
 INT4_GROUPS = [5, 8, 16, 24, 32, 64, 128]
 
@@ -100,7 +100,7 @@ def test_random_shape_chain(i):
     assert_bits_equal(to_host(got), want, what + " residual decode")
 
 
-N_POOL_CASES = 24
+N_POOL_CASES = 80
 
 
 def draw_pool_case(i):
