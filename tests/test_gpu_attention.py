@@ -236,3 +236,58 @@ def test_head_dim_256_large(fmt, gk, gv):
     kr, vr = reconstruct(ok), reconstruct(ov)
     want = decode_attention(q, kr, vr, 1.0 / np.sqrt(d))
     check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"D=256 large {fmt}")
+
+
+N_RANDOM = 48
+
+
+def draw_attention_case(i):
+    """A seeded draw over everything the kernels take: format, K and V group sizes within the
+    kernel's constraints, head dim, tokens (ragged against 16-token sub-tiles and 64-token
+    blocks), KV heads, query heads per KV head (including tiles past 16 rows), and an optional
+    residual of any format."""
+    rng = np.random.default_rng(7000 + i)
+    d = int(rng.choice([64, 128, 256]))
+    fmts = ["int4", "nvfp4", "nvfp4_row", "fp8_row"]
+
+    def groups(fmt):
+        if fmt == "int4":
+            vg = [g for g in (8, 16, 32, 64, 128, 256) if max(8, d // 16) <= g <= d]
+            return int(rng.choice([16, 32, 64, 128])), int(rng.choice(vg))
+        return (16, 16) if fmt in ("nvfp4", "nvfp4_row") else (0, 0)
+
+    fmt = fmts[i % 4]
+    gk, gv = groups(fmt)
+    res = None
+    if rng.integers(0, 3) == 0:
+        rfmt = fmts[int(rng.integers(0, 4))]
+        res = (rfmt, *groups(rfmt))
+    H = int(rng.integers(1, 5))
+    rep = int(rng.choice([1, 2, 4, 8, 16, 20]))
+    T = int(rng.integers(1, 3000))
+    return dict(seed=7000 + i, d=d, fmt=fmt, gk=gk, gv=gv, res=res, H=H, Hq=H * rep, T=T)
+
+
+@pytest.mark.parametrize("i", range(N_RANDOM))
+def test_random_attention_vs_oracle(i):
+    c = draw_attention_case(i)
+    rng = np.random.default_rng(c["seed"])
+    d, T, H, Hq, fmt, gk, gv = c["d"], c["T"], c["H"], c["Hq"], c["fmt"], c["gk"], c["gv"]
+    k0, v0 = normal_kv(rng, T, H, d), normal_kv(rng, T, H, d)
+    q = bf16_bits(rng.standard_normal((Hq, d)))
+    gk0, gv0, ok0, ov0 = packed_pair(k0, v0, fmt, gk, gv)
+    if c["res"] is None:
+        out = kvq.decode_attention(to_dev(q), gk0, gv0).cpu().numpy()
+        kr, vr = reconstruct(ok0), reconstruct(ov0)
+    else:
+        rfmt, rgk, rgv = c["res"]
+        k1 = bf16_bits(oracle.bf16_to_f32(k0).astype(np.float64) + 0.1 * rng.standard_normal(k0.shape))
+        v1 = bf16_bits(oracle.bf16_to_f32(v0).astype(np.float64) + 0.1 * rng.standard_normal(v0.shape))
+        grk = kvq.encode_residual(to_dev(k1), kvq.unpack(gk0), "key", rfmt, rgk)
+        grv = kvq.encode_residual(to_dev(v1), kvq.unpack(gv0), "value", rfmt, rgv)
+        ork = oracle.encode_residual(k1, oracle.unpack(ok0), "key", rfmt, rgk)
+        orv = oracle.encode_residual(v1, oracle.unpack(ov0), "value", rfmt, rgv)
+        out = kvq.decode_attention(to_dev(q), gk0, gv0, grk, grv).cpu().numpy()
+        kr, vr = reconstruct(ok0, ork), reconstruct(ov0, orv)
+    want = decode_attention(q, kr, vr, 1.0 / np.sqrt(d))
+    check(out, want, np.abs(oracle.bf16_to_f32(vr)).max(), f"case {i} {c}")
