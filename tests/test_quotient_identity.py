@@ -17,7 +17,6 @@ significand; this test pins the arithmetic identity the encoders rely on.
 
 import os
 import subprocess
-import tempfile
 
 import pytest
 
@@ -118,8 +117,8 @@ int main(int argc, char** argv) {
 
 
 @pytest.fixture(scope="module")
-def sweep_binary():
-    d = tempfile.mkdtemp(prefix="kvq_quot_")
+def sweep_binary(tmp_path_factory):
+    d = str(tmp_path_factory.mktemp("kvq_quot"))
     src, exe = os.path.join(d, "quot.c"), os.path.join(d, "quot")
     with open(src, "w") as f:
         f.write(C_SRC)
@@ -169,11 +168,11 @@ def test_fp8_row_range_bound_is_needed(sweep_binary):
     assert n > 0 and bad > 0
 
 
-def test_plain_product_is_not_enough(sweep_binary):
+def test_plain_product_is_not_enough(sweep_binary, tmp_path):
     """The correction is needed: RN(d * RN(1/s)) alone misses RN(d/s) on these inputs, so the
     sweeps above are not vacuous."""
     src = C_SRC.replace("return fmaf(r, y, q0);", "(void)r; return q0;")
-    d = tempfile.mkdtemp(prefix="kvq_quot_plain_")
+    d = str(tmp_path)
     with open(os.path.join(d, "p.c"), "w") as f:
         f.write(src)
     exe = os.path.join(d, "p")
