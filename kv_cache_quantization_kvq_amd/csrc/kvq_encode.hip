@@ -125,19 +125,20 @@ __device__ __forceinline__ uint32_t int4_word(const u32x4& v, const Int4Group* g
 
 // ---- VALUE, vector path ------------------------------------------------------------------------
 
-// INT4 VALUE groups of 64 channels (8 lanes) over RW = 8 or 4 rows per task: instead of
+// INT4 VALUE groups of 64 channels (8 lanes) over RW = 8, 4 or 2 rows per task: instead of
 // all-reducing every row's minimum and maximum over the group's 8 lanes (and then computing the
 // same group constants on all 8), the statistics are reduce-scattered so that lane j of the group
-// ends with row j's (RW = 8; with RW = 4 lanes j and j ^ 1 both end with row j / 2), computes
-// that row's constants alone, and the constants reach the other lanes by ds_bpermute. Every lane
-// then holds exactly the constants the all-reduce would give it, so the codes and metadata are
-// the same bits. Three butterfly steps pair lanes j <-> 7 - j (DPP row_half_mirror), j <-> j ^ 2
-// and j <-> j ^ 1; at each step a lane keeps the half of its rows whose index bit matches its own
-// lane bit and sends the other half (with RW = 4 the last step combines the one row both hold).
+// ends with row j's (RW = 8; with RW = 4 lanes j and j ^ 1 both end with row j / 2, with RW = 2
+// lanes 0-3 with row 0 and 4-7 with row 1), computes that row's constants alone, and the
+// constants reach the other lanes by ds_bpermute. Every lane then holds exactly the constants the
+// all-reduce would give it, so the codes and metadata are the same bits. Three butterfly steps
+// pair lanes j <-> 7 - j (DPP row_half_mirror), j <-> j ^ 2 and j <-> j ^ 1; at each step a lane
+// keeps the half of its rows whose index bit matches its own lane bit and sends the other half
+// (once a lane holds a single row, the remaining steps combine the row its partner holds too).
 template <int RW, bool DIFF, bool GATHER, bool LG>
 __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v)[RW], int lane, int64_t r0, int nr,
                                                bool valid, uint32_t c8, uint32_t c8raw) {
-    static_assert(RW == 8 || RW == 4, "G64 VALUE rows per task");
+    static_assert(RW == 8 || RW == 4 || RW == 2, "G64 VALUE rows per task");
     uint32_t mn8[RW], mx8[RW];  // unsigned keys
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -157,7 +158,7 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
         mn4[k] = min(b2 ? mn8[k + H1] : mn8[k], dpp<0x141>(b2 ? mn8[k] : mn8[k + H1]));
         mx4[k] = max(b2 ? mx8[k + H1] : mx8[k], dpp<0x141>(b2 ? mx8[k] : mx8[k + H1]));
     }
-    uint32_t mn2[H2], mx2[H2];  // rows H1 b2 + H2 b1 + k
+    uint32_t mn2[H2 > 0 ? H2 : 1], mx2[H2 > 0 ? H2 : 1];  // rows H1 b2 + H2 b1 + k
 #pragma unroll
     for (int k = 0; k < H2; ++k) {
         mn2[k] = min(b1 ? mn4[k + H2] : mn4[k], dpp<0x4E>(b1 ? mn4[k] : mn4[k + H2]));
@@ -167,9 +168,13 @@ __device__ __forceinline__ void int4_value_g64(const EncArgs& a, const u32x4 (&v
     if constexpr (RW == 8) {
         gmn = min(b0 ? mn2[1] : mn2[0], dpp<0xB1>(b0 ? mn2[0] : mn2[1]));
         gmx = max(b0 ? mx2[1] : mx2[0], dpp<0xB1>(b0 ? mx2[0] : mx2[1]));
-    } else {
+    } else if constexpr (RW == 4) {
         gmn = min(mn2[0], dpp<0xB1>(mn2[0]));
         gmx = max(mx2[0], dpp<0xB1>(mx2[0]));
+    } else {  // one row per half of the 8 lanes: all-reduce over each half
+        const uint32_t n = min(mn4[0], dpp<0x4E>(mn4[0])), x = max(mx4[0], dpp<0x4E>(mx4[0]));
+        gmn = min(n, dpp<0xB1>(n));
+        gmx = max(x, dpp<0xB1>(x));
     }
     constexpr uint32_t LPR = 8 / RW;  // lanes per row after the scatter
     const uint32_t jr = j / LPR;
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 
     u32x4 v[RW];
     load_rows8<RW, DIFF, GATHER, !LG>(a, r0, h, d, v);
-    if constexpr (FMT == FMT_INT4 && (RW == 8 || RW == 4)) {
+    if constexpr (FMT == FMT_INT4 && (RW == 8 || RW == 4 || RW == 2)) {
         if (lpg == 8) {  // G = 64 (wave-uniform)
             int4_value_g64<RW, DIFF, GATHER, LG>(a, v, lane, r0, nr, valid, c8, c8raw);
             return;

@@ -25,11 +25,13 @@ constexpr int32_t kNoPaging = 62;
 // grids and the kernels. All measured on the bulk shape ([131072, 8, 128]) against eight rows:
 //  * decoder: four rows (a KEY decode needs G % KVQ_DECODE_ROWS == 0 so that a task's rows share
 //    one token group), 6-7% faster on residual decodes and plain unpacks; two rows were slower.
-//  * VALUE encoder: four rows, except eight for a plain NVFP4 pack (four were 2 us slower
-//    there). Residual encodes gained most: INT4 98.5 -> 96 us and NVFP4 198 -> 192 us in step,
-//    3-4 us on a clean cache; the INT4 pack about 1 us on a clean cache.
+//  * VALUE encoder: four rows for a residual encode, eight for a plain NVFP4 pack (four were
+//    2 us slower there) and two for the other plain packs. Residual encodes gained most: INT4
+//    98.5 -> 96 us and NVFP4 198 -> 192 us in step, 3-4 us on a clean cache. The INT4 G64 pack
+//    went 62 -> 61 us at four rows and to 59 us at two (60.5 -> 59.5 us on a clean cache).
 //  * row-format encoders (NVFP4-row, FP8-row; an even count for NVFP4-row's lane pairs): four,
-//    packs 2-4 us and residual encodes 4-5 us faster, in step and on a clean cache.
+//    packs 2-4 us and residual encodes 4-5 us faster, in step and on a clean cache; two rows
+//    made the packs 1-3 us slower again.
 //  * KEY encoder: min(G, 8) rows per wave for a pack, min(G, 4) for a residual encode (a power
 //    of two), but at least G / 16 so that the G / rows waves sharing a token group fit one block
 //    of at most 1024 threads. Four rows: INT4 G64 residual encode 100.5 -> 97.5 us and NVFP4
@@ -40,7 +42,7 @@ constexpr int32_t kNoPaging = 62;
 #ifndef KVQ_ROW_ENCODE_ROWS
 #define KVQ_ROW_ENCODE_ROWS 4
 #endif
-constexpr int value_encode_rows(bool nvfp4, bool residual) { return nvfp4 && !residual ? 8 : 4; }
+constexpr int value_encode_rows(bool nvfp4, bool residual) { return residual ? 4 : nvfp4 ? 8 : 2; }
 constexpr int key_rows_per_wave(int G, bool residual) {
     const int cap = residual ? 4 : 8;
     const int r = G < cap ? G : cap;
