@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_gen(DecArgs a) {
     if constexpr (FMT == FMT_NVFP4) fp4_table_fill(tab, *a.gscale);
     const int D = a.D, G = a.G;
     const int Dp = (D + 1) / 2;
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = (int64_t)(a.gen_base + (uint64_t)blockIdx.x * kThreads + threadIdx.x);
     if (idx >= a.rows * a.H * Dp) return;
     const int64_t r = idx / ((int64_t)a.H * Dp);
     const int64_t rem = idx - r * a.H * Dp;
@@ -200,7 +200,7 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_copy_rows(CopyArgs a) {
     if constexpr (VEC) {
         const uint64_t total = (uint64_t)a.T * (uint32_t)a.C8;
-        const uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+        const uint64_t u = a.gen_base + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
         if (u >= total) return;
         const uint32_t r = fdiv((uint32_t)u, a.div_C8);
         const uint32_t c8 = (uint32_t)u - r * (uint32_t)a.C8;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void k_copy_rows(CopyArgs a) {
             *reinterpret_cast<const uint4*>(a.src + (far ? a.src_jump : 0) + (int64_t)r * a.sst + (int64_t)h * a.ssh + d);
     } else {
         const uint64_t total = (uint64_t)a.T * a.H * a.D;
-        const uint64_t u = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+        const uint64_t u = a.gen_base + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
         if (u >= total) return;
         const int64_t HD = (int64_t)a.H * a.D;
         const int64_t r = (int64_t)(u / (uint64_t)HD);
@@ -266,8 +266,9 @@ hipError_t decode_launch(const DecArgs& a, bool vec, hipStream_t s) {
         }
     } else {
         const uint64_t n = (uint64_t)a.rows * a.H * ((a.D + 1) / 2);
-        hipLaunchKernelGGL((k_decode_gen<FMT, KIND, ADD, SCATTER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0,
-                           s, a);
+        launch_in_chunks(a, n, kThreads, [&](const DecArgs& b, dim3 grid) {
+            hipLaunchKernelGGL((k_decode_gen<FMT, KIND, ADD, SCATTER>), grid, dim3(kThreads), 0, s, b);
+        });
     }
     return hipGetLastError();
 }
@@ -293,10 +294,12 @@ hipError_t launch_decode(int fmt, int kind, const DecArgs& a, bool add, bool sca
 hipError_t launch_copy_rows(const CopyArgs& a, bool vec, hipStream_t s) {
     const uint64_t n = vec ? (uint64_t)a.T * (uint32_t)a.C8 : (uint64_t)a.T * a.H * a.D;
     if (n == 0) return hipSuccess;
-    if (vec)
-        hipLaunchKernelGGL(k_copy_rows<true>, dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_copy_rows<false>, dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0, s, a);
+    launch_in_chunks(a, n, kThreads, [&](const CopyArgs& b, dim3 grid) {
+        if (vec)
+            hipLaunchKernelGGL(k_copy_rows<true>, grid, dim3(kThreads), 0, s, b);
+        else
+            hipLaunchKernelGGL(k_copy_rows<false>, grid, dim3(kThreads), 0, s, b);
+    });
     return hipGetLastError();
 }
 

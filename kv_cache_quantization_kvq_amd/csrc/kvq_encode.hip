@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_gen(EncArgs a) {
         g = *a.gscale;
         fp4_table_fill(tab, g);
     }
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = (int64_t)(a.gen_base + (uint64_t)blockIdx.x * kThreads + threadIdx.x);
     if (idx >= a.rows * a.H) return;
     const int64_t r = idx / a.H;
     const int64_t h = idx - r * a.H;
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_k_gen(EncArgs a) {
     const int D = a.D, G = a.G;
     const int Dp = (D + 1) / 2;
     const int64_t nb = (a.rows + G - 1) / G;
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = (int64_t)(a.gen_base + (uint64_t)blockIdx.x * kThreads + threadIdx.x);
     if (idx >= nb * a.H * Dp) return;
     const int64_t b = idx / ((int64_t)a.H * Dp);
     const int64_t rem = idx - b * a.H * Dp;
@@ -802,13 +802,15 @@ hipError_t encode_dispatch(int kind, const EncArgs& a, bool vec, hipStream_t s) 
     } else {
         if (kind == KIND_VALUE) {
             const uint64_t n = (uint64_t)a.rows * a.H;
-            hipLaunchKernelGGL((k_encode_v_gen<FMT, DIFF, GATHER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0,
-                               s, a);
+            launch_in_chunks(a, n, kThreads, [&](const EncArgs& b, dim3 grid) {
+                hipLaunchKernelGGL((k_encode_v_gen<FMT, DIFF, GATHER>), grid, dim3(kThreads), 0, s, b);
+            });
         } else {
             const uint64_t nb = (uint64_t)(a.rows + a.G - 1) / a.G;
             const uint64_t n = nb * a.H * ((a.D + 1) / 2);
-            hipLaunchKernelGGL((k_encode_k_gen<FMT, DIFF, GATHER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0,
-                               s, a);
+            launch_in_chunks(a, n, kThreads, [&](const EncArgs& b, dim3 grid) {
+                hipLaunchKernelGGL((k_encode_k_gen<FMT, DIFF, GATHER>), grid, dim3(kThreads), 0, s, b);
+            });
         }
     }
     return hipGetLastError();

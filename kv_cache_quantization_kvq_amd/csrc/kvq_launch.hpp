@@ -66,7 +66,22 @@ struct CopyArgs {
     int64_t split, src_jump, dst_jump;
     int32_t H, D, C8;
     FastDiv div_C8, div_D8;
+    uint64_t gen_base;  // first work item of this launch (launch_in_chunks)
 };
+
+// A generic kernel (one work item per thread) over n items runs as launches of at most
+// kGenChunk items, each told its first item in `gen_base`, so that no dispatch reaches the
+// 32-bit limit on work items (tensors of up to 2^36 elements take the generic kernels when
+// their layout does not suit the vector ones).
+constexpr uint64_t kGenChunk = (uint64_t)1 << 31;
+template <class Args, class F>
+inline void launch_in_chunks(Args a, uint64_t n, uint32_t threads, F&& launch_one) {
+    for (uint64_t b0 = 0; b0 < n; b0 += kGenChunk) {
+        a.gen_base = b0;
+        const uint64_t m = n - b0 < kGenChunk ? n - b0 : kGenChunk;
+        launch_one(a, dim3((uint32_t)((m + threads - 1) / threads)));
+    }
+}
 
 // A launch of the vector encoder or decoder can carry a row copy (a BF16 window's protected
 // rows): the launcher appends blocks from win_block0 on, and their waves copy kWinChunks
@@ -100,6 +115,7 @@ struct EncArgs {
     uint32_t* ws;  // NVFP4: per-block partial maxima of the amax pass
     CopyArgs win;
     uint32_t win_tasks, win_block0;
+    uint64_t gen_base;  // generic kernels: first work item of this launch
 };
 
 // Rows being decoded: output row r reads packed row src ? src[r] : r and goes to output row
@@ -125,6 +141,7 @@ struct DecArgs {
     FastDiv div_D8, div_slabs;
     CopyArgs win;
     uint32_t win_tasks, win_block0;
+    uint64_t gen_base;  // generic kernels: first work item of this launch
 };
 
 // Lanes of a vector-path task. Rows of 64 or more 8-channel chunks (or a count that does not

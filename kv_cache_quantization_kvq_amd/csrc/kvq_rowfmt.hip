@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_row_encode_vec(EncArgs a) {
 // Generic encoder: one thread per (row, head).
 template <int FMT, bool DIFF, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_row_encode_gen(EncArgs a) {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = (int64_t)(a.gen_base + (uint64_t)blockIdx.x * kThreads + threadIdx.x);
     if (idx >= a.rows * a.H) return;
     const int64_t r = idx / a.H;
     const int64_t h = idx - r * a.H;
@@ -383,7 +383,7 @@ template <int FMT, bool ADD, bool SCATTER>
 __global__ __launch_bounds__(kThreads) void k_row_decode_gen(DecArgs a) {
     const int D = a.D;
     const int Dp = (D + 1) / 2;
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = (int64_t)(a.gen_base + (uint64_t)blockIdx.x * kThreads + threadIdx.x);
     if (idx >= a.rows * a.H * Dp) return;
     const int64_t r = idx / ((int64_t)a.H * Dp);
     const int64_t rem = idx - r * a.H * Dp;
@@ -428,9 +428,11 @@ void row_encode_launch(const EncArgs& a, bool vec, hipStream_t s) {
     } else if (vec) {
         if (win) hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, false, false, true>), grid, dim3(kThreads), 0, s, b);
         else hipLaunchKernelGGL((k_row_encode_vec<FMT, DIFF, GATHER, false, false>), grid, dim3(kThreads), 0, s, b);
-    } else
-        hipLaunchKernelGGL((k_row_encode_gen<FMT, DIFF, GATHER>), dim3(ceil_div_u((uint64_t)a.rows * a.H, kThreads)),
-                           dim3(kThreads), 0, s, a);
+    } else {
+        launch_in_chunks(a, (uint64_t)a.rows * a.H, kThreads, [&](const EncArgs& b, dim3 grid) {
+            hipLaunchKernelGGL((k_row_encode_gen<FMT, DIFF, GATHER>), grid, dim3(kThreads), 0, s, b);
+        });
+    }
 }
 
 template <int FMT, bool ADD, bool SCATTER>
@@ -448,8 +450,9 @@ void row_decode_launch(const DecArgs& a, bool vec, hipStream_t s) {
         }
     } else {
         const uint64_t n = (uint64_t)a.rows * a.H * ((a.D + 1) / 2);
-        hipLaunchKernelGGL((k_row_decode_gen<FMT, ADD, SCATTER>), dim3(ceil_div_u(n, kThreads)), dim3(kThreads), 0, s,
-                           a);
+        launch_in_chunks(a, n, kThreads, [&](const DecArgs& b, dim3 grid) {
+            hipLaunchKernelGGL((k_row_decode_gen<FMT, ADD, SCATTER>), grid, dim3(kThreads), 0, s, b);
+        });
     }
 }
 

@@ -9,6 +9,12 @@ the rows from just before element 2^32 (token 2^22) to the end, whose last KEY g
 (36 tokens). Windows start on group boundaries, so the oracle's pack of a window forms the same
 groups; NVFP4 windows are packed with the multiplier the oracle computes from the whole tensor's
 amax. Every code, metadata and reconstructed element of the windows must agree bit for bit.
+
+A second test sends the same tensor through the generic kernels (one work item per thread),
+which run in launches of at most 2^31 work items: an unpack into a view whose token pitch is
+not 16-byte aligned (2^31 + 51 200 work items, two launches) and the out-of-place decode of a
+sparse residual into such a view, which first copies every element of the predecessor (2^32 +
+102 400 work items, three launches) and then scatters the kept rows.
 """
 
 import numpy as np
@@ -92,3 +98,42 @@ def test_beyond_32bit_elements(tensors, fmt, G, kind):
                               f"{what} residual decode rows {t0}:{t1}")
     del gp, R0, gr, R1
     torch.cuda.empty_cache()
+
+
+def odd_pitch(T_, H_, D_):
+    """An uninitialized bf16 [T, H, D] view whose token pitch (H*D + 3) breaks 16-byte rows."""
+    buf = torch.empty((T_, H_ * D_ + 3), dtype=torch.bfloat16, device=dev())
+    return buf[:, :H_ * D_].unflatten(1, (H_, D_))
+
+
+def test_generic_kernels_beyond_32bit_work_items(tensors):
+    x0, x1, X0, X1, _ = tensors
+    kind, fmt, G = "key", "int4", 64
+    gp = kvq.pack(x0, kind, fmt, G)
+    out = odd_pitch(T, H, D)
+    kvq.unpack(gp, out=out)
+    R0 = kvq.unpack(gp)
+    pos_list = [0, (1 << 21) + 5, (1 << 22) + 7, T - 1]
+    r = kvq.encode_residual(x1, R0, kind, fmt, G,
+                            positions=torch.tensor(pos_list, dtype=torch.int32, device=dev()))
+    out2 = odd_pitch(T, H, D)
+    kvq.decode_residual(r, R0, out=out2)
+    torch.cuda.synchronize()
+    oR0 = {}
+    for t0, t1 in WINDOWS:
+        w = oracle.unpack(oracle.pack(X0[t0:t1], kind, fmt, G))
+        assert_bits_equal(to_host(out[t0:t1]), w, f"generic unpack rows {t0}:{t1}")
+        for t in range(t0, t1):
+            oR0[t] = w[t - t0]
+    # the kept rows: the oracle's residual of those rows alone (KEY groups run over the compact
+    # rows), added to the oracle's reconstruction
+    P = np.stack([oR0[t] for t in pos_list])
+    orr = oracle.encode_residual(np.ascontiguousarray(X1[pos_list]), P, kind, fmt, G)
+    want_kept = oracle.decode_residual(orr, P)
+    got = to_host(out2[torch.tensor(pos_list, device=dev())])
+    assert_bits_equal(got, want_kept, "sparse decode kept rows")
+    kept = set(pos_list)
+    for t0, t1 in WINDOWS:
+        rows = [t for t in range(t0, t1) if t not in kept]
+        got = to_host(out2[torch.tensor(rows, device=dev())])
+        assert_bits_equal(got, np.stack([oR0[t] for t in rows]), f"sparse decode copied rows {t0}:{t1}")
