@@ -533,6 +533,140 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G, DIFF)) void k_encode_k_
     }
 }
 
+// INT4 G64 KEY pack over half slabs (a plain pack of an unpaged view whose rows hold a multiple
+// of 32 chunks): an item is one 64-token group of 32 chunks (256 channels), its 8 waves take 8
+// rows each, and a lane loads 4 of them: lanes 0-31 the first and lanes 32-63 the second row of
+// each of the wave's 4 row pairs, so a wave holds 4 KB in flight instead of 8 KB and the grid has
+// twice the blocks. Lanes l and l + 32 hold the same channels and first merge their statistics
+// (lane swap across the halves); the rest is the full-slab kernel's: the LDS exchange over the
+// group's waves, wave w working out every lane's channel w constants, and the codes channel pair
+// by channel pair. Same codes and metadata, bit for bit. With WIN, blocks from win_block0 on
+// copy a BF16 window's protected rows instead.
+template <bool WIN>
+__global__ __launch_bounds__(512) void k_encode_k_half(EncArgs a) {
+    constexpr int G = 64, WPG = 8, RL = 4;  // RL: rows per lane
+    if (WIN && blockIdx.x >= a.win_block0) {
+        window_copy_wave(a.win, __builtin_amdgcn_readfirstlane((blockIdx.x - a.win_block0) * 8u + (threadIdx.x >> 6)),
+                         threadIdx.x & 63);
+        return;
+    }
+    __shared__ uint32_t lds[WPG * 8 * 64];
+    __shared__ f4_t cst[8 * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t nhs = (uint32_t)a.C8 >> 5;  // half slabs per row
+    const uint32_t b = __builtin_amdgcn_readfirstlane(blockIdx.x / nhs);
+    const uint32_t hs = blockIdx.x - b * nhs;
+    const uint32_t sub = (uint32_t)lane >> 5;
+    const uint32_t c8 = hs * 32u + ((uint32_t)lane & 31u);
+    const uint32_t h = fdiv(c8, a.div_D8);
+    const uint32_t d = (c8 - h * (uint32_t)a.D8) * 8u;
+    const int64_t rw = (int64_t)b * G + (int64_t)wave * (2 * RL);  // the wave's first row
+    const bool full = (int64_t)(b + 1) * G <= a.rows;               // wave-uniform
+
+    u32x4 v[RL];
+    if (full) {  // a row pair's second row lies one token pitch after the first
+        const uint32_t off = (uint32_t)(((int64_t)h * a.csh + d) * 2 + (int64_t)sub * a.cst * 2);
+#pragma unroll
+        for (int i = 0; i < RL; ++i) v[i] = ld_stream_at(wave_base(a.cur, (rw + 2 * i) * a.cst * 2), off);
+    } else {  // the last, partial group: rows past the end read the last row, which lies in it
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            const int64_t r = min<int64_t>(rw + 2 * i + sub, a.rows - 1);
+            v[i] = ld_stream(a.cur + r * a.cst + (int64_t)h * a.csh + d);
+        }
+    }
+
+    // per-channel statistics over the lane's rows, then over both halves
+    short2_t mn[4], mx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        mn[j] = keys2(v[0][j]);
+        mx[j] = mn[j];
+    }
+#pragma unroll
+    for (int i = 1; i < RL; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const short2_t k = keys2(v[i][j]);
+            mn[j] = min2(mn[j], k);
+            mx[j] = max2(mx[j], k);
+        }
+    }
+    uint32_t st[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const auto pn = __builtin_amdgcn_permlane32_swap(s2_as_u(mn[j]), s2_as_u(mn[j]), false, false);
+        const auto px = __builtin_amdgcn_permlane32_swap(s2_as_u(mx[j]), s2_as_u(mx[j]), false, false);
+        st[j] = s2_as_u(min2(as_s2(pn[0]), as_s2(pn[1])));
+        st[4 + j] = s2_as_u(max2(as_s2(px[0]), as_s2(px[1])));
+    }
+
+    // wave w reduces channel w of every lane over the group's waves and leaves its constants in
+    // LDS (the slow flag as a negative reciprocal); after a second barrier every wave reads all 8
+#pragma unroll
+    for (int k = 0; k < 8; ++k) lds[(wave * 8 + k) * 64 + lane] = st[k];
+    __syncthreads();
+    {
+        const int c = wave, j = c >> 1;
+        uint32_t m = lds[j * 64 + lane], x = lds[(4 + j) * 64 + lane];
+#pragma unroll
+        for (int o = 1; o < WPG; ++o) {
+            m = s2_as_u(min2(as_s2(m), as_s2(lds[(o * 8 + j) * 64 + lane])));
+            x = s2_as_u(max2(as_s2(x), as_s2(lds[(o * 8 + 4 + j) * 64 + lane])));
+        }
+        const short2_t ms = as_s2(m), xs = as_s2(x);
+        const Int4Group gc = int4_group(key_to_f32((c & 1) ? ms.y : ms.x), key_to_f32((c & 1) ? xs.y : xs.x));
+        cst[c * 64 + lane] = (f4_t){gc.mn, gc.scale, gc.slow ? -1.0f : gc.y, 0.0f};
+    }
+    __syncthreads();
+
+    uint32_t ev[RL], od[RL];
+#pragma unroll
+    for (int i = 0; i < RL; ++i) ev[i] = od[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f4_t t0 = cst[(2 * j) * 64 + lane], t1 = cst[(2 * j + 1) * 64 + lane];
+        Int4Group g0, g1;
+        g0.mn = t0[0]; g0.scale = t0[1]; g0.y = t0[2]; g0.slow = t0[2] < 0.0f;
+        g1.mn = t1[0]; g1.scale = t1[1]; g1.y = t1[2]; g1.slow = t1[2] < 0.0f;
+        if (__builtin_expect(g0.slow || g1.slow, 0)) {
+#pragma unroll
+            for (int i = 0; i < RL; ++i) {
+                const float d0 = __fsub_rn(bf16lo(v[i][j]), g0.mn), d1 = __fsub_rn(bf16hi(v[i][j]), g1.mn);
+                ev[i] = __builtin_amdgcn_cvt_pk_u8_f32(g0.slow ? d0 / g0.scale : int4_quot_raw(d0, g0), j, ev[i]);
+                od[i] = __builtin_amdgcn_cvt_pk_u8_f32(g1.slow ? d1 / g1.scale : int4_quot_raw(d1, g1), j, od[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RL; ++i) {
+                const float d0 = __fsub_rn(bf16lo(v[i][j]), g0.mn), d1 = __fsub_rn(bf16hi(v[i][j]), g1.mn);
+                ev[i] = __builtin_amdgcn_cvt_pk_u8_f32(int4_quot_raw(d0, g0), j, ev[i]);
+                od[i] = __builtin_amdgcn_cvt_pk_u8_f32(int4_quot_raw(d1, g1), j, od[i]);
+            }
+        }
+    }
+    const uint32_t coff = (sub * (uint32_t)a.C8 + c8) * 4u;
+#pragma unroll
+    for (int i = 0; i < RL; ++i) {
+        const uint32_t word = ev[i] | (od[i] << 4);
+        if (full || rw + 2 * i + sub < a.rows)
+            st_code_at<true>(wave_base_w(a.codes, (rw + 2 * i) * (int64_t)a.C8 * 4), coff, word);
+    }
+    if (wave == 0 && sub == 0) {
+        const size_t mbase = ((size_t)b * (uint32_t)a.C8 + c8) * 8u;
+        u32x4 mins, scales;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f4_t t0 = cst[(2 * j) * 64 + lane], t1 = cst[(2 * j + 1) * 64 + lane];
+            mins[j] = f32_to_f16(t0[0]) | (f32_to_f16(t1[0]) << 16);
+            scales[j] = f32_to_f16(t0[1]) | (f32_to_f16(t1[1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.meta0) + mbase) = mins;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.meta1) + mbase) = scales;
+    }
+}
+
 // ---- generic paths -----------------------------------------------------------------------------
 
 // VALUE: one thread per (row, head), groups walked along the row.
@@ -761,6 +895,21 @@ void launch_key_vec_w(const EncArgs& a, hipStream_t s) {
 // A row copy rides only on dense launches (a window never gathers).
 template <int FMT, int G, bool DIFF, bool GATHER>
 void launch_key_vec(const EncArgs& a, hipStream_t s) {
+    if constexpr (FMT == FMT_INT4 && G == 64 && !DIFF && !GATHER) {
+        // the half-slab pack (61.5 -> 59.4 us on the bulk shape): full-width rows, unpaged, a
+        // token pitch whose odd rows stay within the 32-bit lane offsets
+        if (a.ri_shift == 0 && a.C8 % 32 == 0 && a.cpshift == kNoPaging && a.cst >= 0 && a.cst < ((int64_t)1 << 29)) {
+            EncArgs b = a;
+            const uint32_t items = (uint32_t)((a.rows + G - 1) / G) * (uint32_t)(a.C8 / 32);
+            if (a.win_tasks) {
+                const dim3 grid = grid_with_copy(b, items, 8u);  // sets b.win_block0 before the launch copies b
+                hipLaunchKernelGGL(k_encode_k_half<true>, grid, dim3(512), 0, s, b);
+            } else {
+                hipLaunchKernelGGL(k_encode_k_half<false>, dim3(items), dim3(512), 0, s, b);
+            }
+            return;
+        }
+    }
     if constexpr (!GATHER) {
         if (a.win_tasks) return launch_key_vec_w<FMT, G, DIFF, GATHER, true>(a, s);
     }
