@@ -533,16 +533,17 @@ __global__ __launch_bounds__(64 * key_waves_per_block(G, DIFF)) void k_encode_k_
     }
 }
 
-// INT4 G64 KEY pack over half slabs (a plain pack of an unpaged view whose rows hold a multiple
-// of 32 chunks): an item is one 64-token group of 32 chunks (256 channels), its 8 waves take 8
-// rows each, and a lane loads 4 of them: lanes 0-31 the first and lanes 32-63 the second row of
-// each of the wave's 4 row pairs, so a wave holds 4 KB in flight instead of 8 KB and the grid has
-// twice the blocks. Lanes l and l + 32 hold the same channels and first merge their statistics
-// (lane swap across the halves); the rest is the full-slab kernel's: the LDS exchange over the
-// group's waves, wave w working out every lane's channel w constants, and the codes channel pair
-// by channel pair. Same codes and metadata, bit for bit. With WIN, blocks from win_block0 on
-// copy a BF16 window's protected rows instead.
-template <bool WIN>
+// INT4 G64 KEY pack or dense residual encode over half slabs (an unpaged view whose rows hold a
+// multiple of 32 chunks): an item is one 64-token group of 32 chunks (256 channels), its 8 waves
+// take 8 rows each, and a lane loads 4 of them: lanes 0-31 the first and lanes 32-63 the second
+// row of each of the wave's 4 row pairs. A wave then holds 4 KB of each input in flight, and the
+// grid has twice the blocks of the full-slab kernel with 8 rows per wave. Lanes l and l + 32 hold
+// the same channels and first merge their statistics (lane swap across the halves); the rest is
+// the full-slab kernel's: the LDS exchange over the group's waves, wave w working out every
+// lane's channel w constants, and the codes channel pair by channel pair. Same codes and
+// metadata, bit for bit. With DIFF the lane loads the same rows of `prev` and codes
+// bf16(cur - prev); with WIN, blocks from win_block0 on copy a BF16 window's protected rows.
+template <bool DIFF, bool WIN>
 __global__ __launch_bounds__(512) void k_encode_k_half(EncArgs a) {
     constexpr int G = 64, WPG = 8, RL = 4;  // RL: rows per lane
     if (WIN && blockIdx.x >= a.win_block0) {
@@ -564,16 +565,31 @@ __global__ __launch_bounds__(512) void k_encode_k_half(EncArgs a) {
     const int64_t rw = (int64_t)b * G + (int64_t)wave * (2 * RL);  // the wave's first row
     const bool full = (int64_t)(b + 1) * G <= a.rows;               // wave-uniform
 
-    u32x4 v[RL];
+    u32x4 v[RL], p[DIFF ? RL : 1];
     if (full) {  // a row pair's second row lies one token pitch after the first
         const uint32_t off = (uint32_t)(((int64_t)h * a.csh + d) * 2 + (int64_t)sub * a.cst * 2);
 #pragma unroll
         for (int i = 0; i < RL; ++i) v[i] = ld_stream_at(wave_base(a.cur, (rw + 2 * i) * a.cst * 2), off);
+        if constexpr (DIFF) {
+            const uint32_t poff = (uint32_t)(((int64_t)h * a.psh + d) * 2 + (int64_t)sub * a.pst * 2);
+#pragma unroll
+            for (int i = 0; i < RL; ++i) p[i] = ld_stream_at(wave_base(a.prev, (rw + 2 * i) * a.pst * 2), poff);
+        }
     } else {  // the last, partial group: rows past the end read the last row, which lies in it
 #pragma unroll
         for (int i = 0; i < RL; ++i) {
             const int64_t r = min<int64_t>(rw + 2 * i + sub, a.rows - 1);
             v[i] = ld_stream(a.cur + r * a.cst + (int64_t)h * a.csh + d);
+            if constexpr (DIFF) p[i] = ld_stream(a.prev + r * a.pst + (int64_t)h * a.psh + d);
+        }
+    }
+    if constexpr (DIFF) {  // the residual bf16(cur - prev)
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            v[i].x = sub_bf16x2(v[i].x, p[i].x);
+            v[i].y = sub_bf16x2(v[i].y, p[i].y);
+            v[i].z = sub_bf16x2(v[i].z, p[i].z);
+            v[i].w = sub_bf16x2(v[i].w, p[i].w);
         }
     }
 
@@ -651,7 +667,7 @@ __global__ __launch_bounds__(512) void k_encode_k_half(EncArgs a) {
     for (int i = 0; i < RL; ++i) {
         const uint32_t word = ev[i] | (od[i] << 4);
         if (full || rw + 2 * i + sub < a.rows)
-            st_code_at<true>(wave_base_w(a.codes, (rw + 2 * i) * (int64_t)a.C8 * 4), coff, word);
+            st_code_at<!DIFF>(wave_base_w(a.codes, (rw + 2 * i) * (int64_t)a.C8 * 4), coff, word);
     }
     if (wave == 0 && sub == 0) {
         const size_t mbase = ((size_t)b * (uint32_t)a.C8 + c8) * 8u;
@@ -895,17 +911,20 @@ void launch_key_vec_w(const EncArgs& a, hipStream_t s) {
 // A row copy rides only on dense launches (a window never gathers).
 template <int FMT, int G, bool DIFF, bool GATHER>
 void launch_key_vec(const EncArgs& a, hipStream_t s) {
-    if constexpr (FMT == FMT_INT4 && G == 64 && !DIFF && !GATHER) {
-        // the half-slab pack (61.5 -> 59.4 us on the bulk shape): full-width rows, unpaged, a
-        // token pitch whose odd rows stay within the 32-bit lane offsets
-        if (a.ri_shift == 0 && a.C8 % 32 == 0 && a.cpshift == kNoPaging && a.cst >= 0 && a.cst < ((int64_t)1 << 29)) {
+    if constexpr (FMT == FMT_INT4 && G == 64 && !GATHER) {
+        // the half-slab kernel (bulk shape: pack 61.5 -> 59.4 us; dense residual encode 105.5 ->
+        // 100.5 us on a clean cache, the same in step): full-width rows, unpaged, token pitches
+        // whose odd rows stay within the 32-bit lane offsets
+        const bool pitches = a.cst >= 0 && a.cst < ((int64_t)1 << 29) &&
+                             (!DIFF || (a.pst >= 0 && a.pst < ((int64_t)1 << 29)));
+        if (a.ri_shift == 0 && a.C8 % 32 == 0 && a.cpshift == kNoPaging && pitches) {
             EncArgs b = a;
             const uint32_t items = (uint32_t)((a.rows + G - 1) / G) * (uint32_t)(a.C8 / 32);
             if (a.win_tasks) {
                 const dim3 grid = grid_with_copy(b, items, 8u);  // sets b.win_block0 before the launch copies b
-                hipLaunchKernelGGL(k_encode_k_half<true>, grid, dim3(512), 0, s, b);
+                hipLaunchKernelGGL((k_encode_k_half<DIFF, true>), grid, dim3(512), 0, s, b);
             } else {
-                hipLaunchKernelGGL(k_encode_k_half<false>, dim3(items), dim3(512), 0, s, b);
+                hipLaunchKernelGGL((k_encode_k_half<DIFF, false>), dim3(items), dim3(512), 0, s, b);
             }
             return;
         }

@@ -36,8 +36,9 @@ constexpr int32_t kNoPaging = 62;
 //    of two), but at least G / 16 so that the G / rows waves sharing a token group fit one block
 //    of at most 1024 threads. Four rows: INT4 G64 residual encode 100.5 -> 97.5 us and NVFP4
 //    199 -> 195.5 us in step (within 1 us on a clean cache); the INT4 pack was 1 us slower.
-//    The INT4 G64 pack of full-width unpaged rows instead runs the half-slab kernel
-//    (k_encode_k_half: 8 rows per wave over 256 channels, 4 per lane): 61.5 -> 59 us.
+//    The INT4 G64 pack and dense residual encode of full-width unpaged rows instead run the
+//    half-slab kernel (k_encode_k_half: 8 rows per wave over 256 channels, 4 per lane): pack
+//    61.5 -> 59 us, residual encode 105.5 -> 100.5 us on a clean cache.
 #ifndef KVQ_DECODE_ROWS
 #define KVQ_DECODE_ROWS 4
 #endif
