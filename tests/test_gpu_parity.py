@@ -235,6 +235,34 @@ def test_ties_zeros_and_constants(kind):
         assert_bits_equal(gy, oy, f"zeros {fmt} decoded")
 
 
+def test_key_half_slab_degenerate_groups():
+    """The INT4 G64 KEY half-slab kernel (rows of a multiple of 32 chunks, at least 64) on groups
+    that take its division path: channels constant over a group (scale 0) and ranges of 2^-120
+    (scales below 2^-100; larger scales than 2^100 would overflow the f16 metadata, outside the
+    codec's domain), with half-integer ramps, signed zeros, coarse values with many ties, and a
+    partial last group (T = 150), for the pack and a dense residual against the reconstruction."""
+    T, H, D = 150, 4, 128
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((T, H, D))
+    t = np.arange(T)[:, None]
+    x[:, 0, 0:8] = 3.5                                      # constant channels
+    x[:, 0, 8:16] = np.where(t % 2 == 0, 0.0, 2.0 ** -120)  # tiny ranges
+    x[:, 1, :32] = -2.0 + (t % 31) * 0.25                   # ramps through half-integer quotients
+    x[:, 2, :16] = np.where(t % 2 == 0, 0.0, -0.0)          # signed zeros only
+    x[:, 3, 64:] = rng.integers(-40, 41, (T, 64)) * 0.1     # coarse values, many ties
+    xb = bf16_bits(x)
+    gp, op, gy, oy = roundtrip(xb, "key", "int4", 64)
+    assert_same_packed(gp, op, "half-slab pack")
+    assert_bits_equal(gy, oy, "half-slab unpack")
+    x1 = bf16_bits(oracle.bf16_to_f32(xb).astype(np.float64) + 0.01 * rng.standard_normal((T, H, D)))
+    x1[:, 0, 0:8] = xb[:, 0, 0:8]  # residual channels that are exactly zero
+    gr = kvq.encode_residual(to_dev(x1), to_dev(gy), "key", "int4", 64)
+    orr = oracle.encode_residual(x1, oy, "key", "int4", 64)
+    assert_same_packed(gr, orr, "half-slab residual")
+    assert_bits_equal(to_host(kvq.decode_residual(gr, to_dev(oy))), oracle.decode_residual(orr, oy),
+                      "half-slab residual decode")
+
+
 def test_workspace_reuse_across_calls():
     rng = np.random.default_rng(9)
     a = normal_kv(rng, 256, 8, 128)
