@@ -293,10 +293,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_v_vec(EncArgs a) {
 // An item is one token group (G rows) of one 64-chunk column slab. WPG waves share an item,
 // RPW rows each; a block of WPB waves holds WPB/WPG items.
 template <int FMT, int G, bool DIFF, bool GATHER, bool LG, bool WIN>
-__global__ __launch_bounds__(64 * key_waves_per_block(G, DIFF)) void k_encode_k_vec(EncArgs a) {
-    constexpr int WPG = key_waves_per_group(G, DIFF);
-    constexpr int RPW = key_rows_per_wave(G, DIFF);
-    constexpr int WPB = key_waves_per_block(G, DIFF);
+__global__ __launch_bounds__(64 * key_waves_per_block(G, DIFF, FMT == FMT_INT4)) void k_encode_k_vec(EncArgs a) {
+    constexpr int WPG = key_waves_per_group(G, DIFF, FMT == FMT_INT4);
+    constexpr int RPW = key_rows_per_wave(G, DIFF, FMT == FMT_INT4);
+    constexpr int WPB = key_waves_per_block(G, DIFF, FMT == FMT_INT4);
     constexpr int IPB = WPB / WPG;
     constexpr int NW = (FMT == FMT_INT4) ? 8 : 4;  // exchanged words per lane
     static_assert(WPB <= 16 && WPB % WPG == 0, "KEY encoder block shape");
@@ -897,15 +897,14 @@ inline uint32_t ceil_div_u(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 
 // One block per WPB / WPG token-group items (and the blocks of a carried row copy).
 template <int FMT, int G, bool DIFF, bool GATHER, bool WIN>
 void launch_key_vec_w(const EncArgs& a, hipStream_t s) {
-    constexpr uint32_t ipb = (uint32_t)(key_waves_per_block(G, DIFF) / key_waves_per_group(G, DIFF));
+    constexpr uint32_t wpb = (uint32_t)key_waves_per_block(G, DIFF, FMT == FMT_INT4);
+    constexpr uint32_t ipb = wpb / (uint32_t)key_waves_per_group(G, DIFF, FMT == FMT_INT4);
     EncArgs b = a;
-    const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, ipb), (uint32_t)key_waves_per_block(G, DIFF));
+    const dim3 grid = grid_with_copy(b, ceil_div_u(a.n_tasks, ipb), wpb);
     if (a.ri_shift > 0)
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true, WIN>), grid, dim3(64 * key_waves_per_block(G, DIFF)),
-                           0, s, b);
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, true, WIN>), grid, dim3(64 * wpb), 0, s, b);
     else
-        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false, WIN>), grid, dim3(64 * key_waves_per_block(G, DIFF)),
-                           0, s, b);
+        hipLaunchKernelGGL((k_encode_k_vec<FMT, G, DIFF, GATHER, false, WIN>), grid, dim3(64 * wpb), 0, s, b);
 }
 
 // A row copy rides only on dense launches (a window never gathers).

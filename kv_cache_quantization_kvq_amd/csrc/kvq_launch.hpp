@@ -36,6 +36,9 @@ constexpr int32_t kNoPaging = 62;
 //    of two), but at least G / 16 so that the G / rows waves sharing a token group fit one block
 //    of at most 1024 threads. Four rows: INT4 G64 residual encode 100.5 -> 97.5 us and NVFP4
 //    199 -> 195.5 us in step (within 1 us on a clean cache); the INT4 pack was 1 us slower.
+//    The INT4 G16 pack (page-local groups of 16-token pages) takes four rows as well: 63.8 ->
+//    62 us in step, 66 -> 63 us on a clean cache; the NVFP4 G16 pack keeps eight (four made
+//    its head-shard pack 9% slower).
 //    The INT4 G64 pack and dense residual encode of full-width unpaged rows instead run the
 //    half-slab kernel (k_encode_k_half: 8 rows per wave over 256 channels, 4 per lane): pack
 //    61.5 -> 59 us, residual encode 105.5 -> 100.5 us on a clean cache.
@@ -46,14 +49,16 @@ constexpr int32_t kNoPaging = 62;
 #define KVQ_ROW_ENCODE_ROWS 4
 #endif
 constexpr int value_encode_rows(bool nvfp4, bool residual) { return residual ? 4 : nvfp4 ? 8 : 2; }
-constexpr int key_rows_per_wave(int G, bool residual) {
-    const int cap = residual ? 4 : 8;
+constexpr int key_rows_per_wave(int G, bool residual, bool int4) {
+    const int cap = residual || (int4 && G == 16) ? 4 : 8;
     const int r = G < cap ? G : cap;
     return r < G / 16 ? G / 16 : r;
 }
-constexpr int key_waves_per_group(int G, bool residual) { return G / key_rows_per_wave(G, residual); }
-constexpr int key_waves_per_block(int G, bool residual) {
-    return key_waves_per_group(G, residual) > 4 ? key_waves_per_group(G, residual) : 4;
+constexpr int key_waves_per_group(int G, bool residual, bool int4) {
+    return G / key_rows_per_wave(G, residual, int4);
+}
+constexpr int key_waves_per_block(int G, bool residual, bool int4) {
+    return key_waves_per_group(G, residual, int4) > 4 ? key_waves_per_group(G, residual, int4) : 4;
 }
 enum : int { KIND_KEY = 0, KIND_VALUE = 1 };
 
